@@ -1,0 +1,80 @@
+"""The five synthetic workloads the path is checked and measured on.
+
+Shapes follow the OneLA operator suite (§4.1: R requests, W beams, T decode
+steps, H heads, K = d_k, V = d_v) and the DeltaLog recurrent-kernel table
+(Table 3: H/d_k/d_v = 32/128/128, FP32 state, BF16 K / FP32 U log, M = 8).
+Seeds: the tiny workload uses seed 0; the others use their index.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from . import synth
+
+
+@dataclass(frozen=True)
+class BeamWorkload:
+    name: str
+    R: int
+    H: int
+    dk: int
+    dv: int
+    W: int
+    L: int
+    s0_std: float
+    seed: int
+    parents: str
+    channel_decay: bool = False
+    hot_frac: float = 0.3
+
+    @property
+    def beam_steps(self) -> int:
+        return self.R * self.W * self.L
+
+    def inputs(self, **over):
+        kw = dict(R=self.R, H=self.H, dk=self.dk, dv=self.dv, W=self.W, L=self.L,
+                  s0_std=self.s0_std, seed=self.seed, parents=self.parents,
+                  channel_decay=self.channel_decay, hot_frac=self.hot_frac)
+        kw.update(over)
+        return synth.make_inputs(**kw)
+
+
+@dataclass(frozen=True)
+class SequenceWorkload:
+    """Bounded-log decoding of independent sequences (one beam each)."""
+    name: str
+    R: int
+    H: int
+    dk: int
+    dv: int
+    T: int
+    M: int
+    s0_std: float
+    seed: int
+    channel_decay: bool = False
+
+    @property
+    def sequence_steps(self) -> int:
+        return self.R * self.T
+
+    def inputs(self, **over):
+        kw = dict(R=self.R, H=self.H, dk=self.dk, dv=self.dv, T=self.T,
+                  s0_std=self.s0_std, seed=self.seed, channel_decay=self.channel_decay)
+        kw.update(over)
+        return synth.make_sequence_inputs(**kw)
+
+
+TINY = BeamWorkload("tiny_gdn_beam", R=1, H=2, dk=16, dv=16, W=4, L=3,
+                    s0_std=0.1, seed=0, parents="uniform")
+SINGLE = BeamWorkload("gdn_single_request", R=1, H=32, dk=128, dv=128, W=128, L=3,
+                      s0_std=0.05, seed=1, parents="topk")
+LARGE = BeamWorkload("gdn_large_beam", R=8, H=32, dk=128, dv=128, W=512, L=4,
+                     s0_std=0.05, seed=2, parents="topk_hot", hot_frac=0.3)
+DELTALOG = SequenceWorkload("deltalog_bounded_log", R=128, H=32, dk=128, dv=128,
+                            T=64, M=8, s0_std=0.05, seed=3)
+KDA = BeamWorkload("kda_channel_decay_beam", R=16, H=32, dk=128, dv=128, W=256, L=4,
+                   s0_std=0.05, seed=4, parents="topk", channel_decay=True)
+
+ALL = (TINY, SINGLE, LARGE, DELTALOG, KDA)
+BY_NAME = {w.name: w for w in ALL}

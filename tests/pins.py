@@ -1,0 +1,302 @@
+"""Pins that tie the FP64 oracle to facts other than its own code.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+a value printed or worked by hand from the pages, a closed form of the
+recurrence, an invariant, an independent definition, or brute force on tiny
+inputs.  ``test_oracle_pins`` runs them; ``test_oracle_mutations`` plants
+plausible mistakes in the oracle and checks that some pin catches each one.
+"""
+
+from __future__ import annotations
+
+import itertools
+import json
+import os
+
+import numpy as np
+
+import oracle.gdn_oracle as O
+from linear_attention_beam_gdn_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def rel(x, ref):
+    """max |x - ref| / max |ref| (over the whole array)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(x - ref)) / (den if den > 0 else 1.0))
+
+
+def small(channel=False, seed=11, **kw):
+    base = dict(R=2, H=2, dk=8, dv=6, W=5, L=4, s0_std=0.3, seed=seed,
+                parents="uniform", channel_decay=channel)
+    base.update(kw)
+    return synth.make_inputs(**base)
+
+
+def walk_ancestor(parents, t, r, b, j):
+    """Ancestor slot at depth j of beam b at step t, by following parent
+    pointers back from step t (independent of the ancestry recursion)."""
+    x = b
+    for s in range(t, j, -1):
+        x = int(parents[s][r, x])
+    return x
+
+
+def f64(bits):
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+# -------------------------------------------------------------- golden values
+
+def pin_hand_worked():
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_transitions.json")))
+    ex = g["gdn_two_steps"]
+    S = np.array(ex["S0"], np.float64)[None]
+    for st in ex["steps"]:
+        S, d = O.transition(S, np.array([st["k"]], float), np.array([st["v"]], float),
+                            np.array([st["alpha"]], float), np.array([st["beta"]], float))
+        o = O.readout(S, np.array([st["q"]], float))
+        assert np.allclose(d[0], st["delta"], atol=1e-12), (d, st["delta"])
+        assert np.allclose(S[0], st["S"], atol=1e-12), (S, st["S"])
+        assert np.allclose(o[0], st["o"], atol=1e-12), (o, st["o"])
+    ex = g["kda_one_step"]
+    S, d = O.transition(np.array(ex["S0"], float)[None], np.array([ex["k"]], float),
+                        np.array([ex["v"]], float), np.array([ex["alpha"]], float),
+                        np.array([ex["beta"]], float))
+    o = O.readout(S, np.array([ex["q"]], float))
+    assert np.allclose(d[0], ex["delta"], atol=1e-12), (d, ex["delta"])
+    assert np.allclose(S[0], ex["S"], atol=1e-12)
+    assert np.allclose(o[0], ex["o"], atol=1e-12)
+
+
+# ------------------------------------------------------------------ ancestry
+
+def pin_ancestry_walk():
+    rng = np.random.default_rng(5)
+    widths = [3, 6, 4, 7, 5]
+    R = 3
+    parents = [None] + [rng.integers(0, widths[t - 1], size=(R, widths[t])) for t in range(1, 5)]
+    anc = O.ancestry(parents, R, widths[0])
+    for t in range(5):
+        assert anc[t].shape == (R, widths[t], t)
+        for r, b, j in itertools.product(range(R), range(widths[t]), range(t)):
+            assert anc[t][r, b, j] == walk_ancestor(parents, t, r, b, j)
+
+
+def pin_ancestry_identity_and_fanout():
+    R, W = 2, 6
+    ident = [None] + [np.tile(np.arange(W), (R, 1)) for _ in range(3)]
+    anc = O.ancestry(ident, R, W)
+    for t in range(4):
+        assert np.all(anc[t] == np.arange(W)[None, :, None])
+    fan = [None] + [np.full((R, W), 2) for _ in range(3)]
+    anc = O.ancestry(fan, R, W)
+    for t in range(1, 4):
+        assert np.all(anc[t] == 2)
+        assert np.all(anc[t] == anc[t][:, :1])
+
+
+# -------------------------------------------------------------- closed forms
+
+def _chain_slots(inp, t, r, b):
+    parents = [s.get("parent") for s in inp["steps"]]
+    return [walk_ancestor(parents, t, r, b, j) for j in range(t)] + [b]
+
+
+def pin_beta_zero(channel=False):
+    """beta = 0: records carry no update, so S_t = (prod of decays) S0."""
+    inp = small(channel=channel, beta_const=0.0)
+    ref = O.beam_decode(inp["S0"], inp["steps"])
+    R, H, dk, dv = inp["S0"].shape
+    for t, st in enumerate(inp["steps"]):
+        assert np.all(ref["delta"][t] == 0.0)
+        for r, b, h in itertools.product(range(R), range(st["q"].shape[1]), range(H)):
+            slots = _chain_slots(inp, t, r, b)
+            gate = np.ones(dk) if channel else 1.0
+            for j, s in enumerate(slots):
+                gate = gate * inp["steps"][j]["alpha"][r, s, h].astype(np.float64)
+            q = f64(st["q"][r, b, h])
+            S0 = inp["S0"][r, h].astype(np.float64)
+            expect = (gate * q) @ S0 if channel else gate * (q @ S0)
+            assert rel(ref["o"][t][r, b, h], expect) < 1e-13
+
+
+def _basis_inputs(S0_zero):
+    """alpha = beta = 1, key at step j = e_{sigma(j)}, q at step t = key of
+    depth t // 2.  Retrieval must return that depth's v for every beam."""
+    inp = small(alpha_const=1.0, beta_const=1.0, dk=8, dv=6, L=4, seed=21)
+    sigma = [5, 1, 7, 2]
+    one = synth.bf16_bits(np.float32(1.0))
+    for t, st in enumerate(inp["steps"]):
+        st["k"][:] = 0
+        st["k"][..., sigma[t]] = one
+        st["q"][:] = 0
+        st["q"][..., sigma[t // 2]] = one
+    if S0_zero:
+        inp["S0"][:] = 0
+    return inp
+
+
+def pin_orthonormal_retrieval():
+    for S0_zero in (True, False):
+        inp = _basis_inputs(S0_zero)
+        ref = O.beam_decode(inp["S0"], inp["steps"])
+        R, H = inp["S0"].shape[:2]
+        for t, st in enumerate(inp["steps"]):
+            for r, b, h in itertools.product(range(R), range(st["q"].shape[1]), range(H)):
+                j = t // 2
+                slot = _chain_slots(inp, t, r, b)[j]
+                v = f64(inp["steps"][j]["v"][r, slot, h])
+                if S0_zero:
+                    assert np.array_equal(ref["o"][t][r, b, h], v)
+                else:
+                    assert rel(ref["o"][t][r, b, h], v) < 1e-12
+
+
+def pin_delta_rule_write():
+    """After one step with a unit key, S_t^T k = (1 - beta) decayed^T k + beta v."""
+    rng = np.random.default_rng(3)
+    N, dk, dv = 7, 9, 5
+    S = rng.standard_normal((N, dk, dv))
+    k = rng.standard_normal((N, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((N, dv))
+    alpha = rng.uniform(0.1, 0.9, N)
+    beta = rng.uniform(0.1, 0.9, N)
+    S1, _ = O.transition(S, k, v, alpha, beta)
+    read = np.einsum("nkv,nk->nv", S1, k)
+    prior = alpha[:, None] * np.einsum("nkv,nk->nv", S, k)
+    assert rel(read, (1 - beta)[:, None] * prior + beta[:, None] * v) < 1e-13
+
+
+def _unrolled_state(inp, t, r, b, h, channel):
+    """S_t = A_t...A_0 S0 + sum_j A_t...A_{j+1} beta_j k_j v_j^T with
+    A_j = alpha_j (I - beta_j k_j k_j^T) (scalar decay) or
+    A_j = (I - beta_j k_j k_j^T) D(a_j) (channel decay), as dense matrices."""
+    S0 = inp["S0"][r, h].astype(np.float64)
+    dk = S0.shape[0]
+    mats, adds = [], []
+    for j, s in enumerate(_chain_slots(inp, t, r, b)):
+        st = inp["steps"][j]
+        k = f64(st["k"][r, s, h])
+        v = f64(st["v"][r, s, h])
+        a = st["alpha"][r, s, h].astype(np.float64)
+        be = float(st["beta"][r, s, h])
+        P = np.eye(dk) - be * np.outer(k, k)
+        mats.append(P @ np.diag(a) if channel else a * P)
+        adds.append(be * np.outer(k, v))
+    S = S0
+    for A, B in zip(mats, adds):
+        S = A @ S + B
+    # expand the product form explicitly
+    n = len(mats)
+    total = np.eye(dk)
+    for A in mats:
+        total = A @ total
+    Sx = total @ S0
+    for j in range(n):
+        tail = np.eye(dk)
+        for A in mats[j + 1:]:
+            tail = A @ tail
+        Sx = Sx + tail @ adds[j]
+    assert rel(S, Sx) < 1e-12
+    return Sx
+
+
+def pin_unrolled_closed_form(channel=False, square=False):
+    inp = small(channel=channel, seed=31, **(dict(dk=8, dv=8) if square else {}))
+    ref = O.beam_decode(inp["S0"], inp["steps"])
+    R, H = inp["S0"].shape[:2]
+    for t in range(len(inp["steps"])):
+        pairs = [(r, b) for r in range(R) for b in (0, 3)]
+        states = O.beam_states(inp["S0"], inp["steps"], t, pairs)
+        for i, (r, b) in enumerate(pairs):
+            for h in range(H):
+                Sx = _unrolled_state(inp, t, r, b, h, channel)
+                assert rel(states[i, h], Sx) < 1e-12
+                q = f64(inp["steps"][t]["q"][r, b, h])
+                assert rel(ref["o"][t][r, b, h], q @ Sx) < 1e-12
+
+
+def pin_replay_equals_eager(channel=False, seed=41, square=False):
+    inp = small(channel=channel, seed=seed, **(dict(dk=8, dv=8) if square else {}))
+    a = O.beam_decode(inp["S0"], inp["steps"])
+    b = O.beam_decode_replay(inp["S0"], inp["steps"])
+    for t in range(len(inp["steps"])):
+        assert rel(b["o"][t], a["o"][t]) < 1e-12
+        assert rel(b["delta"][t], a["delta"][t]) < 1e-12
+
+
+def pin_kda_uniform_equals_scalar():
+    """A per-channel decay vector with equal entries is the scalar decay."""
+    inp = small(channel=False, seed=51)
+    vec = {"S0": inp["S0"], "steps": []}
+    for st in inp["steps"]:
+        s2 = dict(st)
+        s2["alpha"] = np.repeat(st["alpha"][..., None], inp["S0"].shape[2], axis=-1)
+        vec["steps"].append(s2)
+    a = O.beam_decode(inp["S0"], inp["steps"])
+    b = O.beam_decode(vec["S0"], vec["steps"])
+    for t in range(len(inp["steps"])):
+        assert rel(b["o"][t], a["o"][t]) < 1e-14
+
+
+def pin_sequence_equals_single_beam():
+    """Independent sequences = one beam that always extends itself."""
+    R, H, dk, dv, T, M = 3, 2, 8, 6, 8, 4
+    seq = synth.make_sequence_inputs(R=R, H=H, dk=dk, dv=dv, T=T, s0_std=0.3, seed=61)
+    ref = O.sequence_decode(seq["S0"], seq["tokens"], M)
+    steps = []
+    for i in range(M):
+        st = {n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")}
+        if i:
+            st["parent"] = np.zeros((R, 1), np.int32)
+        steps.append(st)
+    beam = O.beam_decode(seq["S0"], steps)
+    for i in range(M):
+        o = beam["o"][i][:, 0].reshape(R * H, dv)  # rows in (r, h) order, as ref
+        assert rel(ref["o"][i], o) < 1e-14
+    pairs = [(r, 0) for r in range(R)]
+    S = O.beam_states(seq["S0"], steps, M - 1, pairs)
+    assert rel(ref["bases"][0], S.reshape(R * H, dk, dv)) < 1e-14
+
+
+def pin_bruteforce_tiny():
+    """Every parent vector at step 1 of a W = 4, L = 3 decode (4^4 cases)."""
+    base = synth.make_inputs(R=1, H=2, dk=16, dv=16, W=4, L=3, s0_std=0.1, seed=0,
+                             parents="uniform")
+    for pv in itertools.product(range(4), repeat=4):
+        inp = {"S0": base["S0"], "steps": [dict(s) for s in base["steps"]]}
+        inp["steps"][1]["parent"] = np.array([pv], np.int32)
+        a = O.beam_decode(inp["S0"], inp["steps"])
+        b = O.beam_decode_replay(inp["S0"], inp["steps"])
+        for t in range(3):
+            assert rel(b["o"][t], a["o"][t]) < 1e-12
+            for bb in range(4):
+                assert [int(x) for x in a["anc"][t][0, bb]] == _chain_slots(inp, t, 0, bb)[:-1]
+        Sx = _unrolled_state(inp, 2, 0, int(pv[1]) % 4, 1, False)
+        S = O.beam_states(inp["S0"], inp["steps"], 2, [(0, int(pv[1]) % 4)], heads=[1])
+        assert rel(S[0, 1], Sx) < 1e-12
+
+
+ALL_PINS = {
+    "hand_worked": pin_hand_worked,
+    "ancestry_walk": pin_ancestry_walk,
+    "ancestry_identity_fanout": pin_ancestry_identity_and_fanout,
+    "beta_zero_scalar": lambda: pin_beta_zero(False),
+    "beta_zero_channel": lambda: pin_beta_zero(True),
+    "orthonormal_retrieval": pin_orthonormal_retrieval,
+    "delta_rule_write": pin_delta_rule_write,
+    "unrolled_scalar": lambda: pin_unrolled_closed_form(False),
+    "unrolled_channel": lambda: pin_unrolled_closed_form(True),
+    "unrolled_square_scalar": lambda: pin_unrolled_closed_form(False, square=True),
+    "unrolled_square_channel": lambda: pin_unrolled_closed_form(True, square=True),
+    "replay_scalar": lambda: pin_replay_equals_eager(False),
+    "replay_square_channel": lambda: pin_replay_equals_eager(True, square=True),
+    "replay_channel": lambda: pin_replay_equals_eager(True),
+    "kda_uniform_scalar": pin_kda_uniform_equals_scalar,
+    "sequence_single_beam": pin_sequence_equals_single_beam,
+}

@@ -1,0 +1,48 @@
+"""The byte model against the capacity and write figures printed on the OneLA
+page (§4.4, Figure 8b), and against its own definitions."""
+
+import json
+import os
+
+import numpy as np
+from linear_attention_beam_gdn_amd import accounting as A
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _matches_printed(x, printed, digits=3):
+    """x rounds to ``printed`` at the page's 3 significant digits (halves up)."""
+    ulp = 10.0 ** (np.floor(np.log10(abs(printed))) - digits + 1)
+    return abs(x - printed) <= 0.5 * ulp + 1e-9
+
+
+def test_fig8b_capacity_and_writes():
+    g = json.load(open(os.path.join(GOLDEN, "onela_fig8b_state_bytes.json")))
+    geo = g["geometry"]
+    for row in g["printed"]:
+        got = A.onela_fig8b(R=geo["R"], W=geo["W"], H=geo["H"], K=geo["K"], V=geo["V"],
+                            O=row["O"], record_bytes_per_head=g["record_bytes_per_head"])
+        assert _matches_printed(got["capacity_mib"], row["capacity_mib"]), got
+        assert _matches_printed(got["writes_mib"], row["writes_mib"]), got
+        assert _matches_printed(got["capacity_ratio"], row["capacity_reduction_vs_fullstate"]), got
+        assert round(got["write_ratio"]) == row["write_reduction_vs_fullstate"]
+
+
+def test_record_and_input_sizes():
+    assert A.record_bytes(128, 128) == 772
+    assert A.record_bytes(128, 128, channel_decay=True) == 1280
+    assert A.input_bytes(128, 128) == 776
+    assert A.input_bytes(128, 128, channel_decay=True) == 1284
+
+
+def test_large_beam_step_bytes_per_beam_gather():
+    # 8 requests x 512 beams, H = 32, d_k = d_v = 128, 4 steps
+    tot = sum(A.beam_step_bytes(R=8, H=32, dk=128, dv=128, W_t=512, t=t) for t in range(4))
+    anc = sum(4 * 8 * 512 * 2 * t for t in range(4))
+    assert tot - anc == 4 * 286_785_536 + 6 * 101_187_584
+
+
+def test_unique_ancestors():
+    row = np.array([[0, 1], [0, 1], [0, 2], [3, 2]])
+    assert A.unique_ancestors(row, 4) == 2 + 2
+    assert A.unique_ancestors(row, 2) == 1 + 1
