@@ -1,0 +1,150 @@
+/*
+ * gdn_beam.h -- C ABI of the GDN large-beam decode library (libgdnbeam.so,
+ * built for AMD gfx950 / MI355X).
+ *
+ * The method.  Gated DeltaNet keeps one recurrent state per head and updates
+ * it once per token (OneLA, "Scaling Linear-Attention Decoding to Large Beams
+ * in Generative Recommendation", §2.2).  For large-beam decoding every beam of
+ * a request starts from one shared post-prefill state and diverges only
+ * through a few decode steps (§2.4, §3.1).  So a beam is stored as
+ *   - the request's shared state S0 (kept once), plus
+ *   - an append-only chain of transition records r_t = (alpha_t, delta_t, k_t),
+ *     delta_t = beta_t (v_t - alpha_t S_{t-1}^T k_t)              (§3.2),
+ *   - found through an ancestry index h_t(b, j): the slot written at step j by
+ *     the ancestor of beam b (§3.3).
+ * Each decode step replays a beam's records on the two projections S^T q and
+ * S^T k it needs, never rebuilding the state (§3.2 replay equations), and
+ * appends the beam's new record (§3.4).  The same store, with one beam per
+ * request, is the bounded log of DeltaLog ("Deferred Materialization of
+ * Recurrent States for Linear Attention Decoding", Figure 4): a dense base
+ * plus up to L_max records, folded back into the base by a merge.
+ *
+ * Orientation.  States are stored [d_k][d_v] (d_v contiguous), the transpose
+ * of OneLA's d_v x d_k notation, so o_t = S_t^T q_t and
+ *   S_t = alpha_t S_{t-1} + k_t delta_t^T.
+ * With per-channel decay (the KDA row of DeltaLog Table 1) alpha_t is a d_k
+ * vector scaling the rows of S_{t-1}.
+ *
+ * Conventions for every entry point.
+ *   - All tensors are row-major and contiguous, in device memory, and owned
+ *     by the caller.  The library never allocates, frees or synchronises.
+ *   - "bf16" means raw bfloat16 bit patterns in uint16_t.
+ *   - Tensors must be 16-byte aligned; int32 index arrays 4-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; execution errors surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is enqueued and a negative status is returned.
+ *   - No global mutable state: calls on different stores or streams are
+ *     independent.  Calls that write the same store must be stream-ordered.
+ */
+#ifndef GDN_BEAM_H
+#define GDN_BEAM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_BEAM_ABI_VERSION 1
+
+/* status codes */
+#define GDN_OK 0
+#define GDN_EINVAL (-1)       /* null/misaligned pointer, index or size out of range */
+#define GDN_EUNSUPPORTED (-2) /* (d_k, d_v) pair or decay kind not built in */
+#define GDN_EHIP (-3)         /* the HIP runtime rejected a kernel launch */
+
+/* decay kinds */
+#define GDN_DECAY_SCALAR 0  /* GDN: one alpha per (beam, head, step)      */
+#define GDN_DECAY_CHANNEL 1 /* KDA: one alpha per key channel (A = d_k)   */
+
+/* largest L_max (records per chain / log capacity) */
+#define GDN_MAX_STEPS 16
+
+/* Geometry of a store.  A = 1 for GDN_DECAY_SCALAR, A = dk for _CHANNEL.
+ * Built-in (dk, dv): (16,16) (32,32) (64,64) (128,128). */
+typedef struct gdn_shape {
+  int32_t R;          /* requests (W_max == 1: independent sequences)  >= 1 */
+  int32_t W_max;      /* beam slots per step                            >= 1 */
+  int32_t H;          /* heads                                          >= 1 */
+  int32_t dk;         /* key head dim                                        */
+  int32_t dv;         /* value head dim                                      */
+  int32_t L_max;      /* steps held (1 .. GDN_MAX_STEPS)                     */
+  int32_t decay_kind; /* GDN_DECAY_SCALAR or GDN_DECAY_CHANNEL               */
+} gdn_shape;
+
+/* The record / ancestry store (caller-allocated device memory). */
+typedef struct gdn_store {
+  float* S;          /* [R][H][dk][dv]  FP32 shared state (dense base)       */
+  float* rec_delta;  /* [L_max][R][W_max][H][dv]  FP32 update vectors delta  */
+  uint16_t* rec_k;   /* [L_max][R][W_max][H][dk]  bf16 keys (bit copies)     */
+  float* rec_alpha;  /* [L_max][R][W_max][H][A]   FP32 decays                */
+  int32_t* anc;      /* [L_max][R][W_max][L_max]  ancestry: anc[t][r][b][j] =
+                        h_t(b, j), j < t (entries j >= t unused)             */
+} gdn_store;
+
+/*
+ * One decode step t for all R requests, W_t beams and H heads (OneLA §3.3,
+ * §3.4; replay equations of §3.2).  In one kernel:
+ *   1. ancestry: h_t(b, t-1) = parent[r][b], h_t(b, j) = h_{t-1}(parent, j)
+ *      for j < t-1, written to anc[t][r][b][0..t-1] (skipped at t == 0);
+ *   2. u_q = S[r]^T q and u_k = S[r]^T k for every beam (for channel decay
+ *      the probes are (prod_{i<=t} a_i) * q and * k over the beam's chain);
+ *   3. replay of the records at (j, h_t(b, j)), j < t, on u_q and u_k;
+ *   4. delta_t = beta_t (v_t - alpha_t u_k), o_t = alpha_t u_q +
+ *      delta_t (k_t . q_t) (channel decay: alpha_t sits in the probes);
+ *   5. writes o and appends (alpha_t, delta_t, k_t) at slot (t, r, b).
+ * Records of steps j < t are only read.
+ *
+ *   t       step index, 0 <= t < L_max; the chain of step t has t records
+ *   W_t     beams at this step, 1 <= W_t <= W_max
+ *   parent  int32 [R][W_t]: parent slot (in step t-1) of each beam; ignored
+ *           (may be NULL) at t == 0.  Precondition: 0 <= parent < W_{t-1}.
+ *           Out-of-range values are clamped into [0, W_max) so no access
+ *           leaves the store, but the result is then meaningless.
+ *   q, k    bf16 [R][W_t][H][dk];  v  bf16 [R][W_t][H][dv]
+ *   alpha   FP32 [R][W_t][H][A];   beta FP32 [R][W_t][H]
+ *   o       FP32 [R][W_t][H][dv] (output)
+ * With W_max == 1 this is one token of DeltaLog-style decoding of R
+ * independent sequences: S is the dense base and t is the current log length.
+ */
+int gdn_beam_decode_step(const gdn_shape* shape, const gdn_store* store, int32_t t,
+                         int32_t W_t, const int32_t* parent, const uint16_t* q,
+                         const uint16_t* k, const uint16_t* v, const float* alpha,
+                         const float* beta, float* o, void* stream);
+
+/*
+ * Dense states after step t of n beams (the conceptual S_{t,b} of OneLA §3.1,
+ * which decoding itself never forms): S[r] folded with the beam's ancestral
+ * records and its own step-t record, S <- alpha_j S + k_j delta_j^T in chain
+ * order (channel decay: S <- diag(a_j) S + k_j delta_j^T).
+ *   t      0 <= t < L_max (anc row t must have been written by step t)
+ *   rb     int32 [n][2] device array of (request, beam) pairs, beam < W_t
+ *   n      >= 0 (0: nothing is enqueued)
+ *   S_out  FP32 [n][H][dk][dv] (output; must not overlap the store)
+ */
+int gdn_materialize(const gdn_shape* shape, const gdn_store* store, int32_t t,
+                    const int32_t* rb, int32_t n, float* S_out, void* stream);
+
+/*
+ * Bounded-log merge (DeltaLog Figure 4 and Figure 5 caption): fold, for every
+ * request r, the first n_rec records of beam `beam`'s chain (its ancestors at
+ * steps 0..n_rec-2 and its own record at step n_rec-1) into S[r] in place.
+ * The caller then restarts decoding at t = 0 on the new base.
+ *   n_rec  1 <= n_rec <= L_max
+ *   beam   0 <= beam < W_max (0 for independent sequences)
+ */
+int gdn_log_merge(const gdn_shape* shape, const gdn_store* store, int32_t n_rec,
+                  int32_t beam, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* gdn_status_string(int status);
+
+/* GDN_BEAM_ABI_VERSION of the built library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_BEAM_H */

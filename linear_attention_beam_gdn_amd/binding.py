@@ -1,0 +1,185 @@
+"""ctypes binding of libgdnbeam.so (C ABI in include/gdn_beam.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch provides device memory and the stream; there is no CPU
+fallback, and a missing library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdnbeam.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "gdn_beam.h")
+
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP = 0, -1, -2, -3
+GDN_DECAY_SCALAR, GDN_DECAY_CHANNEL = 0, 1
+GDN_MAX_STEPS = 16
+
+
+class GdnShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("R", "W_max", "H", "dk", "dv", "L_max", "decay_kind")]
+
+
+class GdnStore(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("S", "rec_delta", "rec_k", "rec_alpha", "anc")]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgdnbeam.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m linear_attention_beam_gdn_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32 = ctypes.c_void_p, ctypes.c_int32
+        L.gdn_beam_decode_step.argtypes = [ctypes.POINTER(GdnShape), ctypes.POINTER(GdnStore), I32, I32,
+                                           P, P, P, P, P, P, P, P]
+        L.gdn_beam_decode_step.restype = ctypes.c_int
+        L.gdn_materialize.argtypes = [ctypes.POINTER(GdnShape), ctypes.POINTER(GdnStore), I32, P, I32, P, P]
+        L.gdn_materialize.restype = ctypes.c_int
+        L.gdn_log_merge.argtypes = [ctypes.POINTER(GdnShape), ctypes.POINTER(GdnStore), I32, I32, P]
+        L.gdn_log_merge.restype = ctypes.c_int
+        L.gdn_status_string.argtypes = [ctypes.c_int]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_abi_version.argtypes = []
+        L.gdn_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/gdn_beam.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+)\s*\(", text, flags=re.M)
+
+
+def status_string(status: int) -> str:
+    return lib().gdn_status_string(int(status)).decode()
+
+
+def _ptr(x) -> int | None:
+    return None if x is None else x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(t: torch.Tensor, name: str, dtypes, shape):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (there is no CPU path)")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+
+
+_BF16 = (torch.bfloat16, torch.int16)
+
+
+class Store:
+    """Caller-owned record / ancestry store (device memory from PyTorch).
+
+    S [R,H,dk,dv] FP32, rec_delta [L,R,W,H,dv] FP32, rec_k [L,R,W,H,dk] bf16,
+    rec_alpha [L,R,W,H,A] FP32, anc [L,R,W,L] int32.
+    """
+
+    def __init__(self, R, W_max, H, dk, dv, L_max, channel_decay=False, device="cuda", S=None):
+        self.R, self.W_max, self.H, self.dk, self.dv, self.L_max = R, W_max, H, dk, dv, L_max
+        self.channel_decay = bool(channel_decay)
+        self.A = dk if channel_decay else 1
+        f32 = dict(dtype=torch.float32, device=device)
+        if S is None:
+            self.S = torch.zeros(R, H, dk, dv, **f32)
+        else:
+            _check(S, "S", (torch.float32,), (R, H, dk, dv))
+            self.S = S
+        self.rec_delta = torch.zeros(L_max, R, W_max, H, dv, **f32)
+        self.rec_k = torch.zeros(L_max, R, W_max, H, dk, dtype=torch.bfloat16, device=device)
+        self.rec_alpha = torch.zeros(L_max, R, W_max, H, self.A, **f32)
+        self.anc = torch.zeros(L_max, R, W_max, L_max, dtype=torch.int32, device=device)
+        self.shape = GdnShape(R, W_max, H, dk, dv, L_max,
+                              GDN_DECAY_CHANNEL if channel_decay else GDN_DECAY_SCALAR)
+        self.cstore = GdnStore(_ptr(self.S), _ptr(self.rec_delta), _ptr(self.rec_k),
+                               _ptr(self.rec_alpha), _ptr(self.anc))
+
+
+def decode_step(store: Store, t, W_t, parent, q, k, v, alpha, beta, o=None, stream=None):
+    """One decode step (gdn_beam_decode_step); returns o [R,W_t,H,dv] FP32."""
+    R, H, dk, dv = store.R, store.H, store.dk, store.dv
+    _check(q, "q", _BF16, (R, W_t, H, dk))
+    _check(k, "k", _BF16, (R, W_t, H, dk))
+    _check(v, "v", _BF16, (R, W_t, H, dv))
+    a_shape = (R, W_t, H, dk) if store.channel_decay else (R, W_t, H)
+    _check(alpha, "alpha", (torch.float32,), a_shape)
+    _check(beta, "beta", (torch.float32,), (R, W_t, H))
+    if t > 0:
+        _check(parent, "parent", (torch.int32,), (R, W_t))
+    if o is None:
+        o = torch.empty(R, W_t, H, dv, dtype=torch.float32, device=q.device)
+    _check(o, "o", (torch.float32,), (R, W_t, H, dv))
+    rc = lib().gdn_beam_decode_step(ctypes.byref(store.shape), ctypes.byref(store.cstore), t, W_t,
+                                    _ptr(parent) if t > 0 else None, _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_beam_decode_step")
+    return o
+
+
+def materialize(store: Store, t, rb, out=None, stream=None):
+    """Dense states after step t of the (request, beam) pairs rb [n,2] int32."""
+    n = int(rb.shape[0])
+    _check(rb, "rb", (torch.int32,), (n, 2))
+    if out is None:
+        out = torch.empty(n, store.H, store.dk, store.dv, dtype=torch.float32, device=rb.device)
+    _check(out, "S_out", (torch.float32,), (n, store.H, store.dk, store.dv))
+    rc = lib().gdn_materialize(ctypes.byref(store.shape), ctypes.byref(store.cstore), t, _ptr(rb), n,
+                               _ptr(out), _stream(stream))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_materialize")
+    return out
+
+
+def log_merge(store: Store, n_rec, beam=0, stream=None):
+    """Fold the first n_rec records of `beam`'s chain into store.S in place."""
+    rc = lib().gdn_log_merge(ctypes.byref(store.shape), ctypes.byref(store.cstore), n_rec, beam,
+                             _stream(stream))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_log_merge")
+
+
+def upload(arrays: dict, device="cuda") -> dict:
+    """Copy a dict of numpy input arrays to device tensors of the ABI's dtypes
+    (uint16 bf16 bit patterns -> torch.bfloat16, float32, int32)."""
+    import numpy as np
+
+    out = {}
+    for name, a in arrays.items():
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            out[name] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        elif a.dtype in (np.float32, np.int32):
+            out[name] = torch.from_numpy(a).to(device)
+        else:
+            raise TypeError(f"{name}: unexpected dtype {a.dtype}")
+    return out

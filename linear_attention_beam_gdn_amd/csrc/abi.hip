@@ -1,0 +1,101 @@
+// C ABI of libgdnbeam (declared in include/gdn_beam.h): host-side argument
+// validation, then dispatch to the gfx950 kernels on the caller's stream.
+// Validation touches no HIP API, so every error path runs without a GPU.
+#include <stdint.h>
+
+#include "gdn_beam.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+bool dims_supported(int dk, int dv) {
+  return (dk == 16 && dv == 16) || (dk == 32 && dv == 32) || (dk == 64 && dv == 64) ||
+         (dk == 128 && dv == 128);
+}
+
+}  // namespace gdn
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(const gdn_shape* s) {
+  if (s == nullptr) return GDN_EINVAL;
+  if (s->R < 1 || s->W_max < 1 || s->H < 1 || s->L_max < 1 || s->L_max > GDN_MAX_STEPS)
+    return GDN_EINVAL;
+  if (s->decay_kind != GDN_DECAY_SCALAR && s->decay_kind != GDN_DECAY_CHANNEL) return GDN_EUNSUPPORTED;
+  if (!gdn::dims_supported(s->dk, s->dv)) return GDN_EUNSUPPORTED;
+  // element counts of the largest arrays must stay far from 2^63
+  const double recs = (double)s->L_max * s->R * s->W_max * s->H * (s->dk > s->dv ? s->dk : s->dv);
+  const double anc = (double)s->L_max * s->R * s->W_max * s->L_max;
+  if (recs > 4.0e18 || anc > 4.0e18) return GDN_EINVAL;
+  return GDN_OK;
+}
+
+int check_store(const gdn_store* st) {
+  if (st == nullptr) return GDN_EINVAL;
+  if (!aligned(st->S, 16) || !aligned(st->rec_delta, 16) || !aligned(st->rec_k, 16) ||
+      !aligned(st->rec_alpha, 16) || !aligned(st->anc, 16))
+    return GDN_EINVAL;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_BEAM_ABI_VERSION; }
+
+const char* gdn_status_string(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_EINVAL: return "invalid argument (null or misaligned pointer, index or size out of range)";
+    case GDN_EUNSUPPORTED: return "unsupported head dims or decay kind";
+    case GDN_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int gdn_beam_decode_step(const gdn_shape* shape, const gdn_store* store, int32_t t, int32_t W_t,
+                         const int32_t* parent, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, const float* alpha, const float* beta, float* o,
+                         void* stream) {
+  int rc = check_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if ((rc = check_store(store)) != GDN_OK) return rc;
+  if (t < 0 || t >= shape->L_max) return GDN_EINVAL;
+  if (W_t < 1 || W_t > shape->W_max) return GDN_EINVAL;
+  if (t > 0 && !aligned(parent, 4)) return GDN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 16) ||
+      !aligned(beta, 16) || !aligned(o, 16))
+    return GDN_EINVAL;
+  const gdn::StepIO io{parent, q, k, v, alpha, beta, o};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (shape->W_max == 1) return gdn::launch_seq_decode(*shape, *store, t, io, s);
+  return gdn::launch_beam_decode(*shape, *store, t, W_t, io, s);
+}
+
+int gdn_materialize(const gdn_shape* shape, const gdn_store* store, int32_t t, const int32_t* rb,
+                    int32_t n, float* S_out, void* stream) {
+  int rc = check_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if ((rc = check_store(store)) != GDN_OK) return rc;
+  if (t < 0 || t >= shape->L_max || n < 0) return GDN_EINVAL;
+  if (n == 0) return GDN_OK;
+  if (!aligned(rb, 4) || !aligned(S_out, 16)) return GDN_EINVAL;
+  return gdn::launch_fold(*shape, *store, t, rb, 0, n, store->S, S_out, true,
+                          reinterpret_cast<hipStream_t>(stream));
+}
+
+int gdn_log_merge(const gdn_shape* shape, const gdn_store* store, int32_t n_rec, int32_t beam,
+                  void* stream) {
+  int rc = check_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if ((rc = check_store(store)) != GDN_OK) return rc;
+  if (n_rec < 1 || n_rec > shape->L_max) return GDN_EINVAL;
+  if (beam < 0 || beam >= shape->W_max) return GDN_EINVAL;
+  return gdn::launch_fold(*shape, *store, n_rec - 1, nullptr, beam, shape->R, store->S, store->S,
+                          false, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

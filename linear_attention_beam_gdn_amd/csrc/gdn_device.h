@@ -1,0 +1,52 @@
+// Device-side helpers shared by the gfx950 kernels of libgdnbeam.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_at(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Round-to-nearest-even FP32 -> bf16 bits (inputs here are finite).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Element e (0..7) of eight bf16 packed in a u32x4.
+__device__ __forceinline__ float bf16x8_elem(const u32x4& v, int e) {
+  const uint32_t w = v[e >> 1];
+  return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// Sum over the four 16-lane groups of a wave64 (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Sum over all 64 lanes of a wave.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+}  // namespace gdn

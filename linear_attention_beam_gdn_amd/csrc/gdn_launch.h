@@ -1,0 +1,40 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_beam.h"
+
+namespace gdn {
+
+// Per-step inputs and output of a decode call (layouts as in gdn_beam.h).
+struct StepIO {
+  const int32_t* parent;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* alpha;
+  const float* beta;
+  float* o;
+};
+
+bool dims_supported(int dk, int dv);
+
+// Beams sharing one state per request (W_max > 1).
+int launch_beam_decode(const gdn_shape& sh, const gdn_store& st, int t, int Wt,
+                       const StepIO& io, hipStream_t stream);
+
+// One beam per request (W_max == 1): bounded-log decoding of sequences.
+int launch_seq_decode(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io,
+                      hipStream_t stream);
+
+// Fold chains of records onto dense states.  Item i is the (request, beam)
+// pair rb[2i], rb[2i+1] (or (i, beam) when rb is NULL); its chain is the
+// ancestors in anc row t and its own record at step t.  Reads the state of
+// its request from `src` and writes either dst[i] (dst_per_item) or the
+// request's own state in place.
+int launch_fold(const gdn_shape& sh, const gdn_store& st, int t, const int32_t* rb, int beam,
+                int n, const float* src, float* dst, bool dst_per_item, hipStream_t stream);
+
+}  // namespace gdn

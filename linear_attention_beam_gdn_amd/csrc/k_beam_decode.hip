@@ -1,0 +1,443 @@
+// Fused shared-context decode step for beams that share one state per
+// request (OneLA §3.4, Figure 5; replay equations of §3.2; ancestry of §3.3).
+//
+// Work split.  One workgroup takes one (request r, head h) and a chunk of
+// beams.  Its NW waves split the d_v axis (RPW value rows each, the B_V tile
+// of §3.4) and each wave keeps its slice of the shared state S0[r,h] in
+// registers for the whole beam chunk, in the A-operand layout of the gfx950
+// bf16 MFMA (16x16x32): S0 is read from memory once per workgroup and reused
+// by every beam of the chunk.  FP32 S0 is split on chip into NPL bf16 planes
+// (hi + mid + lo); q and k arrive as bf16, so each plane product is exact and
+// the MFMA accumulates the projections S0^T q and S0^T k in FP32.
+//
+// Beams are processed 16 at a time (the MFMA N dimension).  Lane (g, c) of a
+// wave (g = lane / 16, c = lane % 16) owns beam c of the tile: it holds a
+// quarter of that beam's q and k (the B operand) and, after the MFMA, 4*MT
+// consecutive value rows of its projections (the C layout).  The dot products
+// k_j . q and k_j . k of the replay are reduced over the four lane groups of
+// the beam; the value-side updates are per lane, so the replay never leaves
+// registers.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+#include <stdlib.h>
+
+namespace gdn {
+namespace {
+
+struct BeamArgs {
+  const float* S;
+  float* rec_delta;
+  uint16_t* rec_k;
+  float* rec_alpha;
+  int32_t* anc;
+  const int32_t* parent;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* alpha;
+  const float* beta;
+  float* o;
+  int R, Wm, H, L, t, Wt;
+  int chunk, nchunk;
+};
+
+template <int DK, int DV>
+struct BeamGeom {
+  static_assert(DK == 16 || DK == 32 || DK % 64 == 0, "d_k must be 16, 32 or a multiple of 64");
+  static_assert(DV % 16 == 0, "d_v must be a multiple of 16");
+  static constexpr int RPW = (DV % 32 == 0) ? 32 : 16;  // value rows per wave
+  static constexpr int NW = DV / RPW;                   // waves per workgroup
+  static constexpr int MT = RPW / 16;                   // 16-row MFMA tiles per wave
+  static constexpr int KS = (DK + 31) / 32;             // 32-deep MFMA steps over d_k
+  static constexpr int VPL = 4 * MT;                    // value rows per lane
+};
+
+// First key channel of the 8 consecutive channels that lane group g feeds to
+// MFMA step s.  Any assignment works as long as the A and B operands use the
+// same one; this one gives each lane 16 (d_k >= 64) contiguous channels.
+template <int DK>
+__device__ __forceinline__ int kchunk(int g, int s) {
+  if constexpr (DK % 64 == 0) return (s >> 1) * 64 + g * 16 + (s & 1) * 8;
+  else return g * 8;
+}
+template <int DK>
+__device__ __forceinline__ bool klive(int g) {
+  if constexpr (DK == 16) return g < 2;  // lane groups 2, 3 feed zero padding
+  else return true;
+}
+
+__device__ __forceinline__ void load_f32x8(const float* p, float* x) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
+
+// Split eight FP32 values into bf16 planes: x ~= sum_p plane[p] (RNE each).
+template <int NP>
+__device__ __forceinline__ void split_planes(const float* x, u32x4* planes) {
+#pragma unroll
+  for (int p = 0; p < NP; ++p) planes[p] = u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float rem = x[e];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint32_t hb = bf16_rne(rem);
+      rem -= bf16_at(uint16_t(hb));
+      planes[p][e >> 1] |= hb << (16 * (e & 1));
+    }
+  }
+}
+
+template <int DK, int DV, bool CH, int NPL>
+__global__ __launch_bounds__((BeamGeom<DK, DV>::NW * 64)) void k_beam_decode(BeamArgs a) {
+  using G = BeamGeom<DK, DV>;
+  constexpr int A = CH ? DK : 1;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+
+  // Workgroups are handed to the 8 XCDs round-robin; renumber them so that
+  // the chunks of one (r, h) run on the same XCD and share its L2.
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int chunk_id = bid % a.nchunk;
+  const int rh = bid / a.nchunk;
+  const int h = rh % a.H;
+  const int r = rh / a.H;
+  const int b_begin = chunk_id * a.chunk;
+  const int b_end = min(b_begin + a.chunk, a.Wt);
+  const int t = a.t;
+  const int dv0 = w * G::RPW + g * G::VPL;  // first value row held by this lane
+
+  // ---- this wave's slice of S0[r, h] as bf16 planes in MFMA A layout.
+  // A row m of tile mt is value row w*RPW + (m/4)*VPL + mt*4 + m%4, so that
+  // C row 4g+i of tile mt lands on value row dv0 + mt*4 + i.
+  u32x4 As[G::MT][G::KS][NPL];
+  {
+    const float* S = a.S + ((size_t)r * a.H + h) * DK * DV;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt) {
+      const int col = w * G::RPW + (c >> 2) * G::VPL + mt * 4 + (c & 3);
+#pragma unroll
+      for (int s = 0; s < G::KS; ++s) {
+        const int k0 = kchunk<DK>(g, s);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = klive<DK>(g) ? S[(size_t)(k0 + e) * DV + col] : 0.f;
+        split_planes<NPL>(x, As[mt][s]);
+      }
+    }
+  }
+
+  const bool anc_writer = (h == 0) && (w == 0) && (g == 0);
+
+  for (int b0 = b_begin; b0 < b_end; b0 += 16) {
+    const int b = b0 + c;
+    const bool valid = b < b_end;
+    const size_t tok = ((size_t)r * a.Wt + (valid ? b : 0)) * a.H + h;
+    const size_t rec_t = (((size_t)t * a.R + r) * a.Wm + (valid ? b : 0)) * a.H + h;
+
+    // ---- ancestry (§3.3): parent slot and the parent's own ancestry row
+    int par = 0;
+    if (t > 0 && valid) par = clampi(a.parent[(size_t)r * a.Wt + b], 0, a.Wm - 1);
+    const int32_t* prow = a.anc + (((size_t)(t > 0 ? t - 1 : 0) * a.R + r) * a.Wm + par) * a.L;
+    auto slot_at = [&](int j) -> int {
+      if (!valid) return 0;
+      return j == t - 1 ? par : clampi(prow[j], 0, a.Wm - 1);
+    };
+    auto rec_at = [&](int j, int slot) -> size_t {
+      return (((size_t)j * a.R + r) * a.Wm + slot) * a.H + h;
+    };
+
+    // ---- current q and k (B operand chunks)
+    u32x4 qf[G::KS], kf[G::KS];
+#pragma unroll
+    for (int s = 0; s < G::KS; ++s) {
+      const int k0 = kchunk<DK>(g, s);
+      const bool ld = valid && klive<DK>(g);
+      qf[s] = ld ? *reinterpret_cast<const u32x4*>(a.q + tok * DK + k0) : u32x4{0, 0, 0, 0};
+      kf[s] = ld ? *reinterpret_cast<const u32x4*>(a.k + tok * DK + k0) : u32x4{0, 0, 0, 0};
+    }
+
+    // current decay: scalar, or this lane's key channels of the vector
+    float at = 0.f;
+    float acur[CH ? G::KS * 8 : 1];
+    if constexpr (!CH) {
+      at = valid ? a.alpha[tok] : 0.f;
+    } else {
+#pragma unroll
+      for (int s = 0; s < G::KS; ++s) {
+        if (valid && klive<DK>(g)) load_f32x8(a.alpha + tok * DK + kchunk<DK>(g, s), acur + 8 * s);
+        else
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acur[8 * s + e] = 0.f;
+      }
+    }
+
+    // ---- S0^T [q | k] on the matrix cores
+    f32x4 uq[G::MT], uk[G::MT];
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt) {
+      uq[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      uk[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if constexpr (!CH) {
+#pragma unroll
+      for (int s = 0; s < G::KS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+          for (int p = NPL - 1; p >= 0; --p) {
+            uq[mt] = mfma16x16x32(As[mt][s][p], qf[s], uq[mt]);
+            uk[mt] = mfma16x16x32(As[mt][s][p], kf[s], uk[mt]);
+          }
+    } else {
+      // Channel decay: the probes are (prod_{i<=t} a_i) * x over the beam's
+      // chain (FP32), split into two bf16 planes; plane pairs whose combined
+      // weight is below 2^-16 relative are dropped.
+      float cum[G::KS * 8];
+#pragma unroll
+      for (int i = 0; i < G::KS * 8; ++i) cum[i] = acur[i];
+      for (int j = 0; j < t; ++j) {
+        const size_t rj = rec_at(j, slot_at(j));
+#pragma unroll
+        for (int s = 0; s < G::KS; ++s) {
+          float aj[8];
+          if (valid && klive<DK>(g)) load_f32x8(a.rec_alpha + rj * A + kchunk<DK>(g, s), aj);
+          else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) aj[e] = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cum[8 * s + e] *= aj[e];
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < G::KS; ++s) {
+        float xq[8], xk[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xq[e] = cum[8 * s + e] * bf16x8_elem(qf[s], e);
+          xk[e] = cum[8 * s + e] * bf16x8_elem(kf[s], e);
+        }
+        u32x4 pq[2], pk[2];
+        split_planes<2>(xq, pq);
+        split_planes<2>(xk, pk);
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) {
+#pragma unroll
+          for (int pa = NPL - 1; pa >= 0; --pa)
+#pragma unroll
+            for (int pb = 1; pb >= 0; --pb) {
+              if (pa + pb >= NPL) continue;
+              uq[mt] = mfma16x16x32(As[mt][s][pa], pq[pb], uq[mt]);
+              uk[mt] = mfma16x16x32(As[mt][s][pa], pk[pb], uk[mt]);
+            }
+        }
+      }
+    }
+
+    // k_t . q_t
+    float sqq = 0.f;
+#pragma unroll
+    for (int s = 0; s < G::KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sqq += bf16x8_elem(kf[s], e) * bf16x8_elem(qf[s], e);
+    sqq = sum_lane_groups(sqq);
+
+    // ---- replay of the ancestral records (§3.2), gathered through h_t
+    if constexpr (!CH) {
+      for (int j = 0; j < t; ++j) {
+        const int slot = slot_at(j);
+        if (anc_writer && valid) a.anc[(((size_t)t * a.R + r) * a.Wm + b) * a.L + j] = slot;
+        const size_t rj = rec_at(j, slot);
+        float pq = 0.f, pk = 0.f;
+#pragma unroll
+        for (int s = 0; s < G::KS; ++s) {
+          const bool ld = valid && klive<DK>(g);
+          const u32x4 kj = ld ? *reinterpret_cast<const u32x4*>(a.rec_k + rj * DK + kchunk<DK>(g, s))
+                              : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float kje = bf16x8_elem(kj, e);
+            pq += kje * bf16x8_elem(qf[s], e);
+            pk += kje * bf16x8_elem(kf[s], e);
+          }
+        }
+        pq = sum_lane_groups(pq);
+        pk = sum_lane_groups(pk);
+        const float aj = valid ? a.rec_alpha[rj] : 0.f;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) {
+          const f32x4 dj = valid ? *reinterpret_cast<const f32x4*>(a.rec_delta + rj * DV + dv0 + mt * 4)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uq[mt][i] = aj * uq[mt][i] + dj[i] * pq;
+            uk[mt][i] = aj * uk[mt][i] + dj[i] * pk;
+          }
+        }
+      }
+    } else {
+      // S_j^T y = S_{j-1}^T (a_j * y) + delta_j (k_j . y), from j = t-1 down;
+      // P holds prod_{i=j+1..t} a_i on this lane's key channels.
+      float P[G::KS * 8];
+#pragma unroll
+      for (int i = 0; i < G::KS * 8; ++i) P[i] = acur[i];
+      for (int j = t - 1; j >= 0; --j) {
+        const int slot = slot_at(j);
+        if (anc_writer && valid) a.anc[(((size_t)t * a.R + r) * a.Wm + b) * a.L + j] = slot;
+        const size_t rj = rec_at(j, slot);
+        float pq = 0.f, pk = 0.f;
+#pragma unroll
+        for (int s = 0; s < G::KS; ++s) {
+          const bool ld = valid && klive<DK>(g);
+          const u32x4 kj = ld ? *reinterpret_cast<const u32x4*>(a.rec_k + rj * DK + kchunk<DK>(g, s))
+                              : u32x4{0, 0, 0, 0};
+          float aj[8];
+          if (ld) load_f32x8(a.rec_alpha + rj * A + kchunk<DK>(g, s), aj);
+          else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) aj[e] = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float y = bf16x8_elem(kj, e) * P[8 * s + e];
+            pq += y * bf16x8_elem(qf[s], e);
+            pk += y * bf16x8_elem(kf[s], e);
+            P[8 * s + e] *= aj[e];
+          }
+        }
+        pq = sum_lane_groups(pq);
+        pk = sum_lane_groups(pk);
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) {
+          const f32x4 dj = valid ? *reinterpret_cast<const f32x4*>(a.rec_delta + rj * DV + dv0 + mt * 4)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uq[mt][i] += dj[i] * pq;
+            uk[mt][i] += dj[i] * pk;
+          }
+        }
+      }
+    }
+
+    // ---- current transition and append (§3.2, §3.4)
+    if (valid) {
+      const float bt = a.beta[tok];
+      float vv[G::VPL];
+      if constexpr (G::VPL == 8) {
+        const u32x4 vw = *reinterpret_cast<const u32x4*>(a.v + tok * DV + dv0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vv[i] = bf16x8_elem(vw, i);
+      } else {
+        const u32x2 vw = *reinterpret_cast<const u32x2*>(a.v + tok * DV + dv0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vv[i] = (i & 1) ? bf16_hi(vw[i >> 1]) : bf16_lo(vw[i >> 1]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt) {
+        f32x4 d, out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (!CH) {
+            d[i] = bt * (vv[mt * 4 + i] - at * uk[mt][i]);
+            out[i] = at * uq[mt][i] + d[i] * sqq;
+          } else {
+            d[i] = bt * (vv[mt * 4 + i] - uk[mt][i]);
+            out[i] = uq[mt][i] + d[i] * sqq;
+          }
+        }
+        *reinterpret_cast<f32x4*>(a.o + tok * DV + dv0 + mt * 4) = out;
+        *reinterpret_cast<f32x4*>(a.rec_delta + rec_t * DV + dv0 + mt * 4) = d;
+      }
+      if (w == 0 && klive<DK>(g)) {
+#pragma unroll
+        for (int s = 0; s < G::KS; ++s) {
+          const int k0 = kchunk<DK>(g, s);
+          *reinterpret_cast<u32x4*>(a.rec_k + rec_t * DK + k0) = kf[s];
+          if constexpr (CH) {
+            *reinterpret_cast<f32x4*>(a.rec_alpha + rec_t * A + k0) =
+                f32x4{acur[8 * s], acur[8 * s + 1], acur[8 * s + 2], acur[8 * s + 3]};
+            *reinterpret_cast<f32x4*>(a.rec_alpha + rec_t * A + k0 + 4) =
+                f32x4{acur[8 * s + 4], acur[8 * s + 5], acur[8 * s + 6], acur[8 * s + 7]};
+          }
+        }
+        if constexpr (!CH)
+          if (g == 0) a.rec_alpha[rec_t] = at;
+      }
+    }
+  }
+}
+
+// Beams per workgroup: a multiple of 16, sized so that the grid holds about
+// 2048 workgroups (8 per CU) when the beam count allows it.
+int pick_chunk(int RH, int Wt) {
+  if (const char* e = getenv("GDN_BEAM_CHUNK")) {
+    const int v = atoi(e);
+    if (v >= 16 && v % 16 == 0) return v;
+  }
+  const long want = ((long)RH * Wt + 2047) / 2048;
+  int chunk = (int)((want + 15) / 16) * 16;
+  if (chunk < 16) chunk = 16;
+  const int full = (Wt + 15) / 16 * 16;
+  return chunk > full ? full : chunk;
+}
+
+template <int DK, int DV, bool CH>
+int launch(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
+           hipStream_t stream) {
+  constexpr int NPL = CH ? 2 : 3;
+  BeamArgs a;
+  a.S = st.S;
+  a.rec_delta = st.rec_delta;
+  a.rec_k = st.rec_k;
+  a.rec_alpha = st.rec_alpha;
+  a.anc = st.anc;
+  a.parent = io.parent;
+  a.q = io.q;
+  a.k = io.k;
+  a.v = io.v;
+  a.alpha = io.alpha;
+  a.beta = io.beta;
+  a.o = io.o;
+  a.R = sh.R;
+  a.Wm = sh.W_max;
+  a.H = sh.H;
+  a.L = sh.L_max;
+  a.t = t;
+  a.Wt = Wt;
+  a.chunk = pick_chunk(sh.R * sh.H, Wt);
+  a.nchunk = (Wt + a.chunk - 1) / a.chunk;
+  const long grid = (long)sh.R * sh.H * a.nchunk;
+  if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
+  hipLaunchKernelGGL((k_beam_decode<DK, DV, CH, NPL>), dim3((unsigned)grid),
+                     dim3(BeamGeom<DK, DV>::NW * 64), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+}  // namespace
+
+int launch_beam_decode(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
+                       hipStream_t stream) {
+  const bool ch = sh.decay_kind == GDN_DECAY_CHANNEL;
+#define GDN_CASE(DK_, DV_)                                                       \
+  if (sh.dk == DK_ && sh.dv == DV_)                                              \
+    return ch ? launch<DK_, DV_, true>(sh, st, t, Wt, io, stream)                \
+              : launch<DK_, DV_, false>(sh, st, t, Wt, io, stream);
+  GDN_CASE(16, 16)
+  GDN_CASE(32, 32)
+  GDN_CASE(64, 64)
+  GDN_CASE(128, 128)
+#undef GDN_CASE
+  return GDN_EUNSUPPORTED;
+}
+
+}  // namespace gdn

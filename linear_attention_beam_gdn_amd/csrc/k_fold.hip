@@ -1,0 +1,129 @@
+// Fold a chain of transition records onto a dense state:
+//   S <- alpha_j S + k_j delta_j^T       (channel decay: diag(a_j) S + ...)
+// in chain order.  This is the eager GDN update written with the stored
+// record r_j = (alpha_j, delta_j, k_j) (OneLA §3.2, GTR equation), so the
+// result is the dense state the chain stands for.  It serves the bounded-log
+// merge of DeltaLog (Figure 4: at a full log the logical state is written
+// back into the dense base; Figure 5: the merge writes back base tiles) and
+// the materialisation of any beam's state.
+//
+// One workgroup per (item, head): each thread owns RPG rows x 4 columns of
+// the [d_k][d_v] state in registers, streams them in and out with 16-byte
+// accesses, and applies every record to them; the key entries and decays of
+// a record are the same for a whole row, the update vector for a column.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+struct FoldArgs {
+  const float* src;
+  float* dst;
+  const float* rec_delta;
+  const uint16_t* rec_k;
+  const float* rec_alpha;
+  const int32_t* anc;
+  const int32_t* rb;
+  int R, Wm, H, L, t, beam;
+  int dst_per_item;
+};
+
+template <int DK, int DV>
+struct FoldGeom {
+  static constexpr int C4 = DV / 4;
+  static constexpr int NRG0 = 256 / C4;
+  static constexpr int NRG = NRG0 < DK ? NRG0 : DK;
+  static_assert(DK % NRG == 0, "d_k must split evenly over row groups");
+  static constexpr int RPG = DK / NRG;
+  static constexpr int NT = C4 * NRG;
+};
+
+template <int DK, int DV, bool CH>
+__global__ __launch_bounds__((FoldGeom<DK, DV>::NT)) void k_fold(FoldArgs a) {
+  using G = FoldGeom<DK, DV>;
+  constexpr int A = CH ? DK : 1;
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x % a.H;
+  const int item = blockIdx.x / a.H;
+  const int c4 = tid % G::C4;
+  const int rg = tid / G::C4;
+  int r = item, b = a.beam;
+  if (a.rb) {
+    r = a.rb[2 * item];
+    b = a.rb[2 * item + 1];
+  }
+  r = clampi(r, 0, a.R - 1);
+  b = clampi(b, 0, a.Wm - 1);
+  const int t = a.t;
+
+  const float* src = a.src + ((size_t)r * a.H + h) * DK * DV;
+  float* dst = a.dst_per_item ? a.dst + ((size_t)item * a.H + h) * DK * DV
+                              : a.dst + ((size_t)r * a.H + h) * DK * DV;
+  f32x4 st[G::RPG];
+#pragma unroll
+  for (int i = 0; i < G::RPG; ++i)
+    st[i] = *reinterpret_cast<const f32x4*>(src + (size_t)(rg * G::RPG + i) * DV + c4 * 4);
+
+  const int32_t* arow = a.anc + (((size_t)t * a.R + r) * a.Wm + b) * a.L;
+  for (int j = 0; j <= t; ++j) {
+    const int slot = j < t ? clampi(arow[j], 0, a.Wm - 1) : b;
+    const size_t rj = (((size_t)j * a.R + r) * a.Wm + slot) * a.H + h;
+    const f32x4 dj = *reinterpret_cast<const f32x4*>(a.rec_delta + rj * DV + c4 * 4);
+    const float aj0 = CH ? 0.f : a.rec_alpha[rj];
+#pragma unroll
+    for (int i = 0; i < G::RPG; ++i) {
+      const int row = rg * G::RPG + i;
+      const float kj = bf16_at(a.rec_k[rj * DK + row]);
+      const float aj = CH ? a.rec_alpha[rj * A + row] : aj0;
+      st[i] = aj * st[i] + kj * dj;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < G::RPG; ++i)
+    *reinterpret_cast<f32x4*>(dst + (size_t)(rg * G::RPG + i) * DV + c4 * 4) = st[i];
+}
+
+template <int DK, int DV, bool CH>
+int launch(const gdn_shape& sh, const gdn_store& st, int t, const int32_t* rb, int beam, int n,
+           const float* src, float* dst, bool dst_per_item, hipStream_t stream) {
+  FoldArgs a;
+  a.src = src;
+  a.dst = dst;
+  a.rec_delta = st.rec_delta;
+  a.rec_k = st.rec_k;
+  a.rec_alpha = st.rec_alpha;
+  a.anc = st.anc;
+  a.rb = rb;
+  a.R = sh.R;
+  a.Wm = sh.W_max;
+  a.H = sh.H;
+  a.L = sh.L_max;
+  a.t = t;
+  a.beam = beam;
+  a.dst_per_item = dst_per_item ? 1 : 0;
+  const long grid = (long)n * sh.H;
+  if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
+  hipLaunchKernelGGL((k_fold<DK, DV, CH>), dim3((unsigned)grid), dim3(FoldGeom<DK, DV>::NT), 0,
+                     stream, a);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+}  // namespace
+
+int launch_fold(const gdn_shape& sh, const gdn_store& st, int t, const int32_t* rb, int beam, int n,
+                const float* src, float* dst, bool dst_per_item, hipStream_t stream) {
+  const bool ch = sh.decay_kind == GDN_DECAY_CHANNEL;
+#define GDN_CASE(DK_, DV_)                                                           \
+  if (sh.dk == DK_ && sh.dv == DV_)                                                  \
+    return ch ? launch<DK_, DV_, true>(sh, st, t, rb, beam, n, src, dst, dst_per_item, stream) \
+              : launch<DK_, DV_, false>(sh, st, t, rb, beam, n, src, dst, dst_per_item, stream);
+  GDN_CASE(16, 16)
+  GDN_CASE(32, 32)
+  GDN_CASE(64, 64)
+  GDN_CASE(128, 128)
+#undef GDN_CASE
+  return GDN_EUNSUPPORTED;
+}
+
+}  // namespace gdn

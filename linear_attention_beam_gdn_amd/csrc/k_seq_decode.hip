@@ -1,0 +1,197 @@
+// Decode step for independent sequences (one beam per request): the
+// bounded-log scheme of DeltaLog (Figure 4: dense base plus a log of compact
+// records, append while the log is not full).  With a single beam there is
+// no cross-beam reuse of the base, so the step is a matrix-vector product
+// bound by reading the base: one workgroup per (sequence, head) streams the
+// [d_k][d_v] FP32 base once with 16-byte loads, forms the two projections
+// base^T x_q and base^T x_k with FP32 FMAs, reduces them across row groups in
+// LDS, replays the log on them, and appends the new record.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+struct SeqArgs {
+  const float* S;
+  float* rec_delta;
+  uint16_t* rec_k;
+  float* rec_alpha;
+  int32_t* anc;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* alpha;
+  const float* beta;
+  float* o;
+  int R, H, L, t;
+};
+
+template <int DK, int DV>
+struct SeqGeom {
+  static_assert(DV % 4 == 0, "d_v must be a multiple of 4");
+  static constexpr int C4 = DV / 4;                      // float4 column groups
+  static constexpr int NRG0 = 256 / C4;
+  static constexpr int NRG = NRG0 < DK ? NRG0 : DK;      // row groups
+  static_assert(DK % NRG == 0, "d_k must split evenly over row groups");
+  static constexpr int RPG = DK / NRG;                   // rows per thread
+  static constexpr int NT = C4 * NRG;                    // threads
+  static constexpr int NWV = (NT + 63) / 64;             // waves
+};
+
+template <int DK, int DV, bool CH>
+__global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a) {
+  using G = SeqGeom<DK, DV>;
+  constexpr int A = CH ? DK : 1;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int h = blockIdx.x % a.H;
+  const int r = blockIdx.x / a.H;
+  const int c4 = tid % G::C4;
+  const int rg = tid / G::C4;
+  const int t = a.t;
+  const size_t tok = (size_t)r * a.H + h;                 // (r, beam 0, h)
+  auto rec_at = [&](int j) -> size_t { return ((size_t)j * a.R + r) * a.H + h; };
+
+  __shared__ float probe_q[DK], probe_k[DK];
+  __shared__ float red_q[G::NRG][DV], red_k[G::NRG][DV];
+  __shared__ float dots_q[GDN_MAX_STEPS], dots_k[GDN_MAX_STEPS], dot_qk;
+
+  // stream this thread's rows of the base first
+  const float* S = a.S + tok * DK * DV;
+  f32x4 st[G::RPG];
+#pragma unroll
+  for (int i = 0; i < G::RPG; ++i)
+    st[i] = *reinterpret_cast<const f32x4*>(S + (size_t)(rg * G::RPG + i) * DV + c4 * 4);
+
+  // probes x_q = c * q, x_k = c * k with c = prod_{i<=t} a_i (channel decay)
+  for (int kk = tid; kk < DK; kk += G::NT) {
+    float cq = 1.f;
+    if constexpr (CH) {
+      cq = a.alpha[tok * DK + kk];
+      for (int j = 0; j < t; ++j) cq *= a.rec_alpha[rec_at(j) * A + kk];
+    }
+    probe_q[kk] = cq * bf16_at(a.q[tok * DK + kk]);
+    probe_k[kk] = cq * bf16_at(a.k[tok * DK + kk]);
+  }
+  // dot products of the replay: wave wv takes log entries j = wv, wv + NWV, ..
+  // (entry t is k_t . q_t); channel decay weights them by prod_{i=j+1..t} a_i
+  for (int j = wv; j <= t; j += G::NWV) {
+    float pq = 0.f, pk = 0.f;
+    for (int kk = lane; kk < DK; kk += 64) {
+      const float qv = bf16_at(a.q[tok * DK + kk]);
+      if (j == t) {
+        pq += bf16_at(a.k[tok * DK + kk]) * qv;
+      } else {
+        float y = bf16_at(a.rec_k[rec_at(j) * DK + kk]);
+        if constexpr (CH) {
+          y *= a.alpha[tok * DK + kk];
+          for (int i = j + 1; i < t; ++i) y *= a.rec_alpha[rec_at(i) * A + kk];
+        }
+        pq += y * qv;
+        pk += y * bf16_at(a.k[tok * DK + kk]);
+      }
+    }
+    pq = wave_sum(pq);
+    pk = wave_sum(pk);
+    if (lane == 0) {
+      if (j == t) dot_qk = pq;
+      else {
+        dots_q[j] = pq;
+        dots_k[j] = pk;
+      }
+    }
+  }
+  __syncthreads();
+
+  // partial projections over this thread's rows
+  f32x4 pq = {0.f, 0.f, 0.f, 0.f}, pk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < G::RPG; ++i) {
+    const int row = rg * G::RPG + i;
+    pq += st[i] * probe_q[row];
+    pk += st[i] * probe_k[row];
+  }
+  *reinterpret_cast<f32x4*>(&red_q[rg][c4 * 4]) = pq;
+  *reinterpret_cast<f32x4*>(&red_k[rg][c4 * 4]) = pk;
+  __syncthreads();
+
+  const float at = CH ? 1.f : a.alpha[tok];
+  const float bt = a.beta[tok];
+  const size_t rec_t = rec_at(t);
+  for (int col = tid; col < DV; col += G::NT) {
+    float uq = 0.f, uk = 0.f;
+#pragma unroll 8
+    for (int g = 0; g < G::NRG; ++g) {
+      uq += red_q[g][col];
+      uk += red_k[g][col];
+    }
+    for (int j = 0; j < t; ++j) {
+      const float dj = a.rec_delta[rec_at(j) * DV + col];
+      if constexpr (!CH) {
+        const float aj = a.rec_alpha[rec_at(j)];
+        uq = aj * uq + dj * dots_q[j];
+        uk = aj * uk + dj * dots_k[j];
+      } else {
+        uq += dj * dots_q[j];
+        uk += dj * dots_k[j];
+      }
+    }
+    const float vv = bf16_at(a.v[tok * DV + col]);
+    const float d = bt * (vv - at * uk);
+    a.o[tok * DV + col] = at * uq + d * dot_qk;
+    a.rec_delta[rec_t * DV + col] = d;
+  }
+  for (int kk = tid; kk < DK; kk += G::NT) {
+    a.rec_k[rec_t * DK + kk] = a.k[tok * DK + kk];
+    if constexpr (CH) a.rec_alpha[rec_t * A + kk] = a.alpha[tok * DK + kk];
+  }
+  if constexpr (!CH)
+    if (tid == 0) a.rec_alpha[rec_t] = at;
+  if (h == 0 && tid < t) a.anc[(((size_t)t * a.R + r) * 1 + 0) * a.L + tid] = 0;
+}
+
+template <int DK, int DV, bool CH>
+int launch(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io, hipStream_t stream) {
+  SeqArgs a;
+  a.S = st.S;
+  a.rec_delta = st.rec_delta;
+  a.rec_k = st.rec_k;
+  a.rec_alpha = st.rec_alpha;
+  a.anc = st.anc;
+  a.q = io.q;
+  a.k = io.k;
+  a.v = io.v;
+  a.alpha = io.alpha;
+  a.beta = io.beta;
+  a.o = io.o;
+  a.R = sh.R;
+  a.H = sh.H;
+  a.L = sh.L_max;
+  a.t = t;
+  const long grid = (long)sh.R * sh.H;
+  if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
+  hipLaunchKernelGGL((k_seq_decode<DK, DV, CH>), dim3((unsigned)grid), dim3(SeqGeom<DK, DV>::NT), 0,
+                     stream, a);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+}  // namespace
+
+int launch_seq_decode(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io,
+                      hipStream_t stream) {
+  const bool ch = sh.decay_kind == GDN_DECAY_CHANNEL;
+#define GDN_CASE(DK_, DV_)                                                       \
+  if (sh.dk == DK_ && sh.dv == DV_)                                              \
+    return ch ? launch<DK_, DV_, true>(sh, st, t, io, stream)                    \
+              : launch<DK_, DV_, false>(sh, st, t, io, stream);
+  GDN_CASE(16, 16)
+  GDN_CASE(32, 32)
+  GDN_CASE(64, 64)
+  GDN_CASE(128, 128)
+#undef GDN_CASE
+  return GDN_EUNSUPPORTED;
+}
+
+}  // namespace gdn

@@ -1,0 +1,111 @@
+"""The C ABI on the host: the library loads, exports what the header
+declares, and rejects bad arguments before touching the GPU (CPU only)."""
+
+import ctypes
+import subprocess
+
+import pytest
+
+from linear_attention_beam_gdn_amd import binding as B
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def shape(**kw):
+    d = dict(R=2, W_max=8, H=2, dk=128, dv=128, L_max=4, decay_kind=0)
+    d.update(kw)
+    return B.GdnShape(**d)
+
+
+def store(**kw):
+    d = dict(S=FAKE, rec_delta=FAKE, rec_k=FAKE, rec_alpha=FAKE, anc=FAKE)
+    d.update(kw)
+    return B.GdnStore(**d)
+
+
+def decode(L, sh=None, st=None, t=1, W_t=4, parent=FAKE, q=FAKE, k=FAKE, v=FAKE, alpha=FAKE,
+           beta=FAKE, o=FAKE):
+    sh = shape() if sh is None else sh
+    st = store() if st is None else st
+    return L.gdn_beam_decode_step(ctypes.byref(sh), ctypes.byref(st), t, W_t, parent, q, k, v,
+                                  alpha, beta, o, None)
+
+
+def test_exports_every_header_function(L):
+    names = B.header_functions()
+    assert set(names) == {"gdn_beam_decode_step", "gdn_materialize", "gdn_log_merge",
+                          "gdn_status_string", "gdn_abi_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_version_and_status_strings(L):
+    assert L.gdn_abi_version() == 1
+    for s in (B.GDN_OK, B.GDN_EINVAL, B.GDN_EUNSUPPORTED, B.GDN_EHIP, 12345):
+        assert isinstance(B.status_string(s), str) and B.status_string(s)
+
+
+def test_decode_validation(L):
+    E, U = B.GDN_EINVAL, B.GDN_EUNSUPPORTED
+    P = ctypes.POINTER
+    assert L.gdn_beam_decode_step(P(B.GdnShape)(), ctypes.byref(store()), 0, 1, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, FAKE, None) == E
+    assert L.gdn_beam_decode_step(ctypes.byref(shape()), P(B.GdnStore)(), 0, 1, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, FAKE, None) == E
+    assert decode(L, sh=shape(R=0)) == E
+    assert decode(L, sh=shape(H=0)) == E
+    assert decode(L, sh=shape(L_max=0)) == E
+    assert decode(L, sh=shape(L_max=B.GDN_MAX_STEPS + 1)) == E
+    assert decode(L, sh=shape(dk=96, dv=96)) == U
+    assert decode(L, sh=shape(dk=128, dv=64)) == U
+    assert decode(L, sh=shape(decay_kind=2)) == U
+    assert decode(L, t=-1) == E
+    assert decode(L, t=4) == E
+    assert decode(L, W_t=0) == E
+    assert decode(L, W_t=9) == E
+    assert decode(L, t=1, parent=None) == E
+    assert decode(L, t=1, parent=FAKE + 2) == E
+    for name in ("q", "k", "v", "alpha", "beta", "o"):
+        assert decode(L, **{name: None}) == E, name
+        assert decode(L, **{name: FAKE + 8}) == E, name
+    for name in ("S", "rec_delta", "rec_k", "rec_alpha", "anc"):
+        assert decode(L, st=store(**{name: None})) == E, name
+        assert decode(L, st=store(**{name: FAKE + 4})) == E, name
+
+
+def test_materialize_and_merge_validation(L):
+    E = B.GDN_EINVAL
+    sh, st = shape(), store()
+    m = lambda t=1, rb=FAKE, n=3, out=FAKE: L.gdn_materialize(ctypes.byref(sh), ctypes.byref(st), t,
+                                                              rb, n, out, None)
+    assert m(n=0) == B.GDN_OK  # nothing to do, nothing enqueued
+    assert m(n=-1) == E
+    assert m(t=4) == E
+    assert m(t=-1) == E
+    assert m(rb=None) == E
+    assert m(out=FAKE + 4) == E
+    g = lambda n_rec=2, beam=0: L.gdn_log_merge(ctypes.byref(sh), ctypes.byref(st), n_rec, beam, None)
+    assert g(n_rec=0) == E
+    assert g(n_rec=5) == E
+    assert g(beam=-1) == E
+    assert g(beam=8) == E
+    bad = shape(dk=48, dv=48)
+    assert L.gdn_log_merge(ctypes.byref(bad), ctypes.byref(st), 1, 0, None) == B.GDN_EUNSUPPORTED
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    st = B.Store.__new__(B.Store)
+    st.R, st.H, st.dk, st.dv, st.channel_decay = 1, 1, 16, 16, False
+    x = torch.zeros(1, 1, 1, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        B.decode_step(st, 0, 1, None, x, x, x, torch.zeros(1, 1, 1), torch.zeros(1, 1, 1))

@@ -1,0 +1,306 @@
+"""Parity of the HIP path, called through the C ABI, with the FP64 oracle.
+
+Bars: ancestry, record keys and decays bit-exact; o_t, delta_t, materialised
+and merged states within 1e-4 max relative error per slice (infinity norm of
+the difference over the infinity norm of the oracle's slice).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.gdn_oracle as O
+from gpu_util import TOL, log, rel_slices, rel_states, run_beam, step_records
+from linear_attention_beam_gdn_amd import binding as B
+from linear_attention_beam_gdn_amd import configs, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def check_beam(inp, channel, requests=None, heads=None, label="", **run_kw):
+    log(f"[parity] {label} R,H,dk,dv={inp['S0'].shape} W={[s['q'].shape[1] for s in inp['steps']]}")
+    store, outs = run_beam(inp, channel, **run_kw)
+    ref = O.beam_decode(inp["S0"], inp["steps"], requests=requests, heads=heads)
+    worst = 0.0
+    for t, st in enumerate(inp["steps"]):
+        W_t = st["q"].shape[1]
+        d, kbits, a, anc = step_records(store, t, W_t)
+        assert np.array_equal(anc, ref["anc"][t]), f"{label}: ancestry differs at t={t}"
+        assert np.array_equal(kbits, st["k"]), f"{label}: record keys differ at t={t}"
+        assert np.array_equal(a.reshape(st["alpha"].shape), st["alpha"]), f"{label}: decays t={t}"
+        eo = rel_slices(outs[t], ref["o"][t])
+        ed = rel_slices(d, ref["delta"][t])
+        worst = max(worst, eo, ed)
+        assert eo <= TOL and ed <= TOL, (label, t, eo, ed)
+    log(f"[parity] {label}: max rel err {worst:.2e}")
+    return store, outs, ref
+
+
+# ----------------------------------------------------------- the five workloads
+
+def test_tiny_workload():
+    check_beam(configs.TINY.inputs(), False, label="tiny")
+
+
+def test_single_request_workload():
+    check_beam(configs.SINGLE.inputs(), False, label="single-request")
+
+
+def test_large_beam_workload_sampled():
+    # full size (8 x 512 beams, H = 32); the oracle recomputes 2 requests x 3 heads
+    check_beam(configs.LARGE.inputs(), False, requests=[0, 5], heads=[0, 13, 31],
+               label="large-beam")
+
+
+def test_kda_workload_sampled():
+    check_beam(configs.KDA.inputs(), True, requests=[0, 15], heads=[0, 31], label="kda")
+
+
+def test_deltalog_workload():
+    w = configs.DELTALOG
+    seq = w.inputs()
+    pairs = [(0, 0), (0, 31), (17, 5), (64, 16), (101, 30), (127, 0), (127, 31), (90, 9)]
+    rs = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    log(f"[parity] deltalog R={w.R} H={w.H} T={w.T} M={w.M}")
+    ref = O.sequence_decode(seq["S0"], seq["tokens"], w.M, pairs=pairs)
+    store = B.Store(w.R, 1, w.H, w.dk, w.dv, w.M, S=torch.from_numpy(seq["S0"]).cuda())
+    zero = torch.zeros(w.R, 1, dtype=torch.int32, device="cuda")
+    rs_d = torch.from_numpy(rs).cuda()
+    hs_d = torch.from_numpy(hs).cuda()
+    worst = 0.0
+    for i in range(w.T):
+        t = i % w.M
+        d = B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")})
+        o = B.decode_step(store, t, 1, zero, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        o_s = o[rs_d, 0, hs_d].cpu().numpy()
+        d_s = store.rec_delta[t, rs_d, 0, hs_d].cpu().numpy()
+        worst = max(worst, rel_slices(o_s, ref["o"][i]), rel_slices(d_s, ref["delta"][i]))
+        if t == w.M - 1:
+            B.log_merge(store, w.M, 0)
+            S_s = store.S[rs_d, hs_d].cpu().numpy()
+            worst = max(worst, rel_states(S_s[:, None], ref["bases"][i // w.M][:, None]))
+        assert worst <= TOL, (i, worst)
+    log(f"[parity] deltalog: max rel err {worst:.2e}")
+
+
+# ------------------------------------------------- shapes: tiles, ragged tails
+
+@pytest.mark.parametrize("channel", [False, True])
+@pytest.mark.parametrize("dims", [(16, 16), (32, 32), (64, 64), (128, 128)])
+def test_ragged_widths(dims, channel):
+    dk, dv = dims
+    inp = synth.make_inputs(R=3, H=3, dk=dk, dv=dv, W=37, L=4, s0_std=0.1, seed=100 + dk,
+                            parents="topk", channel_decay=channel, widths=[37, 29, 37, 20])
+    check_beam(inp, channel, label=f"ragged dk={dk} ch={channel}")
+
+
+@pytest.mark.parametrize("channel", [False, True])
+def test_sequences_small(channel):
+    R, H, dk, dv, T, M = 5, 3, 64, 64, 12, 4
+    seq = synth.make_sequence_inputs(R=R, H=H, dk=dk, dv=dv, T=T, s0_std=0.1, seed=7,
+                                     channel_decay=channel)
+    ref = O.sequence_decode(seq["S0"], seq["tokens"], M)
+    store = B.Store(R, 1, H, dk, dv, M, channel_decay=channel,
+                    S=torch.from_numpy(seq["S0"]).cuda())
+    zero = torch.zeros(R, 1, dtype=torch.int32, device="cuda")
+    for i in range(T):
+        t = i % M
+        d = B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")})
+        o = B.decode_step(store, t, 1, zero, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        assert rel_slices(o[:, 0].cpu().numpy().reshape(R * H, dv), ref["o"][i]) <= TOL
+        if t == M - 1:
+            B.log_merge(store, M, 0)
+            S = store.S.cpu().numpy().reshape(R * H, 1, dk, dv)
+            assert rel_states(S, ref["bases"][i // M][:, None]) <= TOL
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_single_beam_in_wide_store():
+    inp = synth.make_inputs(R=2, H=2, dk=128, dv=128, W=1, L=3, s0_std=0.05, seed=8,
+                            parents="uniform")
+    check_beam(inp, False, W_max=16, label="W_t=1")
+
+
+def test_longest_chain():
+    inp = synth.make_inputs(R=2, H=2, dk=32, dv=32, W=6, L=B.GDN_MAX_STEPS, s0_std=0.1, seed=9,
+                            parents="uniform")
+    check_beam(inp, False, label="L=16")
+    inp = synth.make_inputs(R=1, H=2, dk=32, dv=32, W=6, L=B.GDN_MAX_STEPS, s0_std=0.1, seed=9,
+                            parents="uniform", channel_decay=True)
+    check_beam(inp, True, label="L=16 channel")
+
+
+@pytest.mark.parametrize("kind", ["identity", "fanout"])
+def test_degenerate_lineages(kind):
+    inp = synth.make_inputs(R=2, H=2, dk=128, dv=128, W=24, L=4, s0_std=0.05, seed=10,
+                            parents="uniform")
+    for st in inp["steps"][1:]:
+        st["parent"][:] = np.arange(24) if kind == "identity" else 7
+    _, outs, ref = check_beam(inp, False, label=kind)
+    if kind == "identity":
+        assert np.all(ref["anc"][3] == np.arange(24)[None, :, None])
+
+
+@pytest.mark.parametrize("channel", [False, True])
+def test_gates_at_extremes(channel):
+    # beta = 0: o = (prod decay) S0^T q; alpha = 1: S0 enters at full weight
+    inp = synth.make_inputs(R=2, H=2, dk=128, dv=128, W=20, L=4, s0_std=0.05, seed=11,
+                            parents="topk", channel_decay=channel, beta_const=0.0)
+    store, _, _ = check_beam(inp, channel, label="beta=0")
+    assert torch.count_nonzero(store.rec_delta) == 0
+    inp = synth.make_inputs(R=2, H=2, dk=128, dv=128, W=20, L=4, s0_std=0.05, seed=12,
+                            parents="topk", channel_decay=channel, alpha_const=1.0)
+    check_beam(inp, channel, label="alpha=1")
+
+
+def test_orthonormal_keys_retrieve_exactly():
+    inp = synth.make_inputs(R=2, H=2, dk=32, dv=32, W=9, L=4, s0_std=0.05, seed=13,
+                            parents="uniform", alpha_const=1.0, beta_const=1.0)
+    sigma = [3, 30, 11, 17]
+    one = synth.bf16_bits(np.float32(1.0))
+    for t, st in enumerate(inp["steps"]):
+        st["k"][:] = 0
+        st["k"][..., sigma[t]] = one
+        st["q"][:] = 0
+        st["q"][..., sigma[t // 2]] = one
+    inp["S0"][:] = 0
+    store, outs = run_beam(inp)
+    anc = O.ancestry([s.get("parent") for s in inp["steps"]], 2, 9)
+    for t in range(4):
+        j = t // 2
+        for r in range(2):
+            slot = anc[t][r, :, j] if j < t else np.arange(9)
+            v = synth.bf16_bits_to_f32(inp["steps"][j]["v"][r, slot])
+            assert np.array_equal(outs[t][r], v), (t, r)
+
+
+# --------------------------------------------------------- materialise / merge
+
+@pytest.mark.parametrize("channel", [False, True])
+def test_materialize(channel):
+    inp = synth.make_inputs(R=2, H=3, dk=128, dv=128, W=40, L=3, s0_std=0.05, seed=14,
+                            parents="topk", channel_decay=channel)
+    store, _ = run_beam(inp, channel)
+    pairs = [(0, 0), (1, 39), (0, 17), (1, 5)]
+    rb = torch.tensor(pairs, dtype=torch.int32, device="cuda")
+    for t in range(3):
+        S = B.materialize(store, t, rb).cpu().numpy()
+        ref = O.beam_states(inp["S0"], inp["steps"], t, pairs)
+        err = rel_states(S, ref)
+        log(f"[parity] materialize t={t} ch={channel}: {err:.2e}")
+        assert err <= TOL
+
+
+def test_merge_of_beam_chain():
+    inp = synth.make_inputs(R=3, H=2, dk=64, dv=64, W=12, L=3, s0_std=0.1, seed=15,
+                            parents="topk")
+    store, _ = run_beam(inp)
+    B.log_merge(store, 3, beam=5)
+    ref = O.beam_states(inp["S0"], inp["steps"], 2, [(r, 5) for r in range(3)])
+    assert rel_states(store.S.cpu().numpy(), ref) <= TOL
+
+
+@pytest.mark.parametrize("channel", [False, True])
+def test_merge_then_decode_equals_decode_with_log(channel):
+    R, H, dk, dv, M = 4, 4, 128, 128, 4
+    seq = synth.make_sequence_inputs(R=R, H=H, dk=dk, dv=dv, T=M, s0_std=0.05, seed=16,
+                                     channel_decay=channel)
+    toks = [B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")})
+            for i in range(M)]
+    zero = torch.zeros(R, 1, dtype=torch.int32, device="cuda")
+    S0 = torch.from_numpy(seq["S0"]).cuda()
+    a = B.Store(R, 1, H, dk, dv, M, channel_decay=channel, S=S0.clone())
+    for i, d in enumerate(toks):
+        o_log = B.decode_step(a, i, 1, zero, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+    b = B.Store(R, 1, H, dk, dv, M, channel_decay=channel, S=S0.clone())
+    for i, d in enumerate(toks[:-1]):
+        B.decode_step(b, i, 1, zero, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+    B.log_merge(b, M - 1, 0)
+    d = toks[-1]
+    o_merged = B.decode_step(b, 0, 1, zero, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+    assert rel_slices(o_merged.cpu().numpy(), o_log.cpu().numpy()) <= TOL
+
+
+def test_identity_merge_is_bit_exact():
+    R, H, dk, dv, M = 3, 2, 128, 128, 5
+    seq = synth.make_sequence_inputs(R=R, H=H, dk=dk, dv=dv, T=M, s0_std=0.05, seed=17)
+    seq["tokens"]["alpha"][:] = 1.0
+    seq["tokens"]["beta"][:] = 0.0
+    S0 = torch.from_numpy(seq["S0"]).cuda()
+    st = B.Store(R, 1, H, dk, dv, M, S=S0.clone())
+    zero = torch.zeros(R, 1, dtype=torch.int32, device="cuda")
+    for i in range(M):
+        d = B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")})
+        B.decode_step(st, i, 1, zero, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+    B.log_merge(st, M, 0)
+    assert torch.equal(st.S, S0)
+
+
+# ------------------------------------------ determinism, reordering, isolation
+
+def test_deterministic_and_reorder_invariant():
+    inp = synth.make_inputs(R=2, H=4, dk=128, dv=128, W=48, L=4, s0_std=0.05, seed=18,
+                            parents="topk")
+    _, o1 = run_beam(inp)
+    _, o2 = run_beam(inp)
+    for a, b in zip(o1, o2):
+        assert np.array_equal(a, b)
+    rng = np.random.default_rng(0)
+    perms = [rng.permutation(48) for _ in inp["steps"]]
+    inv = [np.argsort(p) for p in perms]
+    pinp = {"S0": inp["S0"], "steps": []}
+    for t, st in enumerate(inp["steps"]):
+        ps = {n: np.ascontiguousarray(st[n][:, perms[t]]) for n in ("q", "k", "v", "alpha", "beta")}
+        if t:
+            ps["parent"] = inv[t - 1][st["parent"][:, perms[t]]].astype(np.int32)
+        pinp["steps"].append(ps)
+    _, op = run_beam(pinp)
+    for t in range(4):
+        assert np.array_equal(op[t], o1[t][:, perms[t]]), t
+
+
+def test_duplicate_children_agree():
+    inp = synth.make_inputs(R=1, H=2, dk=128, dv=128, W=32, L=3, s0_std=0.05, seed=19,
+                            parents="uniform")
+    for t in (1, 2):
+        st = inp["steps"][t]
+        st["parent"][0, 1] = st["parent"][0, 0]
+        for n in ("q", "k", "v", "alpha", "beta"):
+            st[n][0, 1] = st[n][0, 0]
+        if t == 2:
+            st["parent"][0, 0], st["parent"][0, 1] = 0, 1
+    _, outs = run_beam(inp)
+    assert np.array_equal(outs[1][0, 0], outs[1][0, 1])
+    assert np.array_equal(outs[2][0, 0], outs[2][0, 1])
+
+
+def test_append_only_and_guards():
+    inp = synth.make_inputs(R=2, H=2, dk=128, dv=128, W=30, L=4, s0_std=0.05, seed=20,
+                            parents="topk")
+    W_max, W = 40, 30
+    store = B.Store(2, W_max, 2, 128, 128, 4, S=torch.from_numpy(inp["S0"]).cuda())
+    store.rec_delta.fill_(float("nan"))
+    store.rec_alpha.fill_(float("nan"))
+    n_o = 2 * W * 2 * 128
+    guard = 64
+    o_big = torch.full((n_o + 2 * guard,), -7.0, device="cuda")
+    o = o_big[guard:guard + n_o].view(2, W, 2, 128)
+    snaps = []
+    for t, st in enumerate(inp["steps"]):
+        d = B.upload(st)
+        B.decode_step(store, t, W, d.get("parent"), d["q"], d["k"], d["v"], d["alpha"],
+                      d["beta"], o=o)
+        torch.cuda.synchronize()
+        for j, (sd, sk, sa) in enumerate(snaps):  # earlier records are never rewritten
+            assert torch.equal(store.rec_delta[j, :, :W], sd)
+            assert torch.equal(store.rec_k[j, :, :W], sk)
+            assert torch.equal(store.rec_alpha[j, :, :W], sa)
+        snaps.append((store.rec_delta[t, :, :W].clone(), store.rec_k[t, :, :W].clone(),
+                      store.rec_alpha[t, :, :W].clone()))
+        assert torch.all(o_big[:guard] == -7.0) and torch.all(o_big[guard + n_o:] == -7.0)
+        assert torch.isnan(store.rec_delta[t, :, W:]).all()  # slots >= W_t untouched
+        assert torch.isnan(store.rec_alpha[t, :, W:]).all()
+        assert not torch.isnan(store.rec_delta[t, :, :W]).any()
+        assert not torch.isnan(o).any()
