@@ -17,82 +17,10 @@
 // k_j . q and k_j . k of the replay are reduced over the four lane groups of
 // the beam; the value-side updates are per lane, so the replay never leaves
 // registers.
-#include "gdn_device.h"
-#include "gdn_launch.h"
-
-#include <stdlib.h>
+#include "beam_common.h"
 
 namespace gdn {
 namespace {
-
-struct BeamArgs {
-  const float* S;
-  float* rec_delta;
-  uint16_t* rec_k;
-  float* rec_alpha;
-  int32_t* anc;
-  const int32_t* parent;
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  const float* alpha;
-  const float* beta;
-  float* o;
-  int R, Wm, H, L, t, Wt;
-  int chunk, nchunk;
-};
-
-template <int DK, int DV>
-struct BeamGeom {
-  static_assert(DK == 16 || DK == 32 || DK % 64 == 0, "d_k must be 16, 32 or a multiple of 64");
-  static_assert(DV % 16 == 0, "d_v must be a multiple of 16");
-  static constexpr int RPW = (DV % 32 == 0) ? 32 : 16;  // value rows per wave
-  static constexpr int NW = DV / RPW;                   // waves per workgroup
-  static constexpr int MT = RPW / 16;                   // 16-row MFMA tiles per wave
-  static constexpr int KS = (DK + 31) / 32;             // 32-deep MFMA steps over d_k
-  static constexpr int VPL = 4 * MT;                    // value rows per lane
-};
-
-// First key channel of the 8 consecutive channels that lane group g feeds to
-// MFMA step s.  Any assignment works as long as the A and B operands use the
-// same one; this one gives each lane 16 (d_k >= 64) contiguous channels.
-template <int DK>
-__device__ __forceinline__ int kchunk(int g, int s) {
-  if constexpr (DK % 64 == 0) return (s >> 1) * 64 + g * 16 + (s & 1) * 8;
-  else return g * 8;
-}
-template <int DK>
-__device__ __forceinline__ bool klive(int g) {
-  if constexpr (DK == 16) return g < 2;  // lane groups 2, 3 feed zero padding
-  else return true;
-}
-
-__device__ __forceinline__ void load_f32x8(const float* p, float* x) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = a[i];
-    x[4 + i] = b[i];
-  }
-}
-
-// Split eight FP32 values into bf16 planes: x ~= sum_p plane[p] (RNE each).
-template <int NP>
-__device__ __forceinline__ void split_planes(const float* x, u32x4* planes) {
-#pragma unroll
-  for (int p = 0; p < NP; ++p) planes[p] = u32x4{0, 0, 0, 0};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float rem = x[e];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const uint32_t hb = bf16_rne(rem);
-      rem -= bf16_at(uint16_t(hb));
-      planes[p][e >> 1] |= hb << (16 * (e & 1));
-    }
-  }
-}
 
 template <int DK, int DV, bool CH, int NPL>
 __global__ __launch_bounds__((BeamGeom<DK, DV>::NW * 64)) void k_beam_decode(BeamArgs a) {
@@ -377,20 +305,6 @@ __global__ __launch_bounds__((BeamGeom<DK, DV>::NW * 64)) void k_beam_decode(Bea
   }
 }
 
-// Beams per workgroup: a multiple of 16, sized so that the grid holds about
-// 2048 workgroups (8 per CU) when the beam count allows it.
-int pick_chunk(int RH, int Wt) {
-  if (const char* e = getenv("GDN_BEAM_CHUNK")) {
-    const int v = atoi(e);
-    if (v >= 16 && v % 16 == 0) return v;
-  }
-  const long want = ((long)RH * Wt + 2047) / 2048;
-  int chunk = (int)((want + 15) / 16) * 16;
-  if (chunk < 16) chunk = 16;
-  const int full = (Wt + 15) / 16 * 16;
-  return chunk > full ? full : chunk;
-}
-
 template <int DK, int DV, bool CH>
 int launch(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
            hipStream_t stream) {
@@ -414,7 +328,7 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO
   a.L = sh.L_max;
   a.t = t;
   a.Wt = Wt;
-  a.chunk = pick_chunk(sh.R * sh.H, Wt);
+  a.chunk = pick_chunk(sh.R * sh.H, Wt, 1 << 30, 2048);
   a.nchunk = (Wt + a.chunk - 1) / a.chunk;
   const long grid = (long)sh.R * sh.H * a.nchunk;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
@@ -427,6 +341,10 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO
 
 int launch_beam_decode(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
                        hipStream_t stream) {
+  // GDN_BEAM_GENERIC=1 forces the register-only kernel (for A/B comparisons)
+  const char* generic = getenv("GDN_BEAM_GENERIC");
+  if (beam_staged_supported(sh) && !(generic != nullptr && generic[0] == '1'))
+    return launch_beam_staged(sh, st, t, Wt, io, stream);
   const bool ch = sh.decay_kind == GDN_DECAY_CHANNEL;
 #define GDN_CASE(DK_, DV_)                                                       \
   if (sh.dk == DK_ && sh.dv == DV_)                                              \
