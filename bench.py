@@ -80,6 +80,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=32)
     ap.add_argument("--cpu-workers", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the warm-up, run a plain device copy of this many MiB three times "
+                         "(a known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path shards by request and head with no "
@@ -113,6 +116,15 @@ def main():
                           d["beta"], o=outs[t], stream=stream)
             if ev is not None:
                 ev[t][1].record(stream)
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 18  # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         one_pass()
@@ -160,7 +172,7 @@ def main():
                    "L": w.L, "hot_parent_fraction": w.hot_frac, "parallelism": "single GPU"},
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_beam_decode<128,128,scalar>",
+            "kernel": "k_beam_fused<128,128,t> (t = 0..L-1, one launch per decode step)",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -28,11 +28,19 @@ __device__ __forceinline__ float bf16x8_elem(const u32x4& v, int e) {
   return (e & 1) ? bf16_hi(w) : bf16_lo(w);
 }
 
-// Sum over the four 16-lane groups of a wave64 (lanes l, l^16, l^32, l^48).
+// Sum over the four 16-lane groups of a wave64 (lanes l, l^16, l^32, l^48)
+// with the gfx950 row-swap instructions: plain VALU work, no trip through
+// the LDS crossbar.  permlane16_swap exchanges 16-lane rows 1 <-> 0 and
+// 3 <-> 2 between its two operands, permlane32_swap the two 32-lane halves;
+// with both operands equal, the two results of each swap hold a lane's own
+// row and its partner row, so every lane of a group forms the same sum
+// ((x0 + x1) + (x2 + x3)) in the same order.
 __device__ __forceinline__ float sum_lane_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t v = __float_as_uint(__uint_as_float(a[0]) + __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Sum over all 64 lanes of a wave.

@@ -25,10 +25,12 @@ bool dims_supported(int dk, int dv);
 int launch_beam_decode(const gdn_shape& sh, const gdn_store& st, int t, int Wt,
                        const StepIO& io, hipStream_t stream);
 
-// Scalar-decay beams with d_k, d_v multiples of 32: inputs staged through LDS.
-bool beam_staged_supported(const gdn_shape& sh);
-int launch_beam_staged(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
-                       hipStream_t stream);
+// Scalar-decay beams with (d_k, d_v) in {32, 64, 128} and chains of at most
+// kFusedMaxSteps records: loader/consumer pipeline through LDS.
+constexpr int kFusedMaxSteps = 4;
+bool beam_fused_supported(const gdn_shape& sh, int t);
+int launch_beam_fused(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
+                      hipStream_t stream);
 
 // One beam per request (W_max == 1): bounded-log decoding of sequences.
 int launch_seq_decode(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io,
