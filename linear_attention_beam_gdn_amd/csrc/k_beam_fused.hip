@@ -1,34 +1,53 @@
 // Fused shared-context decode step for scalar-decay GDN beams (OneLA §3.4,
 // Figure 5; replay equations of §3.2; ancestry index of §3.3), built as a
-// producer/consumer pipeline for gfx950.
+// three-role pipeline for gfx950.
 //
 // Work split.  A workgroup takes one (request r, head h) and a chunk of its
-// beams, 16 beams (one MFMA N block) per tile.  It has NW consumer waves,
-// each owning 32 value rows (the B_V tile of §3.4), and one loader wave.
+// beams, 16 beams (one MFMA N block) per tile, and runs three kinds of wave:
 //
-// Loader wave.  Streams every per-tile operand from HBM straight into a ring
-// of NBUF LDS buffers with LDS-DMA loads (global_load_lds, no register round
-// trip): the tile's q, k and v rows, its alpha and beta, and for each beam
-// the T ancestral records (alpha_j, delta_j, k_j) found through the ancestry
-// index.  It keeps up to NBUF - 1 tiles in flight and, before each barrier,
-// waits only for the tile the consumers take next.
+// * Two DMA waves, taking alternate tiles.  They build the chunk's ancestry
+//   slot table in LDS, then stream every tile's q, k, v, alpha, beta and, for
+//   each beam, the keys and decays of its T ancestral records straight from
+//   HBM into a ring of NBUF LDS buffers with LDS-DMA loads (global_load_lds,
+//   no register round trip).  They keep tiles in flight (a wave holds at most
+//   63 memory operations, so two waves double the depth) and, before each
+//   barrier, the owner of the tile the dot wave takes next waits for it alone
+//   (counted vmcnt waits).
+// * Dot wave.  One tile ahead of the consumers, forms for every beam the
+//   replay's dot products k_j . q_t, k_j . k_t and k_t . q_t (bf16 dot2
+//   products reduced over four lane groups) and folds the scalar decays of
+//   the chain into per-beam weights:
+//       alpha_t u^(T-1) = c_0 u^(-1) + sum_j c_{j+1} (k_j . x) delta_j,
+//       c_j = alpha_t prod_{i >= j} alpha_i,  c_T = alpha_t,
+//   so the consumers' replay is one FMA per record and value row.  It
+//   publishes c_0, beta_t, k_t . q_t and the 2T record weights in the tile's
+//   LDS buffer.
+// * Consumer waves (d_v / 16 of them, two per SIMD for d_v = 128).  Each holds
+//   its 16-row slice of the shared state S0[r, h] in registers for the whole
+//   chunk as three bf16 planes (hi + mid + lo, each the RNE of the FP32
+//   residual) in the MFMA A layout, so S0 is read once per workgroup and
+//   reused by every beam.  Per tile: S0^T [q | k] on the matrix cores (q and
+//   k are bf16, so every plane product is exact; FP32 accumulation), the
+//   replay on its value rows with the ancestral update vectors delta_j
+//   (loaded into registers one tile ahead, each wave its own rows), then
+//   delta_t and o_t, stored with 64-byte contiguous writes per beam, plus the
+//   appended record.  Two waves per SIMD hide each other's latencies.
 //
-// Consumer waves.  Hold their slice of the shared state S0[r, h] in registers
-// for the whole chunk as three bf16 planes (hi + mid + lo, each the RNE of
-// the FP32 residual) in the MFMA A layout, so S0 is read once per workgroup
-// and reused by every beam.  Per tile: S0^T [q | k] on the matrix cores (q
-// and k are bf16, so every plane product is exact; FP32 accumulation), the
-// replay of the T records (bf16 dot2 products reduced over the four lane
-// groups of a beam), then delta_t and o_t, stored with 64-byte contiguous
-// writes per beam, plus the appended record.  They issue no vector loads in
-// the tile loop, so they never stall on memory, and they never wait for
-// their own stores.
+// Schedule.  With one chunk per (r, h), the beams are taken in the depth-
+// first order of the beam tree (lexicographic in their ancestry rows), so that
+// beams sharing ancestors share tiles and every ancestral record is gathered
+// from memory about once.  That order is a stable sort of the beams by their
+// parent's position in the previous step's order, which each step keeps in
+// the otherwise unused last entry of its ancestry rows; one wave sorts with a
+// counting sort in LDS.  The order only decides which tile and lane computes
+// a beam: every beam's arithmetic, and so its result, is the same in any
+// order.
 //
 // LDS tile layout ("beam fastest"): a 16-row array with NCH 16-byte chunks
 // per row keeps chunk ch of row b at 16-byte slot (ch/4)*64 + (ch%4)*16 + b.
 // DMA instruction m then fills slots m*64 .. m*64+63 with lane l loading
-// chunk 4m + l/16 of row l%16 (so every loader lane serves one beam), and a
-// consumer read of chunk 4s + g for beam c by lane 16g + c is one contiguous
+// chunk 4m + l/16 of row l%16 (so every DMA lane serves one beam), and a
+// fragment read of chunk 4s + g for beam c by lane 16g + c is one contiguous
 // 1 KiB access, free of bank conflicts.
 #include "beam_common.h"
 
@@ -37,31 +56,39 @@ namespace {
 
 constexpr int kMaxChunkF = 512;         // beams per workgroup at most
 constexpr int kLdsBytes = 160 * 1024;   // LDS of one gfx950 compute unit
+constexpr int kSortMax = 8192;          // largest W_max whose tree order is computed
 
 template <int DK, int DV, int T>
 struct FusedGeom {
   static_assert(DK % 32 == 0 && DV % 32 == 0, "the fused kernel needs d_k, d_v multiples of 32");
-  static constexpr int NW = DV / 32;       // consumer waves
-  static constexpr int NT = (NW + 1) * 64; // plus the loader wave
+  static constexpr int NC = DV / 16;       // consumer waves, 16 value rows each
+  static constexpr int WDMA = NC;          // wave index of the first DMA wave
+  static constexpr int NDMA = 2;           // DMA waves (tile p belongs to DMA wave p % 2)
+  static constexpr int WDOT = NC + NDMA;   // wave index of the dot wave
+  static constexpr int NT = (NC + NDMA + 1) * 64;
   static constexpr int KS = DK / 32;       // 32-deep MFMA steps over d_k
   static constexpr int QB = 16 * DK * 2;   // bytes of a q (or k) tile
   static constexpr int VB = 16 * DV * 2;   // bytes of a v tile
-  static constexpr int NSM = (2 + T) * 16 > 64 ? 2 : 1;  // dword DMAs for alpha, beta, alpha_j
+  static constexpr int NSM = (2 + T) * 16 > 64 ? 2 : 1;  // dword DMAs: alpha_t, beta_t, alpha_j
   static constexpr int SMB = NSM * 256;
   static constexpr int RKB = 16 * DK * 2;  // keys of one record depth
-  static constexpr int RDB = 16 * DV * 4;  // update vectors of one record depth
-  static constexpr int RECB = RKB + RDB;
-  static constexpr int OQ = 0, OKK = QB, OV = 2 * QB, OS = 2 * QB + VB, OR = OS + SMB;
-  static constexpr int BUF = OR + T * RECB;
-  static constexpr int SLOTB = T * kMaxChunkF * 4;
+  static constexpr int NWT = (3 + 2 * T + 3) / 4 * 4;  // weights per beam, padded to 16 B
+  static constexpr int WTB = 16 * NWT * 4;
+  static constexpr int OQ = 0, OKK = QB, OV = 2 * QB, OS = 2 * QB + VB, OW = OS + SMB, ORK = OW + WTB;
+  static constexpr int BUF = ORK + T * RKB;
+  // schedule table: per position {beam, slot_0, slot_1, slot_2}, plus slot_3
+  static constexpr int SLOTB = T > 0 ? kMaxChunkF * 16 + (T > 3 ? kMaxChunkF * 4 : 0) : 0;
   static constexpr int NBUF0 = (kLdsBytes - SLOTB) / BUF;
   static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
-  static_assert(NBUF >= 2, "tile buffers do not fit in LDS");
+  static_assert(NBUF >= 3, "tile buffers do not fit in LDS");
   static constexpr int LDS = NBUF * BUF + SLOTB;
-  // LDS-DMA instructions the loader issues per tile
-  static constexpr int OPT = 2 * (QB / 1024) + VB / 1024 + NSM + T * (RECB / 1024);
-  static_assert(QB % 1024 == 0 && VB % 1024 == 0 && RDB % 1024 == 0, "tile arrays must be whole DMA blocks");
+  // LDS-DMA instructions the DMA wave issues per tile
+  static constexpr int OPT = 2 * (QB / 1024) + VB / 1024 + NSM + T * (RKB / 1024);
+  static_assert(QB % 1024 == 0 && VB % 1024 == 0, "tile arrays must be whole DMA blocks");
   static_assert((2 + T) * 16 <= 128, "too many record depths for the small-value block");
+  static_assert(T <= 4, "the schedule table holds at most four record depths");
+  // the sort's bucket counts live in the (not yet used) tile ring
+  static constexpr int SORT_CAP = NBUF * BUF / 4 < kSortMax ? NBUF * BUF / 4 : kSortMax;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -110,6 +137,19 @@ __device__ __forceinline__ int lds_read_opaque(const void* p) {
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
   return v;
 }
+__device__ __forceinline__ u32x4 lds_read128_opaque(const void* p) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+
+// Raw buffer resource (gfx9 layout) over `bytes` bytes at `base`: stores at
+// offsets past the end are dropped by the hardware, which lets every lane
+// issue the same stores whatever its beam.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_window(void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+constexpr int kOutside = 0x7FFFFFF0;  // an offset past every store window
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -121,13 +161,15 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   using G = FusedGeom<DK, DV, T>;
   constexpr int KS = G::KS;
   constexpr int NPL = 3;
+  constexpr int TT = T > 0 ? T : 1;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
-  int* s_slot = reinterpret_cast<int*>(smem + G::NBUF * G::BUF);  // [T][kMaxChunkF]
+  u32x4* s_tab = reinterpret_cast<u32x4*>(smem + G::NBUF * G::BUF);          // [position]
+  int* s_slot3 = reinterpret_cast<int*>(smem + G::NBUF * G::BUF + kMaxChunkF * 16);  // T == 4
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   // Workgroups are handed to the 8 XCDs round-robin; renumber them so that
-  // the chunks of one (r, h) run on one XCD and share its L2.
+  // the chunks of one (r, h), and the heads of one request, share an XCD.
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
@@ -139,45 +181,103 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   const int b_end = min(b_begin + a.chunk, a.Wt);
   const int nb = b_end - b_begin;
   const int ntiles = (nb + 15) >> 4;
+  const int g = lane >> 4;
+  const int c = lane & 15;
 
-  if (w == G::NW) {
-    // ================================================================ loader
+  // Barriers: P (schedule table written), A (tile 0 resident), then
+  // 0 .. ntiles.
+  // Between barrier i and i + 1 the consumers take tile i, the dot wave
+  // tile i + 1, and a DMA wave refills the buffer of tile i - 1.
+
+  if (w >= G::WDMA && w < G::WDMA + G::NDMA) {
+    // ============================================================ DMA waves
+    const int dw = w - G::WDMA;  // this wave owns tiles p with p % 2 == dw
     const int cg = lane >> 4;
-    if constexpr (T > 0) {
+    if (T > 0 && dw == 0) {
       // Ancestry (§3.3): h_t(b, T-1) = parent, h_t(b, j) = h_{T-1}(parent, j).
       // All parent pointers first, then all parent rows, with every load
       // unconditional (indices past the chunk repeat its last beam) so that
       // each batch is one round trip.
       constexpr int QMAX = kMaxChunkF / 64;
-      int slot[QMAX][T];
+      int slot[QMAX][TT], key[QMAX], pos[QMAX];
 #pragma unroll
       for (int qi = 0; qi < QMAX; ++qi) {
         const int i = min(lane + 64 * qi, nb - 1);
-        slot[qi][T - 1] = clampi(a.parent[(size_t)r * a.Wt + b_begin + i], 0, a.Wm - 1);
+        slot[qi][TT - 1] = clampi(a.parent[(size_t)r * a.Wt + b_begin + i], 0, a.Wm - 1);
       }
 #pragma unroll
       for (int qi = 0; qi < QMAX; ++qi) {
-        const int32_t* prow = a.anc + (((size_t)(T - 1) * a.R + r) * a.Wm + slot[qi][T - 1]) * a.L;
+        const int32_t* prow = a.anc + (((size_t)(TT - 1) * a.R + r) * a.Wm + slot[qi][TT - 1]) * a.L;
 #pragma unroll
         for (int j = 0; j < T - 1; ++j) slot[qi][j] = clampi(prow[j], 0, a.Wm - 1);
+        // the parent's position in the previous step's order (its own slot
+        // when the previous step is the first)
+        key[qi] = T > 1 ? clampi(prow[a.L - 1], 0, a.Wm - 1) : slot[qi][TT - 1];
       }
-      // (table rows past the chunk hold copies and are never read)
+      if (a.nchunk == 1 && a.Wm <= G::SORT_CAP) {
+        // stable-enough counting sort by key (ties in any order): bucket
+        // counts with LDS atomics, an exclusive scan over the buckets, then
+        // each beam's position = bucket start + its rank in the bucket.  One
+        // wave: its LDS accesses complete in program order.
+        int* hist = reinterpret_cast<int*>(smem);  // scratch in the tile ring, not yet in use
+        for (int x = lane; x < a.Wm; x += 64) hist[x] = 0;
+#pragma unroll
+        for (int qi = 0; qi < QMAX; ++qi)
+          if (lane + 64 * qi < nb) pos[qi] = atomicAdd(&hist[key[qi]], 1);
+        const int per = (a.Wm + 63) / 64;
+        const int x0 = min(lane * per, a.Wm), x1 = min(x0 + per, a.Wm);
+        int local = 0;
+        for (int x = x0; x < x1; ++x) local += hist[x];
+        int incl = local;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(incl, d);
+          if (lane >= d) incl += y;
+        }
+        int run = incl - local;
+        for (int x = x0; x < x1; ++x) {
+          const int cnt = hist[x];
+          hist[x] = run;
+          run += cnt;
+        }
+#pragma unroll
+        for (int qi = 0; qi < QMAX; ++qi)
+          if (lane + 64 * qi < nb) pos[qi] += hist[key[qi]];
+      } else {
+#pragma unroll
+        for (int qi = 0; qi < QMAX; ++qi) pos[qi] = lane + 64 * qi;
+      }
+      // Schedule table, this step's ancestry rows, and each beam's position
+      // (read by the next step) in the unused last entry of its row.
 #pragma unroll
       for (int qi = 0; qi < QMAX; ++qi) {
         const int i = lane + 64 * qi;
+        if (i < nb) {
+          s_tab[pos[qi]] = u32x4{(uint32_t)i, (uint32_t)slot[qi][0], (uint32_t)slot[qi][T > 1 ? 1 : 0],
+                                 (uint32_t)slot[qi][T > 2 ? 2 : 0]};
+          if constexpr (T > 3) s_slot3[pos[qi]] = slot[qi][3];
+          if (h == 0) {
+            int32_t* crow = a.anc + (((size_t)T * a.R + r) * a.Wm + b_begin + i) * a.L;
 #pragma unroll
-        for (int j = 0; j < T; ++j) s_slot[j * kMaxChunkF + i] = slot[qi][j];
-        if (h == 0 && i < nb) {
-          int32_t* crow = a.anc + (((size_t)T * a.R + r) * a.Wm + b_begin + i) * a.L;
-#pragma unroll
-          for (int j = 0; j < T; ++j) crow[j] = slot[qi][j];
+            for (int j = 0; j < T; ++j) crow[j] = slot[qi][j];
+            crow[a.L - 1] = pos[qi];
+          }
         }
       }
     }
 
     auto dma_tile = [&](int p) {
       uint8_t* buf = smem + (p % G::NBUF) * G::BUF;
-      const int ib = min(p * 16 + (lane & 15), nb - 1);  // rows past the chunk repeat its last beam
+      const int posi = min(p * 16 + (lane & 15), nb - 1);  // positions past the chunk repeat its last
+      int ib = posi, sl[4] = {0, 0, 0, 0};
+      if constexpr (T > 0) {
+        const u32x4 e = lds_read128_opaque(&s_tab[posi]);
+        ib = (int)e[0];
+        sl[0] = (int)e[1];
+        sl[1] = (int)e[2];
+        sl[2] = (int)e[3];
+        if constexpr (T > 3) sl[3] = lds_read_opaque(&s_slot3[posi]);
+      }
       const size_t tok = ((size_t)r * a.Wt + b_begin + ib) * a.H + h;
       const uint16_t* qrow = a.q + tok * DK;
       const uint16_t* krow = a.k + tok * DK;
@@ -188,21 +288,14 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
       for (int m = 0; m < G::QB / 1024; ++m) dma16(krow + (m * 4 + cg) * 8, buf + G::OKK + m * 1024);
 #pragma unroll
       for (int m = 0; m < G::VB / 1024; ++m) dma16(vrow + (m * 4 + cg) * 8, buf + G::OV + m * 1024);
-      size_t rj[T > 0 ? T : 1];
+      size_t rj[TT];
 #pragma unroll
-      for (int j = 0; j < T; ++j) {
-        const int slot = lds_read_opaque(&s_slot[j * kMaxChunkF + ib]);
-        rj[j] = (((size_t)j * a.R + r) * a.Wm + slot) * a.H + h;
-      }
+      for (int j = 0; j < T; ++j) rj[j] = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + h;
 #pragma unroll
-      for (int j = 0; j < T; ++j) {
-        uint8_t* rec = buf + G::OR + j * G::RECB;
+      for (int j = 0; j < T; ++j)
 #pragma unroll
-        for (int m = 0; m < G::RKB / 1024; ++m) dma16(a.rec_k + rj[j] * DK + (m * 4 + cg) * 8, rec + m * 1024);
-#pragma unroll
-        for (int m = 0; m < G::RDB / 1024; ++m)
-          dma16(a.rec_delta + rj[j] * DV + (m * 4 + cg) * 4, rec + G::RKB + m * 1024);
-      }
+        for (int m = 0; m < G::RKB / 1024; ++m)
+          dma16(a.rec_k + rj[j] * DK + (m * 4 + cg) * 8, buf + G::ORK + j * G::RKB + m * 1024);
       // dword block: group 0 alpha_t, 1 beta_t, 2 + j alpha_j (16 beams each)
 #pragma unroll
       for (int n = 0; n < G::NSM; ++n) {
@@ -215,157 +308,194 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
       }
     };
 
+    // tiles this wave issued after tile q, up to tile `last`
+    auto later = [&](int q, int last) { return last > q ? (last - q) / 2 : 0; };
+    lds_barrier();  // P
     const int npro = min(G::NBUF - 1, ntiles);
-    for (int p = 0; p < npro; ++p) dma_tile(p);
-    wait_tiles<G::OPT, G::NBUF - 2>(npro - 1);  // tile 0 resident
-    lds_barrier();
+    for (int p = dw; p < npro; p += 2) dma_tile(p);
+    if (dw == 0) wait_tiles<G::OPT, 2>(later(0, npro - 1));  // tile 0 resident
+    lds_barrier();                                          // A
+    if (dw == 1) wait_tiles<G::OPT, 2>(later(1, npro - 1));  // tile 1 resident
+    lds_barrier();                                          // 0
     for (int i = 0; i < ntiles; ++i) {
-      // the consumers released buffer (i - 1) % NBUF at the last barrier
-      if (i + G::NBUF - 1 < ntiles) dma_tile(i + G::NBUF - 1);
-      const int last = min(i + G::NBUF - 1, ntiles - 1);
-      wait_tiles<G::OPT, G::NBUF - 2>(max(0, last - (i + 1)));  // tile i + 1 resident
-      lds_barrier();
+      // buffer (i - 1) % NBUF was released at the last barrier
+      const int p = i + G::NBUF - 1;
+      if (p < ntiles && (p & 1) == dw) dma_tile(p);
+      const int last = min(p, ntiles - 1);
+      if (i + 2 < ntiles && ((i + 2) & 1) == dw) wait_tiles<G::OPT, 2>(later(i + 2, last));  // tile i + 2 resident
+      lds_barrier();                                                                     // i + 1
     }
     return;
   }
 
-  // ================================================================ consumers
-  const int g = lane >> 4;
-  const int c = lane & 15;
+  if (w == G::WDOT) {
+    // ============================================================ dot wave
+    auto dots = [&](int p) {
+      uint8_t* buf = smem + (p % G::NBUF) * G::BUF;
+      const float* sm = reinterpret_cast<const float*>(buf + G::OS);
+      u32x4 qf[KS], kf[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        qf[s] = *reinterpret_cast<const u32x4*>(buf + G::OQ + (s * 64 + lane) * 16);
+        kf[s] = *reinterpret_cast<const u32x4*>(buf + G::OKK + (s * 64 + lane) * 16);
+      }
+      float wt[3 + 2 * T];
+      float sqq = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sqq = dot2(kf[s][e], qf[s][e], sqq);
+      float cdec = sm[c];  // alpha_t
+#pragma unroll
+      for (int j = T - 1; j >= 0; --j) {
+        float pq = 0.f, pk = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const u32x4 kj = *reinterpret_cast<const u32x4*>(buf + G::ORK + j * G::RKB + (s * 64 + lane) * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pq = dot2(kj[e], qf[s][e], pq);
+            pk = dot2(kj[e], kf[s][e], pk);
+          }
+        }
+        wt[3 + j] = cdec * sum_lane_groups(pq);
+        wt[3 + T + j] = cdec * sum_lane_groups(pk);
+        cdec *= sm[(2 + j) * 16 + c];
+      }
+      wt[0] = cdec;
+      wt[1] = sm[16 + c];
+      wt[2] = sum_lane_groups(sqq);
+      float* wout = reinterpret_cast<float*>(buf + G::OW) + c * G::NWT;
+#pragma unroll
+      for (int v = 0; v < 3 + 2 * T; ++v)
+        if ((v & 3) == g) wout[v] = wt[v];
+    };
+    lds_barrier();  // P
+    lds_barrier();  // A
+    dots(0);
+    lds_barrier();  // 0
+    for (int i = 0; i < ntiles; ++i) {
+      if (i + 1 < ntiles) dots(i + 1);
+      lds_barrier();  // i + 1
+    }
+    return;
+  }
 
+  // ============================================================ consumers
   // This wave's slice of S0[r, h] as bf16 planes in the MFMA A layout: lane
-  // (g, c) of tile mt holds key channels 32s + 8g .. +7 of value row
-  // 32w + 16mt + c, so C row 4g + i of tile mt is value row 32w + 16mt + 4g + i.
-  u32x4 As[2][KS][NPL];
+  // (g, c) holds key channels 32s + 8g .. +7 of value row 16w + c, so C row
+  // 4g + i is value row 16w + 4g + i.
+  u32x4 As[KS][NPL];
   {
     const float* S = a.S + ((size_t)r * a.H + h) * DK * DV;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int col = w * 32 + mt * 16 + c;
+    for (int s = 0; s < KS; ++s) {
+      float x[8];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = S[(size_t)(s * 32 + g * 8 + e) * DV + col];
-        split_planes<NPL>(x, As[mt][s]);
-      }
+      for (int e = 0; e < 8; ++e) x[e] = S[(size_t)(s * 32 + g * 8 + e) * DV + w * 16 + c];
+      split_planes<NPL>(x, As[s]);
     }
   }
-  lds_barrier();
+  const int row0 = w * 16 + 4 * g;  // first of this lane's 4 value rows
+
+  // Store windows over the chunk's beams [b_begin, b_end): a lane whose beam
+  // is past the chunk (last tile) lands outside its window.
+  const int so = a.H * DV * 4, sk = a.H * DK * 2, sa = a.H * 4;  // bytes between beams
+  const size_t tok0 = ((size_t)r * a.Wt + b_begin) * a.H + h;
+  const size_t rec0 = (((size_t)T * a.R + r) * a.Wm + b_begin) * a.H + h;
+  const __amdgpu_buffer_rsrc_t w_o = store_window(a.o + tok0 * DV, (nb - 1) * so + DV * 4);
+  const __amdgpu_buffer_rsrc_t w_d = store_window(a.rec_delta + rec0 * DV, (nb - 1) * so + DV * 4);
+  const __amdgpu_buffer_rsrc_t w_k = store_window(a.rec_k + rec0 * DK, (nb - 1) * sk + DK * 2);
+  const __amdgpu_buffer_rsrc_t w_a = store_window(a.rec_alpha + rec0, (nb - 1) * sa + 4);
+  // this wave's share of the appended key row: 4 channels per lane
+  const int ks = w >> 1, kh = w & 1;
+
+  // ancestral update vectors of one tile, this lane's 4 rows of beam c
+  auto load_deltas = [&](int p, f32x4* d) {
+    if constexpr (T > 0) {
+      const int posi = min(p * 16 + c, nb - 1);
+      const u32x4 e = s_tab[posi];
+      const int sl[4] = {(int)e[1], (int)e[2], (int)e[3], T > 3 ? s_slot3[posi] : 0};
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const size_t rj = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + h;
+        d[j] = *reinterpret_cast<const f32x4*>(a.rec_delta + rj * DV + row0);
+      }
+    }
+  };
+
+  lds_barrier();  // P: schedule table written
+  f32x4 dnext[TT];
+  load_deltas(0, dnext);  // in flight while tile 0 arrives
+  lds_barrier();  // A: tile 0 resident
+  lds_barrier();  // 0
 
   for (int it = 0; it < ntiles; ++it) {
-    const uint8_t* buf = smem + (it % G::NBUF) * G::BUF;
-    const float* sm = reinterpret_cast<const float*>(buf + G::OS);
+    f32x4 dcur[TT];
+#pragma unroll
+    for (int j = 0; j < T; ++j) dcur[j] = dnext[j];
+    if (it + 1 < ntiles) load_deltas(it + 1, dnext);
 
+    const uint8_t* buf = smem + (it % G::NBUF) * G::BUF;
     u32x4 qf[KS], kf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       qf[s] = *reinterpret_cast<const u32x4*>(buf + G::OQ + (s * 64 + lane) * 16);
       kf[s] = *reinterpret_cast<const u32x4*>(buf + G::OKK + (s * 64 + lane) * 16);
     }
-    u32x2 vw[2];
+    const int vch = w * 2 + (g >> 1);  // 16-byte v chunk holding rows row0 .. row0 + 3
+    const u32x2 vw = *reinterpret_cast<const u32x2*>(buf + G::OV + ((vch >> 2) * 64 + (vch & 3) * 16 + c) * 16 +
+                                                     (g & 1) * 8);
+    float wt[G::NWT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int ch = w * 4 + mt * 2 + (g >> 1);
-      vw[mt] = *reinterpret_cast<const u32x2*>(buf + G::OV + ((ch >> 2) * 64 + (ch & 3) * 16 + c) * 16 + (g & 1) * 8);
+    for (int v = 0; v < G::NWT; v += 4) {
+      const f32x4 q4 = *reinterpret_cast<const f32x4*>(buf + G::OW + (c * G::NWT + v) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wt[v + e] = q4[e];
     }
-    const float at = sm[c];
-    const float bt = sm[16 + c];
 
     // S0^T [q | k] on the matrix cores, smallest plane first
-    f32x4 uq[2], uk[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      uq[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      uk[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    f32x4 uq = {0.f, 0.f, 0.f, 0.f}, uk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int p = NPL - 1; p >= 0; --p) {
-          uq[mt] = mfma16x16x32(As[mt][s][p], qf[s], uq[mt]);
-          uk[mt] = mfma16x16x32(As[mt][s][p], kf[s], uk[mt]);
-        }
-
-    float sqq = 0.f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sqq = dot2(kf[s][e], qf[s][e], sqq);
-    sqq = sum_lane_groups(sqq);
-
-    // Replay of the ancestral records j = 0 .. T-1 (§3.2) with the decays
-    // gathered into per-beam scalars: alpha_t u^(T-1) = c_0 u^(-1) +
-    // sum_j c_{j+1} (k_j . x) delta_j, where c_j = alpha_t prod_{i >= j} alpha_i
-    // over the chain (c_T = alpha_t), so every record costs one FMA per
-    // value row and projection.
-    float wq[T > 0 ? T : 1], wk[T > 0 ? T : 1];
-    float cdec = at;
-#pragma unroll
-    for (int j = T - 1; j >= 0; --j) {
-      const uint8_t* rec = buf + G::OR + j * G::RECB;
-      float pq = 0.f, pk = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const u32x4 kj = *reinterpret_cast<const u32x4*>(rec + (s * 64 + lane) * 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pq = dot2(kj[e], qf[s][e], pq);
-          pk = dot2(kj[e], kf[s][e], pk);
-        }
+      for (int p = NPL - 1; p >= 0; --p) {
+        uq = mfma16x16x32(As[s][p], qf[s], uq);
+        uk = mfma16x16x32(As[s][p], kf[s], uk);
       }
-      wq[j] = cdec * sum_lane_groups(pq);
-      wk[j] = cdec * sum_lane_groups(pk);
-      cdec *= sm[(2 + j) * 16 + c];
-    }
-    f32x4 xq[2], xk[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      xq[mt] = cdec * uq[mt];
-      xk[mt] = cdec * uk[mt];
-    }
+
+    // replay (§3.2) with the dot wave's weights, then the current transition
+    f32x4 xq = wt[0] * uq, xk = wt[0] * uk;
 #pragma unroll
     for (int j = 0; j < T; ++j) {
-      const uint8_t* rec = buf + G::OR + j * G::RECB;
+      xq += wt[3 + j] * dcur[j];
+      xk += wt[3 + T + j] * dcur[j];
+    }
+    f32x4 dt, ot;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const f32x4 dj = *reinterpret_cast<const f32x4*>(rec + G::RKB + ((w * 2 + mt) * 64 + lane) * 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          xq[mt][i] += wq[j] * dj[i];
-          xk[mt][i] += wk[j] * dj[i];
-        }
-      }
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t word = vw[i >> 1];
+      const float vv = (i & 1) ? bf16_hi(word) : bf16_lo(word);
+      dt[i] = wt[1] * (vv - xk[i]);
+      ot[i] = xq[i] + dt[i] * wt[2];
     }
 
-    // current transition and append (§3.2, §3.4)
-    f32x4 dt[2], ot[2];
+    // output and append (§3.4): every wave issues the same four stores; a
+    // position past the chunk stores outside the windows
+    const int posi = it * 16 + c;
+    const int ib = posi >= nb ? kOutside / so : (T > 0 ? (int)s_tab[posi][0] : posi);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, ib * so + row0 * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, ib * so + row0 * 4, 0, 0);
+    u32x4 kk = kf[0];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t word = vw[mt][i >> 1];
-        const float vv = (i & 1) ? bf16_hi(word) : bf16_lo(word);
-        dt[mt][i] = bt * (vv - xk[mt][i]);
-        ot[mt][i] = xq[mt][i] + dt[mt][i] * sqq;
-      }
-    const int b = b_begin + it * 16 + c;
-    if (b < b_end) {
-      const size_t tok = ((size_t)r * a.Wt + b) * a.H + h;
-      const size_t rec_t = (((size_t)T * a.R + r) * a.Wm + b) * a.H + h;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        *reinterpret_cast<f32x4*>(a.o + tok * DV + w * 32 + mt * 16 + 4 * g) = ot[mt];
-        *reinterpret_cast<f32x4*>(a.rec_delta + rec_t * DV + w * 32 + mt * 16 + 4 * g) = dt[mt];
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        if (s % G::NW == w) *reinterpret_cast<u32x4*>(a.rec_k + rec_t * DK + s * 32 + g * 8) = kf[s];
-      if (w == 0 && g == 0) a.rec_alpha[rec_t] = at;
-    }
-    lds_barrier();
+    for (int s = 1; s < KS; ++s)
+      if (ks == s) kk = kf[s];
+    __builtin_amdgcn_raw_buffer_store_b64(kh ? u32x2{kk[2], kk[3]} : u32x2{kk[0], kk[1]}, w_k,
+                                          ib * sk + (ks * 32 + g * 8 + kh * 4) * 2, 0, 0);
+    const float at = *reinterpret_cast<const float*>(buf + G::OS + c * 4);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(at), w_a,
+                                          (w == G::NC - 1 && g == 0) ? ib * sa : kOutside, 0, 0);
+    lds_barrier();  // it + 1
   }
 }
 
@@ -403,14 +533,8 @@ int launch(const gdn_shape& sh, const gdn_store& st, int Wt, const StepIO& io, h
   a.L = sh.L_max;
   a.t = T;
   a.Wt = Wt;
-  // as many workgroups as can be resident at once
-  static const int per_cu = [] {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_beam_fused<DK, DV, T>, G::NT, 0) != hipSuccess || n < 1)
-      n = 1;
-    return n;
-  }();
-  a.chunk = pick_chunk(sh.R * sh.H, Wt, kMaxChunkF, cu_count() * per_cu);
+  // one workgroup per compute unit: the tile ring takes most of its LDS
+  a.chunk = pick_chunk(sh.R * sh.H, Wt, kMaxChunkF, cu_count());
   a.nchunk = (Wt + a.chunk - 1) / a.chunk;
   const long grid = (long)sh.R * sh.H * a.nchunk;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
