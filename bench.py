@@ -88,6 +88,111 @@ def cpu_baseline(inp, n_pairs, workers):
     }
 
 
+def _timed(torch, stream, fn, reps):
+    """Mean duration (us) of fn() over reps calls, each bracketed by HIP
+    events recorded on the launch stream."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+
+def _bw(nbytes, us):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"bytes": float(nbytes), "us": us, "achieved_GBps": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+
+def beam_row(B, torch, dev, stream, wl, reps):
+    """The L decode steps of a beam workload: per-launch durations and
+    bandwidth under the unique-record byte model."""
+    inp = wl.inputs()
+    steps = [B.upload(st, dev) for st in inp["steps"]]
+    store = B.Store(wl.R, wl.W, wl.H, wl.dk, wl.dv, wl.L, channel_decay=wl.channel_decay,
+                    S=torch.from_numpy(inp["S0"]).to(dev))
+    outs = [torch.empty(wl.R, wl.W, wl.H, wl.dv, dtype=torch.float32, device=dev) for _ in range(wl.L)]
+
+    def launch(t):
+        d = steps[t]
+        B.decode_step(store, t, wl.W, d.get("parent"), d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                      o=outs[t], stream=stream)
+
+    for _ in range(2):
+        for t in range(wl.L):
+            launch(t)
+    torch.cuda.synchronize()
+    us = [0.0] * wl.L
+    for _ in range(reps):  # keep the step order: step t reads step t-1's records
+        for t in range(wl.L):
+            us[t] += _timed(torch, stream, lambda: launch(t), 1) / reps
+    anc = store.anc.cpu().numpy()
+    per = []
+    for t in range(wl.L):
+        uniq = sum(accounting.unique_ancestors(anc[t, r, :, :t], wl.W) for r in range(wl.R))
+        nbytes = accounting.beam_step_bytes(R=wl.R, H=wl.H, dk=wl.dk, dv=wl.dv, W_t=wl.W, t=t,
+                                            channel_decay=wl.channel_decay, unique_records=uniq)
+        per.append(_bw(nbytes, us[t]))
+    tot_b, tot_us = sum(p["bytes"] for p in per), sum(us)
+    return {"workload": wl.name, "beam_steps_per_s": wl.R * wl.W * wl.L / (tot_us * 1e-6),
+            "launch_us": us, **{k: v for k, v in _bw(tot_b / wl.L, tot_us / wl.L).items() if k != "us"}}
+
+
+def sequence_row(B, torch, dev, stream, wl):
+    """Bounded-log decoding of independent sequences: every token's decode
+    (log length token mod M) and the merge after every M tokens."""
+    seq = wl.inputs()
+    store = B.Store(wl.R, 1, wl.H, wl.dk, wl.dv, wl.M, channel_decay=wl.channel_decay,
+                    S=torch.from_numpy(seq["S0"]).to(dev))
+    toks = [B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")}, dev)
+            for i in range(wl.T)]
+    zero = torch.zeros(wl.R, 1, dtype=torch.int32, device=dev)
+    o = torch.empty(wl.R, 1, wl.H, wl.dv, dtype=torch.float32, device=dev)
+
+    def decode(i):
+        d = toks[i]
+        B.decode_step(store, i % wl.M, 1, zero, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o=o, stream=stream)
+
+    dec_us = [0.0] * wl.M
+    merge_us, n_merge = 0.0, 0
+    for i in range(wl.T):
+        dec_us[i % wl.M] += _timed(torch, stream, lambda: decode(i), 1) * wl.M / wl.T
+        if i % wl.M == wl.M - 1:
+            merge_us += _timed(torch, stream, lambda: B.log_merge(store, wl.M, 0, stream=stream), 1)
+            n_merge += 1
+    merge_us /= max(n_merge, 1)
+    dec_b = [accounting.sequence_token_bytes(R=wl.R, H=wl.H, dk=wl.dk, dv=wl.dv, log_len=j,
+                                             channel_decay=wl.channel_decay) for j in range(wl.M)]
+    mrg_b = accounting.merge_bytes(R=wl.R, H=wl.H, dk=wl.dk, dv=wl.dv, n_rec=wl.M, channel_decay=wl.channel_decay)
+    cycle_us = sum(dec_us) + merge_us
+    return {"workload": wl.name, "sequence_steps_per_s": wl.R * wl.M / (cycle_us * 1e-6),
+            "us_per_token_amortised": cycle_us / wl.M,
+            "decode": {**_bw(float(np.mean(dec_b)), float(np.mean(dec_us))), "us_by_log_length": dec_us},
+            "merge": _bw(mrg_b, merge_us),
+            "cycle": _bw(sum(dec_b) + mrg_b, cycle_us)}
+
+
+def materialize_row(B, torch, dev, stream, wl, n_items, reps):
+    """Dense states of n_items beams after the last step of a beam workload."""
+    inp = wl.inputs()
+    store = B.Store(wl.R, wl.W, wl.H, wl.dk, wl.dv, wl.L, channel_decay=wl.channel_decay,
+                    S=torch.from_numpy(inp["S0"]).to(dev))
+    for t, st in enumerate(inp["steps"]):
+        d = B.upload(st, dev)
+        B.decode_step(store, t, wl.W, d.get("parent"), d["q"], d["k"], d["v"], d["alpha"], d["beta"], stream=stream)
+    rng = np.random.default_rng(0)
+    pairs = np.stack([np.arange(n_items) % wl.R, rng.integers(0, wl.W, n_items)], 1).astype(np.int32)
+    rb = torch.from_numpy(pairs).to(dev)
+    out = torch.empty(n_items, wl.H, wl.dk, wl.dv, dtype=torch.float32, device=dev)
+    B.materialize(store, wl.L - 1, rb, out=out, stream=stream)
+    us = _timed(torch, stream, lambda: B.materialize(store, wl.L - 1, rb, out=out, stream=stream), reps)
+    rec = accounting.record_bytes(wl.dk, wl.dv, wl.channel_decay)
+    reqs = len(set(pairs[:, 0].tolist()))
+    nbytes = reqs * wl.H * 4 * wl.dk * wl.dv + n_items * wl.H * (4 * wl.dk * wl.dv + wl.L * rec)
+    return {"workload": f"{wl.name}: {n_items} beams after step {wl.L - 1}", **_bw(nbytes, us)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +201,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=32)
     ap.add_argument("--cpu-workers", type=int, default=0)
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the other path rows (channel decay, bounded log, materialise)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the warm-up, run a plain device copy of this many MiB three times "
                          "(a known-size reference for HBM byte counters)")
@@ -208,6 +315,14 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if not args.no_rows:
+        reps = max(3, min(args.steps, 10))
+        line["rows"] = {
+            "single_request_beam_decode": beam_row(B, torch, dev, stream, configs.SINGLE, reps),
+            "channel_decay_beam_decode": beam_row(B, torch, dev, stream, configs.KDA, reps),
+            "bounded_log_decode_and_merge": sequence_row(B, torch, dev, stream, configs.DELTALOG),
+            "materialize": materialize_row(B, torch, dev, stream, WORKLOAD, 64, reps),
+        }
     print(json.dumps(line), flush=True)
 
 

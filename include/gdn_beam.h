@@ -80,7 +80,13 @@ typedef struct gdn_store {
   uint16_t* rec_k;   /* [L_max][R][W_max][H][dk]  bf16 keys (bit copies)     */
   float* rec_alpha;  /* [L_max][R][W_max][H][A]   FP32 decays                */
   int32_t* anc;      /* [L_max][R][W_max][L_max]  ancestry: anc[t][r][b][j] =
-                        h_t(b, j), j < t (entries j >= t unused)             */
+                        h_t(b, j), j < t.  The decode step may keep in the
+                        last entry, anc[t][r][b][L_max-1], the beam's
+                        position in the depth-first order of the beam tree
+                        (read by step t+1 to schedule beams that share
+                        ancestors together; any value there only affects
+                        speed, never results).  Other entries j >= t are
+                        unused.                                               */
 } gdn_store;
 
 /*
