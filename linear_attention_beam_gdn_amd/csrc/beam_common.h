@@ -64,15 +64,14 @@ __device__ __forceinline__ void load_f32x8(const float* p, float* x) {
 template <int NP>
 __device__ __forceinline__ void split_planes(const float* x, u32x4* planes) {
 #pragma unroll
-  for (int p = 0; p < NP; ++p) planes[p] = u32x4{0, 0, 0, 0};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float rem = x[e];
+  for (int e = 0; e < 8; e += 2) {
+    float r0 = x[e], r1 = x[e + 1];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const uint32_t hb = bf16_rne(rem);
-      rem -= bf16_at(uint16_t(hb));
-      planes[p][e >> 1] |= hb << (16 * (e & 1));
+      const uint32_t hb = bf16x2_rne(r0, r1);
+      planes[p][e >> 1] = hb;
+      r0 -= bf16_lo(hb);
+      r1 -= bf16_hi(hb);
     }
   }
 }

@@ -1,0 +1,181 @@
+// Device helpers shared by the fused beam decode kernels (scalar and
+// per-channel decay): LDS-DMA staging with counted waits, barriers, opaque
+// LDS reads, store windows, and the ancestry-order schedule of a chunk.
+#pragma once
+
+#include "beam_common.h"
+
+namespace gdn {
+namespace fused {
+
+constexpr int kMaxChunkF = 512;         // beams per workgroup at most
+constexpr int kLdsBytes = 160 * 1024;   // LDS of one gfx950 compute unit
+constexpr int kSortMax = 8192;          // largest W_max whose tree order is computed
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
+// 64 lanes x 16 (or 4) bytes from per-lane global addresses into the LDS
+// block at `blk` (wave-uniform), lane l at blk + l * size.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* blk) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)blk, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, uint8_t* blk) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)blk, 4, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N < 63 ? N : 63) : "memory");
+}
+
+// Wait until at most k tiles of OPT loads each (k <= KMAX) are in flight.
+template <int OPT, int KMAX>
+__device__ __forceinline__ void wait_tiles(int k) {
+  if constexpr (KMAX >= 4)
+    if (k >= 4) return wait_vm<4 * OPT>();
+  if constexpr (KMAX >= 3)
+    if (k == 3) return wait_vm<3 * OPT>();
+  if constexpr (KMAX >= 2)
+    if (k == 2) return wait_vm<2 * OPT>();
+  if constexpr (KMAX >= 1)
+    if (k == 1) return wait_vm<OPT>();
+  wait_vm<0>();
+}
+
+// Workgroup barrier after this wave's LDS accesses have completed; also a
+// compiler barrier for memory accesses.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// LDS read issued as opaque assembly: the compiler does not order it behind
+// this wave's outstanding LDS-DMA loads (which target other LDS bytes).
+__device__ __forceinline__ int lds_read_opaque(const void* p) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+__device__ __forceinline__ u32x4 lds_read128_opaque(const void* p) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+
+// Raw buffer resource (gfx9 layout) over `bytes` bytes at `base`: stores at
+// offsets past the end are dropped by the hardware, which lets every lane
+// issue the same stores whatever its beam.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_window(void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+constexpr int kOutside = 0x7FFFFFF0;  // an offset past every store window
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Schedule of a chunk for a decode step with T records per chain (run by one
+// wave).  Builds the chunk's ancestry (OneLA §3.3: h_t(b, T-1) = parent,
+// h_t(b, j) = h_{T-1}(parent, j)), orders the beams depth-first in the beam
+// tree when the chunk holds the whole step (a counting sort of the beams by
+// their parent's position in the previous step's order, with the bucket
+// counts in `scratch`), and writes
+//   s_tab[position]  = {beam, slot_0, slot_1, slot_2}, s_slot3[position] = slot_3,
+//   anc row T of every beam (h == 0 workgroups), with the beam's position in
+//   the unused last entry for the next step.
+// The order only decides which lanes compute a beam, never its result.
+template <int T>
+__device__ __forceinline__ void build_schedule(const BeamArgs& a, int r, int h, int b_begin, int nb, int lane,
+                                               int sort_cap, uint8_t* scratch, u32x4* s_tab, int* s_slot3) {
+  constexpr int TT = T > 0 ? T : 1;
+  uint8_t* smem = scratch;
+  // Ancestry (§3.3): h_t(b, T-1) = parent, h_t(b, j) = h_{T-1}(parent, j).
+  // All parent pointers first, then all parent rows, with every load
+  // unconditional (indices past the chunk repeat its last beam) so that
+  // each batch is one round trip.
+  constexpr int QMAX = kMaxChunkF / 64;
+  int slot[QMAX][TT], key[QMAX], pos[QMAX];
+#pragma unroll
+  for (int qi = 0; qi < QMAX; ++qi) {
+    const int i = min(lane + 64 * qi, nb - 1);
+    slot[qi][TT - 1] = clampi(a.parent[(size_t)r * a.Wt + b_begin + i], 0, a.Wm - 1);
+  }
+#pragma unroll
+  for (int qi = 0; qi < QMAX; ++qi) {
+    const int32_t* prow = a.anc + (((size_t)(TT - 1) * a.R + r) * a.Wm + slot[qi][TT - 1]) * a.L;
+#pragma unroll
+    for (int j = 0; j < T - 1; ++j) slot[qi][j] = clampi(prow[j], 0, a.Wm - 1);
+    // the parent's position in the previous step's order (its own slot
+    // when the previous step is the first)
+    key[qi] = T > 1 ? clampi(prow[a.L - 1], 0, a.Wm - 1) : slot[qi][TT - 1];
+  }
+  const bool sorted = a.nchunk == 1 && a.Wm <= sort_cap;
+  if (sorted) {
+    // stable-enough counting sort by key (ties in any order): bucket
+    // counts with LDS atomics, an exclusive scan over the buckets, then
+    // each beam's position = bucket start + its rank in the bucket.  One
+    // wave: its LDS accesses complete in program order.
+    int* hist = reinterpret_cast<int*>(smem);  // scratch in the tile ring, not yet in use
+    for (int x = lane; x < a.Wm; x += 64) hist[x] = 0;
+#pragma unroll
+    for (int qi = 0; qi < QMAX; ++qi)
+      if (lane + 64 * qi < nb) pos[qi] = atomicAdd(&hist[key[qi]], 1);
+    const int per = (a.Wm + 63) / 64;
+    const int x0 = min(lane * per, a.Wm), x1 = min(x0 + per, a.Wm);
+    int local = 0;
+    for (int x = x0; x < x1; ++x) local += hist[x];
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    int run = incl - local;
+    for (int x = x0; x < x1; ++x) {
+      const int cnt = hist[x];
+      hist[x] = run;
+      run += cnt;
+    }
+#pragma unroll
+    for (int qi = 0; qi < QMAX; ++qi)
+      if (lane + 64 * qi < nb) pos[qi] += hist[key[qi]];
+  } else {
+#pragma unroll
+    for (int qi = 0; qi < QMAX; ++qi) pos[qi] = lane + 64 * qi;  // chunk order
+  }
+  // Schedule table, this step's ancestry rows, and each beam's position
+  // (read by the next step) in the unused last entry of its row.
+#pragma unroll
+  for (int qi = 0; qi < QMAX; ++qi) {
+    const int i = lane + 64 * qi;
+    if (i < nb) {
+      s_tab[pos[qi]] = u32x4{(uint32_t)i, (uint32_t)slot[qi][0], (uint32_t)slot[qi][T > 1 ? 1 : 0],
+                             (uint32_t)slot[qi][T > 2 ? 2 : 0]};
+      if constexpr (T > 3) s_slot3[pos[qi]] = slot[qi][3];
+      if (h == 0) {
+        int32_t* crow = a.anc + (((size_t)T * a.R + r) * a.Wm + b_begin + i) * a.L;
+#pragma unroll
+        for (int j = 0; j < T; ++j) crow[j] = slot[qi][j];
+        crow[a.L - 1] = sorted ? pos[qi] : b_begin + i;  // order key for the next step
+      }
+    }
+  }
+}
+
+inline int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace fused
+}  // namespace gdn

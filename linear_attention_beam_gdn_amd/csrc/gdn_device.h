@@ -15,11 +15,13 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_at(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// Round-to-nearest-even FP32 -> bf16 bits (inputs here are finite).
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two FP32 values rounded to nearest-even bf16 in one packed word (element 0
+// in the low half): gfx950's packed conversion instruction.
+__device__ __forceinline__ uint32_t bf16x2_rne(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
 }
 
 // Element e (0..7) of eight bf16 packed in a u32x4.

@@ -32,6 +32,12 @@ bool beam_fused_supported(const gdn_shape& sh, int t);
 int launch_beam_fused(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
                       hipStream_t stream);
 
+// Channel-decay beams with (d_k, d_v) in {64, 128} and chains of at most 3
+// records: the same pipeline with 8-beam tiles.
+bool beam_fused_kda_supported(const gdn_shape& sh, int t);
+int launch_beam_fused_kda(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
+                          hipStream_t stream);
+
 // One beam per request (W_max == 1): bounded-log decoding of sequences.
 int launch_seq_decode(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io,
                       hipStream_t stream);

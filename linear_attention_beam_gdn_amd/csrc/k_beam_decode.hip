@@ -343,8 +343,9 @@ int launch_beam_decode(const gdn_shape& sh, const gdn_store& st, int t, int Wt, 
                        hipStream_t stream) {
   // GDN_BEAM_GENERIC=1 forces the register-only kernel (for A/B comparisons)
   const char* generic = getenv("GDN_BEAM_GENERIC");
-  if (beam_fused_supported(sh, t) && !(generic != nullptr && generic[0] == '1'))
-    return launch_beam_fused(sh, st, t, Wt, io, stream);
+  const bool force_generic = generic != nullptr && generic[0] == '1';
+  if (beam_fused_supported(sh, t) && !force_generic) return launch_beam_fused(sh, st, t, Wt, io, stream);
+  if (beam_fused_kda_supported(sh, t) && !force_generic) return launch_beam_fused_kda(sh, st, t, Wt, io, stream);
   const bool ch = sh.decay_kind == GDN_DECAY_CHANNEL;
 #define GDN_CASE(DK_, DV_)                                                       \
   if (sh.dk == DK_ && sh.dv == DV_)                                              \

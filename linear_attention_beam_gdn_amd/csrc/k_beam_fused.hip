@@ -49,14 +49,12 @@
 // chunk 4m + l/16 of row l%16 (so every DMA lane serves one beam), and a
 // fragment read of chunk 4s + g for beam c by lane 16g + c is one contiguous
 // 1 KiB access, free of bank conflicts.
-#include "beam_common.h"
+#include "fused_common.h"
 
 namespace gdn {
 namespace {
 
-constexpr int kMaxChunkF = 512;         // beams per workgroup at most
-constexpr int kLdsBytes = 160 * 1024;   // LDS of one gfx950 compute unit
-constexpr int kSortMax = 8192;          // largest W_max whose tree order is computed
+using namespace fused;
 
 template <int DK, int DV, int T>
 struct FusedGeom {
@@ -90,71 +88,6 @@ struct FusedGeom {
   // the sort's bucket counts live in the (not yet used) tile ring
   static constexpr int SORT_CAP = NBUF * BUF / 4 < kSortMax ? NBUF * BUF / 4 : kSortMax;
 };
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
-}
-
-// 64 lanes x 16 (or 4) bytes from per-lane global addresses into the LDS
-// block at `blk` (wave-uniform), lane l at blk + l * size.
-__device__ __forceinline__ void dma16(const void* src, uint8_t* blk) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)blk, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* src, uint8_t* blk) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)blk, 4, 0, 0);
-}
-
-// Wait until at most N vector-memory operations of this wave are in flight.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N < 63 ? N : 63) : "memory");
-}
-
-// Wait until at most k tiles of OPT loads each (k <= KMAX) are in flight.
-template <int OPT, int KMAX>
-__device__ __forceinline__ void wait_tiles(int k) {
-  if constexpr (KMAX >= 4)
-    if (k >= 4) return wait_vm<4 * OPT>();
-  if constexpr (KMAX >= 3)
-    if (k == 3) return wait_vm<3 * OPT>();
-  if constexpr (KMAX >= 2)
-    if (k == 2) return wait_vm<2 * OPT>();
-  if constexpr (KMAX >= 1)
-    if (k == 1) return wait_vm<OPT>();
-  wait_vm<0>();
-}
-
-// Workgroup barrier after this wave's LDS accesses have completed; also a
-// compiler barrier for memory accesses.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// LDS read issued as opaque assembly: the compiler does not order it behind
-// this wave's outstanding LDS-DMA loads (which target other LDS bytes).
-__device__ __forceinline__ int lds_read_opaque(const void* p) {
-  int v;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
-  return v;
-}
-__device__ __forceinline__ u32x4 lds_read128_opaque(const void* p) {
-  u32x4 v;
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
-  return v;
-}
-
-// Raw buffer resource (gfx9 layout) over `bytes` bytes at `base`: stores at
-// offsets past the end are dropped by the hardware, which lets every lane
-// issue the same stores whatever its beam.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_window(void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
-}
-constexpr int kOutside = 0x7FFFFFF0;  // an offset past every store window
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
 
 template <int DK, int DV, int T>
 __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamArgs a) {
@@ -193,78 +126,8 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     // ============================================================ DMA waves
     const int dw = w - G::WDMA;  // this wave owns tiles p with p % 2 == dw
     const int cg = lane >> 4;
-    if (T > 0 && dw == 0) {
-      // Ancestry (§3.3): h_t(b, T-1) = parent, h_t(b, j) = h_{T-1}(parent, j).
-      // All parent pointers first, then all parent rows, with every load
-      // unconditional (indices past the chunk repeat its last beam) so that
-      // each batch is one round trip.
-      constexpr int QMAX = kMaxChunkF / 64;
-      int slot[QMAX][TT], key[QMAX], pos[QMAX];
-#pragma unroll
-      for (int qi = 0; qi < QMAX; ++qi) {
-        const int i = min(lane + 64 * qi, nb - 1);
-        slot[qi][TT - 1] = clampi(a.parent[(size_t)r * a.Wt + b_begin + i], 0, a.Wm - 1);
-      }
-#pragma unroll
-      for (int qi = 0; qi < QMAX; ++qi) {
-        const int32_t* prow = a.anc + (((size_t)(TT - 1) * a.R + r) * a.Wm + slot[qi][TT - 1]) * a.L;
-#pragma unroll
-        for (int j = 0; j < T - 1; ++j) slot[qi][j] = clampi(prow[j], 0, a.Wm - 1);
-        // the parent's position in the previous step's order (its own slot
-        // when the previous step is the first)
-        key[qi] = T > 1 ? clampi(prow[a.L - 1], 0, a.Wm - 1) : slot[qi][TT - 1];
-      }
-      if (a.nchunk == 1 && a.Wm <= G::SORT_CAP) {
-        // stable-enough counting sort by key (ties in any order): bucket
-        // counts with LDS atomics, an exclusive scan over the buckets, then
-        // each beam's position = bucket start + its rank in the bucket.  One
-        // wave: its LDS accesses complete in program order.
-        int* hist = reinterpret_cast<int*>(smem);  // scratch in the tile ring, not yet in use
-        for (int x = lane; x < a.Wm; x += 64) hist[x] = 0;
-#pragma unroll
-        for (int qi = 0; qi < QMAX; ++qi)
-          if (lane + 64 * qi < nb) pos[qi] = atomicAdd(&hist[key[qi]], 1);
-        const int per = (a.Wm + 63) / 64;
-        const int x0 = min(lane * per, a.Wm), x1 = min(x0 + per, a.Wm);
-        int local = 0;
-        for (int x = x0; x < x1; ++x) local += hist[x];
-        int incl = local;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int y = __shfl_up(incl, d);
-          if (lane >= d) incl += y;
-        }
-        int run = incl - local;
-        for (int x = x0; x < x1; ++x) {
-          const int cnt = hist[x];
-          hist[x] = run;
-          run += cnt;
-        }
-#pragma unroll
-        for (int qi = 0; qi < QMAX; ++qi)
-          if (lane + 64 * qi < nb) pos[qi] += hist[key[qi]];
-      } else {
-#pragma unroll
-        for (int qi = 0; qi < QMAX; ++qi) pos[qi] = lane + 64 * qi;
-      }
-      // Schedule table, this step's ancestry rows, and each beam's position
-      // (read by the next step) in the unused last entry of its row.
-#pragma unroll
-      for (int qi = 0; qi < QMAX; ++qi) {
-        const int i = lane + 64 * qi;
-        if (i < nb) {
-          s_tab[pos[qi]] = u32x4{(uint32_t)i, (uint32_t)slot[qi][0], (uint32_t)slot[qi][T > 1 ? 1 : 0],
-                                 (uint32_t)slot[qi][T > 2 ? 2 : 0]};
-          if constexpr (T > 3) s_slot3[pos[qi]] = slot[qi][3];
-          if (h == 0) {
-            int32_t* crow = a.anc + (((size_t)T * a.R + r) * a.Wm + b_begin + i) * a.L;
-#pragma unroll
-            for (int j = 0; j < T; ++j) crow[j] = slot[qi][j];
-            crow[a.L - 1] = pos[qi];
-          }
-        }
-      }
-    }
+    if (T > 0 && dw == 0)
+      build_schedule<T>(a, r, h, b_begin, nb, lane, G::SORT_CAP, smem, s_tab, s_slot3);
 
     auto dma_tile = [&](int p) {
       uint8_t* buf = smem + (p % G::NBUF) * G::BUF;
@@ -483,32 +346,22 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     // output and append (§3.4): every wave issues the same four stores; a
     // position past the chunk stores outside the windows
     const int posi = it * 16 + c;
-    const int ib = posi >= nb ? kOutside / so : (T > 0 ? (int)s_tab[posi][0] : posi);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, ib * so + row0 * 4, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, ib * so + row0 * 4, 0, 0);
+    const bool live = posi < nb;
+    const int ib = live ? (T > 0 ? (int)s_tab[posi][0] : posi) : 0;
+    const int off_o = live ? ib * so + row0 * 4 : kOutside;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, off_o, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, off_o, 0, 0);
     u32x4 kk = kf[0];
 #pragma unroll
     for (int s = 1; s < KS; ++s)
       if (ks == s) kk = kf[s];
     __builtin_amdgcn_raw_buffer_store_b64(kh ? u32x2{kk[2], kk[3]} : u32x2{kk[0], kk[1]}, w_k,
-                                          ib * sk + (ks * 32 + g * 8 + kh * 4) * 2, 0, 0);
+                                          live ? ib * sk + (ks * 32 + g * 8 + kh * 4) * 2 : kOutside, 0, 0);
     const float at = *reinterpret_cast<const float*>(buf + G::OS + c * 4);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(at), w_a,
-                                          (w == G::NC - 1 && g == 0) ? ib * sa : kOutside, 0, 0);
+                                          (live && w == G::NC - 1 && g == 0) ? ib * sa : kOutside, 0, 0);
     lds_barrier();  // it + 1
   }
-}
-
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
 }
 
 template <int DK, int DV, int T>

@@ -1,0 +1,495 @@
+// Fused shared-context decode step for beams with per-channel decay: the KDA
+// row of DeltaLog Table 1 (transform D(a_t) S_{t-1}, update pair
+// (k_t, beta_t (v_t - (D(a_t) S_{t-1})^T k_t)), diagonal decay), decoded with
+// OneLA's shared context state, transition records and ancestry index (§3.2,
+// §3.3, §3.4) on LDS-DMA staged tiles like the scalar-decay kernel.
+//
+// Replay with channel decay.  With Q_j = a_j * a_{j+1} * ... * a_t taken
+// channel by channel (Q_{t+1} = 1), the two projections a step needs are
+//   u_x = S0^T (Q_0 * x) + sum_{j<t} delta_j (k_j . (Q_{j+1} * x)),  x in {q_t, k_t},
+// then delta_t = beta_t (v_t - u_k) and o_t = u_q + delta_t (k_t . q_t).  The
+// decay acts on the d_k side, so it lives in the probes: the S0 contraction
+// takes the FP32 probes Q_0 * q and Q_0 * k, split into two bf16 planes.
+//
+// Work split.  A workgroup takes one (request r, head h) and a chunk of its
+// beams, 8 beams per tile.  The 16 columns of the gfx950 16x16x32 bf16 MFMA
+// carry the q-probes (columns 0-7) and the k-probes (columns 8-15) of the
+// same 8 beams, so one MFMA forms both projections.
+// * Two DMA waves (alternate tiles) build the ancestry-ordered schedule and
+//   stream each tile's q|k rows, v, alpha_t, beta_t and, per beam, the keys
+//   and decay vectors of its T ancestral records into a ring of LDS buffers
+//   with LDS-DMA loads and counted waits.
+// * The d_v / 16 consumer waves each hold 16 value rows of S0[r, h] as two
+//   bf16 planes in registers.  Between two barriers a consumer wave
+//   - prepares its share of the next tile (8 / (d_v / 16) beams): each half
+//     wave takes the q or the k row of a beam, walks the chain from the
+//     current step down (y = a_t * x; weight_j = k_j . y; y = a_j * y), and
+//     writes the probe Q_0 * x as hi and lo bf16 planes over the raw row, the
+//     record weights and k_t . q_t; it also appends the beam's key row and
+//     decay vector to the record store;
+//   - then finishes the current tile: hi*hi + hi*lo + lo*hi plane products
+//     on the matrix cores, the q- and k-halves of the result exchanged with
+//     a DPP row rotation, the replay with the ancestral update vectors
+//     (loaded into registers one tile ahead), and the stores of o_t (q-half
+//     lanes) and delta_t (k-half lanes).
+//
+// LDS layouts: the 16-row q|k arrays use the beam-fastest layout of the
+// scalar kernel (chunk ch of row b at slot (ch/4)*64 + (ch%4)*16 + b); the
+// 8-row arrays keep chunk ch of beam b at slot (ch/8)*64 + (ch%8)*8 + b, so
+// DMA instruction m fills slots m*64 .. m*64+63 with lane l loading chunk
+// 8m + l/8 of beam l%8.  Both put beam b's data in the slots congruent to b
+// mod 8, which lets a wave write a beam's probe planes over that beam's raw
+// q|k rows and decay vector.
+#include "fused_common.h"
+
+namespace gdn {
+namespace {
+
+using namespace fused;
+
+template <int DK, int DV, int T>
+struct KdaGeom {
+  static_assert(DK % 64 == 0 && DV % 64 == 0, "the channel-decay kernel needs d_k, d_v multiples of 64");
+  static constexpr int TB = 8;             // beams per tile
+  static constexpr int NC = DV / 16;       // consumer waves, 16 value rows each
+  static_assert(TB % NC == 0, "each consumer wave prepares whole beams");
+  static constexpr int BPW = TB / NC;      // beams a consumer wave prepares per tile
+  static constexpr int EPL = DK / 32;      // channels per lane in the preparation
+  static constexpr int WDMA = NC;          // first DMA wave
+  static constexpr int NDMA = 2;
+  static constexpr int NT = (NC + NDMA) * 64;
+  static constexpr int KS = DK / 32;
+  static constexpr int QKB = 16 * DK * 2;  // q|k rows; then the probes' hi plane
+  // alpha_t of the 8 beams; then the probes' lo plane.  The 8-row slots of
+  // beam b are exactly the 16-row slots of rows b and b + 8, so the wave that
+  // prepares beam b overwrites only what it has already read.
+  static constexpr int VB = TB * DV * 2;
+  static constexpr int AB = TB * DK * 4;
+  static constexpr int SMB = 256;          // beta_t
+  static constexpr int NWT = (2 + 2 * T + 3) / 4 * 4;  // beta, k.q, T q-weights, T k-weights
+  static constexpr int WTB = TB * NWT * 4;
+  static constexpr int RKB = TB * DK * 2;  // keys of one record depth
+  static_assert(AB == QKB, "the lo plane of a tile takes the place of its decay vectors");
+  static constexpr int OQK = 0, OV = QKB, OA = OV + VB, OLO = OA, OS = OA + AB, OW = OS + SMB, ORK = OW + WTB,
+                       ORA = ORK + T * RKB;
+  static constexpr int BUF = ORA + T * AB;
+  static constexpr int SLOTB = T > 0 ? kMaxChunkF * 16 + (T > 3 ? kMaxChunkF * 4 : 0) : 0;
+  static constexpr int NBUF0 = (kLdsBytes - SLOTB) / BUF;
+  static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
+  static_assert(NBUF >= 3, "tile buffers do not fit in LDS");
+  static constexpr int LDS = NBUF * BUF + SLOTB;
+  static constexpr int SORT_CAP = NBUF * BUF / 4 < kSortMax ? NBUF * BUF / 4 : kSortMax;
+  // LDS-DMA instructions per tile (q|k, v, alpha_t, beta_t, then per record k_j, a_j)
+  static constexpr int OPT = QKB / 1024 + VB / 1024 + AB / 1024 + 1 + T * (RKB / 1024 + AB / 1024);
+  static_assert(QKB % 1024 == 0 && VB % 1024 == 0 && AB % 1024 == 0 && RKB % 1024 == 0,
+                "tile arrays must be whole DMA blocks");
+};
+
+// 16-byte slot of chunk ch of row b in the 16-row and the 8-row layouts
+__device__ __forceinline__ int slot16(int b, int ch) { return (ch >> 2) * 64 + (ch & 3) * 16 + b; }
+__device__ __forceinline__ int slot8(int b, int ch) { return (ch >> 3) * 64 + (ch & 7) * 8 + b; }
+
+// value of lane l^8 within each 16-lane row (DPP row_ror:8)
+__device__ __forceinline__ float swap8(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
+// Sum over each 32-lane half of a wave64: quad swaps and row rotations by
+// DPP within the 16-lane rows, then the row pair (0, 1) or (2, 3) with the
+// gfx950 row-swap instruction.  Lane 0 of a half always forms the same sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum_half(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp<0x124>(x);  // row_ror:4
+  x += dpp<0x128>(x);  // row_ror:8
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+// EPL consecutive bf16 (EPL = 2 or 4) as packed words, and EPL floats
+template <int EPL>
+__device__ __forceinline__ void lds_bf16(const uint8_t* p, uint32_t* w) {
+  if constexpr (EPL == 4) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    w[0] = v[0];
+    w[1] = v[1];
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+template <int EPL>
+__device__ __forceinline__ void lds_f32(const uint8_t* p, float* x) {
+  if constexpr (EPL == 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = v[e];
+  } else {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    x[0] = v.x;
+    x[1] = v.y;
+  }
+}
+template <int EPL>
+__device__ __forceinline__ void lds_put(uint8_t* p, const uint32_t* w) {
+  if constexpr (EPL == 4)
+    *reinterpret_cast<u32x2*>(p) = u32x2{w[0], w[1]};
+  else
+    *reinterpret_cast<uint32_t*>(p) = w[0];
+}
+
+template <int DK, int DV, int T>
+__global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(BeamArgs a) {
+  using G = KdaGeom<DK, DV, T>;
+  constexpr int KS = G::KS;
+  constexpr int EPL = G::EPL;
+  constexpr int TT = T > 0 ? T : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
+  u32x4* s_tab = reinterpret_cast<u32x4*>(smem + G::NBUF * G::BUF);
+  int* s_slot3 = reinterpret_cast<int*>(smem + G::NBUF * G::BUF + kMaxChunkF * 16);
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int chunk_id = bid % a.nchunk;
+  const int rh = bid / a.nchunk;
+  const int h = rh % a.H;
+  const int r = rh / a.H;
+  const int b_begin = chunk_id * a.chunk;
+  const int b_end = min(b_begin + a.chunk, a.Wt);
+  const int nb = b_end - b_begin;
+  const int ntiles = (nb + G::TB - 1) / G::TB;
+
+  // Barriers: P (schedule table written), A (tile 0 resident), then
+  // 0 .. ntiles.  Between barrier i and i + 1 the consumers finish tile i and
+  // prepare tile i + 1, and a DMA wave refills the buffer of tile i - 1.
+
+  if (w >= G::WDMA) {
+    // ============================================================ DMA waves
+    const int dw = w - G::WDMA;
+    if (T > 0 && dw == 0) build_schedule<T>(a, r, h, b_begin, nb, lane, G::SORT_CAP, smem, s_tab, s_slot3);
+
+    auto dma_tile = [&](int p) {
+      uint8_t* buf = smem + (p % G::NBUF) * G::BUF;
+      const int posi = min(p * G::TB + (lane & 7), nb - 1);  // positions past the chunk repeat its last
+      int ib = posi, sl[4] = {0, 0, 0, 0};
+      if constexpr (T > 0) {
+        const u32x4 e = lds_read128_opaque(&s_tab[posi]);
+        ib = (int)e[0];
+        sl[0] = (int)e[1];
+        sl[1] = (int)e[2];
+        sl[2] = (int)e[3];
+        if constexpr (T > 3) sl[3] = lds_read_opaque(&s_slot3[posi]);
+      }
+      const size_t tok = ((size_t)r * a.Wt + b_begin + ib) * a.H + h;
+      // q|k: rows 0-7 the q rows, rows 8-15 the k rows of the tile's beams
+      const uint16_t* qkrow = ((lane & 8) ? a.k : a.q) + tok * DK;
+#pragma unroll
+      for (int m = 0; m < G::QKB / 1024; ++m) dma16(qkrow + (m * 4 + (lane >> 4)) * 8, buf + G::OQK + m * 1024);
+#pragma unroll
+      for (int m = 0; m < G::VB / 1024; ++m) dma16(a.v + tok * DV + (m * 8 + (lane >> 3)) * 8, buf + G::OV + m * 1024);
+#pragma unroll
+      for (int m = 0; m < G::AB / 1024; ++m)
+        dma16(a.alpha + tok * DK + (m * 8 + (lane >> 3)) * 4, buf + G::OA + m * 1024);
+      dma4(a.beta + tok, buf + G::OS);
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const size_t rj = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + h;
+#pragma unroll
+        for (int m = 0; m < G::RKB / 1024; ++m)
+          dma16(a.rec_k + rj * DK + (m * 8 + (lane >> 3)) * 8, buf + G::ORK + j * G::RKB + m * 1024);
+#pragma unroll
+        for (int m = 0; m < G::AB / 1024; ++m)
+          dma16(a.rec_alpha + rj * DK + (m * 8 + (lane >> 3)) * 4, buf + G::ORA + j * G::AB + m * 1024);
+      }
+    };
+
+    auto later = [&](int q, int last) { return last > q ? (last - q) / 2 : 0; };
+    lds_barrier();  // P
+    const int npro = min(G::NBUF - 1, ntiles);
+    for (int p = dw; p < npro; p += 2) dma_tile(p);
+    if (dw == 0) wait_tiles<G::OPT, 2>(later(0, npro - 1));  // tile 0 resident
+    lds_barrier();                                          // A
+    if (dw == 1) wait_tiles<G::OPT, 2>(later(1, npro - 1));  // tile 1 resident
+    lds_barrier();                                          // 0
+    for (int i = 0; i < ntiles; ++i) {
+      const int p = i + G::NBUF - 1;  // into the buffer released at the last barrier
+      if (p < ntiles && (p & 1) == dw) dma_tile(p);
+      const int last = min(p, ntiles - 1);
+      if (i + 2 < ntiles && ((i + 2) & 1) == dw) wait_tiles<G::OPT, 2>(later(i + 2, last));  // tile i + 2 resident
+      lds_barrier();                                                                     // i + 1
+    }
+    return;
+  }
+
+  // ============================================================ consumers
+  // record-store windows over the chunk's beams (appends at step T)
+  const size_t rec0 = (((size_t)T * a.R + r) * a.Wm + b_begin) * a.H + h;
+  const int sk = a.H * DK * 2, sa = a.H * DK * 4;  // bytes between beams
+  const __amdgpu_buffer_rsrc_t w_k = store_window(a.rec_k + rec0 * DK, (nb - 1) * sk + DK * 2);
+  const __amdgpu_buffer_rsrc_t w_a = store_window(a.rec_alpha + rec0 * DK, (nb - 1) * sa + DK * 4);
+
+  // Preparation of beams w * BPW .. w * BPW + BPW - 1 of tile p.  Lane
+  // (side, el): channels EPL * el .. EPL * el + EPL - 1 of the q row
+  // (side 0) or the k row (side 1).
+  const int ps = lane >> 5;
+  const int el = lane & 31;
+  const int e0 = el * EPL;
+  const int oqk = slot16(0, e0 >> 3) * 16 + (e0 & 7) * 2;  // row 0; row b adds 16 b
+  const int o8h = slot8(0, e0 >> 3) * 16 + (e0 & 7) * 2;   // bf16 8-row arrays; beam b adds 16 b
+  const int o8f = slot8(0, e0 >> 2) * 16 + (e0 & 3) * 4;   // f32 8-row arrays
+  auto prep = [&](int p) {
+    uint8_t* buf = smem + (p % G::NBUF) * G::BUF;
+#pragma unroll
+    for (int u = 0; u < G::BPW; ++u) {
+      const int pb = w * G::BPW + u;
+      uint32_t xw[EPL / 2], kw[EPL / 2];
+      float at[EPL], y[EPL];
+      lds_bf16<EPL>(buf + G::OQK + oqk + (pb + 8 * ps) * 16, xw);
+      lds_bf16<EPL>(buf + G::OQK + oqk + (pb + 8) * 16, kw);
+      lds_f32<EPL>(buf + G::OA + o8f + pb * 16, at);
+      const float beta = reinterpret_cast<const float*>(buf + G::OS)[pb];
+      float sqq = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float xe = (e & 1) ? bf16_hi(xw[e >> 1]) : bf16_lo(xw[e >> 1]);
+        const float ke = (e & 1) ? bf16_hi(kw[e >> 1]) : bf16_lo(kw[e >> 1]);
+        y[e] = at[e] * xe;
+        sqq += ke * xe;
+      }
+      // walk the chain from the current step down: weight_j = k_j . (Q_{j+1} x)
+      float wj[TT];
+#pragma unroll
+      for (int j = T - 1; j >= 0; --j) {
+        uint32_t kj[EPL / 2];
+        float aj[EPL];
+        lds_bf16<EPL>(buf + G::ORK + j * G::RKB + o8h + pb * 16, kj);
+        lds_f32<EPL>(buf + G::ORA + j * G::AB + o8f + pb * 16, aj);
+        float pj = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          pj += ((e & 1) ? bf16_hi(kj[e >> 1]) : bf16_lo(kj[e >> 1])) * y[e];
+          y[e] *= aj[e];
+        }
+        wj[j] = pj;
+      }
+      // appends of step T: the key row (side 1) and the decay vector (side 0)
+      const int posi = p * G::TB + pb;
+      const bool live = posi < nb;
+      const int ib = T > 0 ? (int)s_tab[min(posi, nb - 1)][0] : posi;  // read unconditionally: no branch
+      if constexpr (EPL == 4) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{kw[0], kw[1]}, w_k, live && ps ? ib * sk + e0 * 2 : kOutside,
+                                              0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{at[0], at[1], at[2], at[3]}), w_a,
+                                               live && !ps ? ib * sa + e0 * 4 : kOutside, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b32(kw[0], w_k, live && ps ? ib * sk + e0 * 2 : kOutside, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(at[0]), __float_as_uint(at[1])}, w_a,
+                                              live && !ps ? ib * sa + e0 * 4 : kOutside, 0, 0);
+      }
+      // probe Q_0 x as hi + lo bf16 planes, over the raw row and this beam's alpha_t
+      uint32_t hw[EPL / 2], lw[EPL / 2];
+#pragma unroll
+      for (int e = 0; e < EPL; e += 2) {
+        hw[e >> 1] = bf16x2_rne(y[e], y[e + 1]);
+        lw[e >> 1] = bf16x2_rne(y[e] - bf16_lo(hw[e >> 1]), y[e + 1] - bf16_hi(hw[e >> 1]));
+      }
+      lds_put<EPL>(buf + G::OQK + oqk + (pb + 8 * ps) * 16, hw);
+      lds_put<EPL>(buf + G::OLO + oqk + (pb + 8 * ps) * 16, lw);
+      // weights: beta, k.q, q-weights (side 0 sums), k-weights (side 1 sums)
+      sqq = sum_half(sqq);
+#pragma unroll
+      for (int j = 0; j < T; ++j) wj[j] = sum_half(wj[j]);
+      // one store for the wave, no branch: lane 0 beta, lane 1 k.q, lanes
+      // 2 + j and 32 + j the q- and k-weights of record j; every other lane
+      // writes beta again to entry 0
+      int wi = 0;
+      float wv = beta;
+      if (lane == 1) wv = sqq;
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        if (lane == 2 + j) wv = wj[j];
+        if (lane == 32 + j) wv = wj[j];
+      }
+      if (lane >= 1 && lane < 2 + T) wi = lane;
+      if (lane >= 32 && lane < 32 + T) wi = lane - 30 + T;
+      reinterpret_cast<float*>(buf + G::OW)[pb * G::NWT + wi] = wv;
+    }
+  };
+
+  // Slice of S0[r, h] as hi + lo bf16 planes in the MFMA A layout: lane
+  // (g, c) holds key channels 32s + 8g .. +7 of value row 16w + c, so C row
+  // 4g + i is value row 16w + 4g + i.
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const int bb = c & 7;     // beam of this lane within the tile
+  const int side = c >> 3;  // 0: q column, 1: k column
+  u32x4 As[KS][2];
+  {
+    const float* S = a.S + ((size_t)r * a.H + h) * DK * DV;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = S[(size_t)(s * 32 + g * 8 + e) * DV + w * 16 + c];
+      split_planes<2>(x, As[s]);
+    }
+  }
+  const int row0 = w * 16 + 4 * g;
+  const int so = a.H * DV * 4;
+  const size_t tok0 = ((size_t)r * a.Wt + b_begin) * a.H + h;
+  const __amdgpu_buffer_rsrc_t w_o = store_window(a.o + tok0 * DV, (nb - 1) * so + DV * 4);
+  const __amdgpu_buffer_rsrc_t w_d = store_window(a.rec_delta + rec0 * DV, (nb - 1) * so + DV * 4);
+
+  auto load_deltas = [&](int p, f32x4* d) {
+    if constexpr (T > 0) {
+      const int posi = min(p * G::TB + bb, nb - 1);
+      const u32x4 e = s_tab[posi];
+      const int sl[4] = {(int)e[1], (int)e[2], (int)e[3], T > 3 ? s_slot3[posi] : 0};
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const size_t rj = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + h;
+        d[j] = *reinterpret_cast<const f32x4*>(a.rec_delta + rj * DV + row0);
+      }
+    }
+  };
+
+  lds_barrier();  // P
+  f32x4 dnext[TT];
+  load_deltas(0, dnext);
+  lds_barrier();  // A
+  prep(0);
+  lds_barrier();  // 0
+
+  for (int it = 0; it < ntiles; ++it) {
+    f32x4 dcur[TT];
+#pragma unroll
+    for (int j = 0; j < T; ++j) dcur[j] = dnext[j];
+    // Next tile, unconditionally so that it shares a basic block with this
+    // tile's work.  Past the last tile it reads a free buffer (no load of
+    // this launch targets it any more), writes only there, and its appends
+    // fall outside the store windows.
+    load_deltas(it + 1, dnext);
+    prep(it + 1);
+
+    const uint8_t* buf = smem + (it % G::NBUF) * G::BUF;
+    u32x4 bh[KS], bl[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      bh[s] = *reinterpret_cast<const u32x4*>(buf + G::OQK + slot16(c, s * 4 + g) * 16);
+      bl[s] = *reinterpret_cast<const u32x4*>(buf + G::OLO + slot16(c, s * 4 + g) * 16);
+    }
+    const int vch = w * 2 + (g >> 1);  // 16-byte v chunk holding rows row0 .. row0 + 3
+    const u32x2 vw = *reinterpret_cast<const u32x2*>(buf + G::OV + slot8(bb, vch) * 16 + (g & 1) * 8);
+    float wt[G::NWT];
+#pragma unroll
+    for (int v = 0; v < G::NWT; v += 4) {
+      const f32x4 q4 = *reinterpret_cast<const f32x4*>(buf + G::OW + (bb * G::NWT + v) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wt[v + e] = q4[e];
+    }
+
+    // S0^T [Q_0 q | Q_0 k] for the tile's 8 beams: hi*hi + hi*lo + lo*hi
+    f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u = mfma16x16x32(As[s][1], bh[s], u);
+      u = mfma16x16x32(As[s][0], bl[s], u);
+      u = mfma16x16x32(As[s][0], bh[s], u);
+    }
+    f32x4 uq, uk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float other = swap8(u[i]);
+      uq[i] = side ? other : u[i];
+      uk[i] = side ? u[i] : other;
+    }
+    f32x4 xq = uq, xk = uk;
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      xq += wt[2 + j] * dcur[j];
+      xk += wt[2 + T + j] * dcur[j];
+    }
+    f32x4 dt, ot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t word = vw[i >> 1];
+      const float vv = (i & 1) ? bf16_hi(word) : bf16_lo(word);
+      dt[i] = wt[0] * (vv - xk[i]);
+      ot[i] = xq[i] + dt[i] * wt[1];
+    }
+
+    // output (q-column lanes) and the appended update vector (k-column lanes)
+    const int posi = it * G::TB + bb;
+    const bool live = posi < nb;
+    const int ib = T > 0 ? (int)s_tab[min(posi, nb - 1)][0] : posi;
+    const int off = live ? ib * so + row0 * 4 : kOutside;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, side ? kOutside : off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, side ? off : kOutside, 0, 0);
+    lds_barrier();  // it + 1
+  }
+}
+
+template <int DK, int DV, int T>
+int launch(const gdn_shape& sh, const gdn_store& st, int Wt, const StepIO& io, hipStream_t stream) {
+  using G = KdaGeom<DK, DV, T>;
+  BeamArgs a;
+  a.S = st.S;
+  a.rec_delta = st.rec_delta;
+  a.rec_k = st.rec_k;
+  a.rec_alpha = st.rec_alpha;
+  a.anc = st.anc;
+  a.parent = io.parent;
+  a.q = io.q;
+  a.k = io.k;
+  a.v = io.v;
+  a.alpha = io.alpha;
+  a.beta = io.beta;
+  a.o = io.o;
+  a.R = sh.R;
+  a.Wm = sh.W_max;
+  a.H = sh.H;
+  a.L = sh.L_max;
+  a.t = T;
+  a.Wt = Wt;
+  // one workgroup per compute unit: the tile ring takes most of its LDS
+  a.chunk = pick_chunk(sh.R * sh.H, Wt, kMaxChunkF, cu_count());
+  a.nchunk = (Wt + a.chunk - 1) / a.chunk;
+  const long grid = (long)sh.R * sh.H * a.nchunk;
+  if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
+  hipLaunchKernelGGL((k_beam_fused_kda<DK, DV, T>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+template <int DK, int DV>
+int launch_dims(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io, hipStream_t stream) {
+  switch (t) {
+    case 0: return launch<DK, DV, 0>(sh, st, Wt, io, stream);
+    case 1: return launch<DK, DV, 1>(sh, st, Wt, io, stream);
+    case 2: return launch<DK, DV, 2>(sh, st, Wt, io, stream);
+    case 3: return launch<DK, DV, 3>(sh, st, Wt, io, stream);
+    default: return GDN_EUNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+bool beam_fused_kda_supported(const gdn_shape& sh, int t) {
+  return sh.decay_kind == GDN_DECAY_CHANNEL && t >= 0 && t <= 3 &&
+         ((sh.dk == 64 && sh.dv == 64) || (sh.dk == 128 && sh.dv == 128));
+}
+
+int launch_beam_fused_kda(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
+                          hipStream_t stream) {
+  if (sh.dk == 64 && sh.dv == 64) return launch_dims<64, 64>(sh, st, t, Wt, io, stream);
+  if (sh.dk == 128 && sh.dv == 128) return launch_dims<128, 128>(sh, st, t, Wt, io, stream);
+  return GDN_EUNSUPPORTED;
+}
+
+}  // namespace gdn
