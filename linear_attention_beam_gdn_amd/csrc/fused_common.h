@@ -81,44 +81,79 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // wave).  Builds the chunk's ancestry (OneLA §3.3: h_t(b, T-1) = parent,
 // h_t(b, j) = h_{T-1}(parent, j)), orders the beams depth-first in the beam
 // tree when the chunk holds the whole step (a counting sort of the beams by
-// their parent's position in the previous step's order, with the bucket
-// counts in `scratch`), and writes
+// their parent's position in the previous step's order), and writes
 //   s_tab[position]  = {beam, slot_0, slot_1, slot_2}, s_slot3[position] = slot_3,
 //   anc row T of every beam (h == 0 workgroups), with the beam's position in
 //   the unused last entry for the next step.
 // The order only decides which lanes compute a beam, never its result.
-template <int T>
+//
+// Memory: the parent pointers and, for T >= 2, the whole previous-step
+// ancestry block of the request (W_max x L_max entries, staged into LDS by
+// LDS DMA when it fits in `scratch`) are fetched in one batch; `mid()` runs
+// once they have arrived (the caller's workgroup barrier), and the sort
+// follows.  `scratch` (scratch_bytes, 16-byte aligned) holds the bucket
+// counts and the staged block and is free for other use afterwards.
+template <int T, class Mid>
 __device__ __forceinline__ void build_schedule(const BeamArgs& a, int r, int h, int b_begin, int nb, int lane,
-                                               int sort_cap, uint8_t* scratch, u32x4* s_tab, int* s_slot3) {
+                                               int scratch_bytes, uint8_t* scratch, u32x4* s_tab, int* s_slot3,
+                                               Mid mid) {
   constexpr int TT = T > 0 ? T : 1;
-  uint8_t* smem = scratch;
-  // Ancestry (§3.3): h_t(b, T-1) = parent, h_t(b, j) = h_{T-1}(parent, j).
-  // All parent pointers first, then all parent rows, with every load
-  // unconditional (indices past the chunk repeat its last beam) so that
-  // each batch is one round trip.
   constexpr int QMAX = kMaxChunkF / 64;
+  const int hist_words = (a.Wm + 63) & ~63;
+  const bool sorted = a.nchunk == 1 && a.Wm <= kSortMax && hist_words * 4 <= scratch_bytes;
+  const int blk_words = a.Wm * a.L;
+  const bool staged = T > 1 && hist_words * 4 + ((blk_words + 63) & ~63) * 4 <= scratch_bytes;
+  int* hist = reinterpret_cast<int*>(scratch);
+  int* rows = reinterpret_cast<int*>(scratch) + hist_words;  // staged ancestry block
+  const int32_t* blk = a.anc + ((size_t)(TT - 1) * a.R + r) * a.Wm * a.L;
+
+  // One batch: every parent pointer (indices past the chunk repeat its last
+  // beam, so every load is unconditional) and the staged block.
   int slot[QMAX][TT], key[QMAX], pos[QMAX];
 #pragma unroll
   for (int qi = 0; qi < QMAX; ++qi) {
     const int i = min(lane + 64 * qi, nb - 1);
-    slot[qi][TT - 1] = clampi(a.parent[(size_t)r * a.Wt + b_begin + i], 0, a.Wm - 1);
+    slot[qi][TT - 1] = a.parent[(size_t)r * a.Wt + b_begin + i];
   }
+  if (staged)
+    for (int x = 0; x < blk_words; x += 64)  // lane l of each block fills word x + l
+      dma4(blk + min(x + lane, blk_words - 1), reinterpret_cast<uint8_t*>(rows + x));
+  wait_vm<0>();
+  mid();
 #pragma unroll
-  for (int qi = 0; qi < QMAX; ++qi) {
-    const int32_t* prow = a.anc + (((size_t)(TT - 1) * a.R + r) * a.Wm + slot[qi][TT - 1]) * a.L;
+  for (int qi = 0; qi < QMAX; ++qi) slot[qi][TT - 1] = clampi(slot[qi][TT - 1], 0, a.Wm - 1);
+  // Ancestry (§3.3): h_t(b, T-1) = parent, h_t(b, j) = h_{T-1}(parent, j);
+  // the parent's position in the previous step's order is the sort key (its
+  // own slot when the previous step is the first).
+  // (two separate paths, so that the staged rows are read as LDS, not
+  // through generic pointers)
+  if constexpr (T > 1) {
+    if (staged) {
 #pragma unroll
-    for (int j = 0; j < T - 1; ++j) slot[qi][j] = clampi(prow[j], 0, a.Wm - 1);
-    // the parent's position in the previous step's order (its own slot
-    // when the previous step is the first)
-    key[qi] = T > 1 ? clampi(prow[a.L - 1], 0, a.Wm - 1) : slot[qi][TT - 1];
+      for (int qi = 0; qi < QMAX; ++qi) {
+        const int* prow = rows + slot[qi][TT - 1] * a.L;
+#pragma unroll
+        for (int j = 0; j < T - 1; ++j) slot[qi][j] = clampi(prow[j], 0, a.Wm - 1);
+        key[qi] = clampi(prow[a.L - 1], 0, a.Wm - 1);
+      }
+    } else {
+#pragma unroll
+      for (int qi = 0; qi < QMAX; ++qi) {
+        const int32_t* prow = blk + (size_t)slot[qi][TT - 1] * a.L;
+#pragma unroll
+        for (int j = 0; j < T - 1; ++j) slot[qi][j] = clampi(prow[j], 0, a.Wm - 1);
+        key[qi] = clampi(prow[a.L - 1], 0, a.Wm - 1);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int qi = 0; qi < QMAX; ++qi) key[qi] = slot[qi][TT - 1];
   }
-  const bool sorted = a.nchunk == 1 && a.Wm <= sort_cap;
   if (sorted) {
-    // stable-enough counting sort by key (ties in any order): bucket
-    // counts with LDS atomics, an exclusive scan over the buckets, then
-    // each beam's position = bucket start + its rank in the bucket.  One
-    // wave: its LDS accesses complete in program order.
-    int* hist = reinterpret_cast<int*>(smem);  // scratch in the tile ring, not yet in use
+    // counting sort by key (ties in any order): bucket counts with LDS
+    // atomics, an exclusive scan over the buckets, then each beam's position
+    // = bucket start + its rank in the bucket.  One wave: its LDS accesses
+    // complete in program order.
     for (int x = lane; x < a.Wm; x += 64) hist[x] = 0;
 #pragma unroll
     for (int qi = 0; qi < QMAX; ++qi)

@@ -79,14 +79,19 @@ struct FusedGeom {
   static constexpr int NBUF0 = (kLdsBytes - SLOTB) / BUF;
   static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
   static_assert(NBUF >= 3, "tile buffers do not fit in LDS");
-  static constexpr int LDS = NBUF * BUF + SLOTB;
+  // S0[r, h] is staged in LDS past the first two tile buffers (which the
+  // prologue fills first) until the consumers have split it into planes; the
+  // schedule's scratch (bucket counts, staged ancestry rows) is the first two.
+  static constexpr int S0B = DK * DV * 4, OS0 = 2 * BUF;
+  static constexpr int RINGB = NBUF * BUF > OS0 + S0B ? NBUF * BUF : OS0 + S0B;
+  static constexpr int LDS = RINGB + SLOTB;
+  static_assert(LDS <= kLdsBytes, "LDS layout does not fit");
+  static_assert(S0B % 1024 == 0, "S0 is staged in whole DMA blocks");
   // LDS-DMA instructions the DMA wave issues per tile
   static constexpr int OPT = 2 * (QB / 1024) + VB / 1024 + NSM + T * (RKB / 1024);
   static_assert(QB % 1024 == 0 && VB % 1024 == 0, "tile arrays must be whole DMA blocks");
   static_assert((2 + T) * 16 <= 128, "too many record depths for the small-value block");
   static_assert(T <= 4, "the schedule table holds at most four record depths");
-  // the sort's bucket counts live in the (not yet used) tile ring
-  static constexpr int SORT_CAP = NBUF * BUF / 4 < kSortMax ? NBUF * BUF / 4 : kSortMax;
 };
 
 template <int DK, int DV, int T>
@@ -96,8 +101,8 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   constexpr int NPL = 3;
   constexpr int TT = T > 0 ? T : 1;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
-  u32x4* s_tab = reinterpret_cast<u32x4*>(smem + G::NBUF * G::BUF);          // [position]
-  int* s_slot3 = reinterpret_cast<int*>(smem + G::NBUF * G::BUF + kMaxChunkF * 16);  // T == 4
+  u32x4* s_tab = reinterpret_cast<u32x4*>(smem + G::RINGB);                    // [position]
+  int* s_slot3 = reinterpret_cast<int*>(smem + G::RINGB + kMaxChunkF * 16);  // T == 4
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -117,7 +122,8 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   const int g = lane >> 4;
   const int c = lane & 15;
 
-  // Barriers: P (schedule table written), A (tile 0 resident), then
+  // Barriers: Q (t > 0: the schedule's loads have arrived), P (schedule
+  // table written), S (S0 staged in LDS), A (tile 0 resident), then
   // 0 .. ntiles.
   // Between barrier i and i + 1 the consumers take tile i, the dot wave
   // tile i + 1, and a DMA wave refills the buffer of tile i - 1.
@@ -126,8 +132,23 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     // ============================================================ DMA waves
     const int dw = w - G::WDMA;  // this wave owns tiles p with p % 2 == dw
     const int cg = lane >> 4;
-    if (T > 0 && dw == 0)
-      build_schedule<T>(a, r, h, b_begin, nb, lane, G::SORT_CAP, smem, s_tab, s_slot3);
+    // S0[r, h] into LDS (wave 1), after the schedule's loads have gone out
+    auto stage_s0 = [&] {
+      const float* S = a.S + ((size_t)r * a.H + h) * DK * DV;
+#pragma unroll
+      for (int m = 0; m < G::S0B / 1024; ++m) dma16(S + m * 256 + lane * 4, smem + G::OS0 + m * 1024);
+    };
+    if (T > 0) {
+      if (dw == 0) {
+        build_schedule<T>(a, r, h, b_begin, nb, lane, G::OS0, smem, s_tab, s_slot3,
+                          [] { lds_barrier(); });  // Q inside, once its loads have arrived
+      } else {
+        lds_barrier();  // Q
+        stage_s0();
+      }
+    } else if (dw == 1) {
+      stage_s0();
+    }
 
     auto dma_tile = [&](int p) {
       uint8_t* buf = smem + (p % G::NBUF) * G::BUF;
@@ -174,10 +195,19 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     // tiles this wave issued after tile q, up to tile `last`
     auto later = [&](int q, int last) { return last > q ? (last - q) / 2 : 0; };
     lds_barrier();  // P
+    // Tiles 0 and 1 first, on their own, so that they are not queued behind
+    // the rest of the prologue (every workgroup of the grid starts at once);
+    // the other prologue tiles follow barrier A, once S0 has left LDS.
     const int npro = min(G::NBUF - 1, ntiles);
-    for (int p = dw; p < npro; p += 2) dma_tile(p);
-    if (dw == 0) wait_tiles<G::OPT, 2>(later(0, npro - 1));  // tile 0 resident
-    lds_barrier();                                          // A
+    if (dw < npro) dma_tile(dw);
+    if (dw == 1) {
+      if (npro > 1) wait_vm<G::OPT>();  // S0 staged; tile 1 may still be in flight
+      else wait_vm<0>();
+    }
+    lds_barrier();              // S
+    if (dw == 0) wait_vm<0>();  // tile 0 resident
+    lds_barrier();              // A
+    for (int p = 2 + dw; p < npro; p += 2) dma_tile(p);
     if (dw == 1) wait_tiles<G::OPT, 2>(later(1, npro - 1));  // tile 1 resident
     lds_barrier();                                          // 0
     for (int i = 0; i < ntiles; ++i) {
@@ -233,7 +263,9 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
       for (int v = 0; v < 3 + 2 * T; ++v)
         if ((v & 3) == g) wout[v] = wt[v];
     };
+    if (T > 0) lds_barrier();  // Q
     lds_barrier();  // P
+    lds_barrier();  // S
     lds_barrier();  // A
     dots(0);
     lds_barrier();  // 0
@@ -248,17 +280,9 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   // This wave's slice of S0[r, h] as bf16 planes in the MFMA A layout: lane
   // (g, c) holds key channels 32s + 8g .. +7 of value row 16w + c, so C row
   // 4g + i is value row 16w + 4g + i.
-  u32x4 As[KS][NPL];
-  {
-    const float* S = a.S + ((size_t)r * a.H + h) * DK * DV;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = S[(size_t)(s * 32 + g * 8 + e) * DV + w * 16 + c];
-      split_planes<NPL>(x, As[s]);
-    }
-  }
+  // A DMA wave stages S0 in LDS; the planes are formed between barriers S
+  // and A.
+  if (T > 0) lds_barrier();  // Q
   const int row0 = w * 16 + 4 * g;  // first of this lane's 4 value rows
 
   // Store windows over the chunk's beams [b_begin, b_end): a lane whose beam
@@ -290,6 +314,18 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   lds_barrier();  // P: schedule table written
   f32x4 dnext[TT];
   load_deltas(0, dnext);  // in flight while tile 0 arrives
+  lds_barrier();  // S: S0 staged
+  u32x4 As[KS][NPL];
+  {
+    const float* S = reinterpret_cast<const float*>(smem + G::OS0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = S[(s * 32 + g * 8 + e) * DV + w * 16 + c];
+      split_planes<NPL>(x, As[s]);
+    }
+  }
   lds_barrier();  // A: tile 0 resident
   lds_barrier();  // 0
 

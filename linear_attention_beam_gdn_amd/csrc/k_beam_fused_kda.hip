@@ -77,8 +77,13 @@ struct KdaGeom {
   static constexpr int NBUF0 = (kLdsBytes - SLOTB) / BUF;
   static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
   static_assert(NBUF >= 3, "tile buffers do not fit in LDS");
-  static constexpr int LDS = NBUF * BUF + SLOTB;
-  static constexpr int SORT_CAP = NBUF * BUF / 4 < kSortMax ? NBUF * BUF / 4 : kSortMax;
+  // S0[r, h] is staged in LDS past the first two tile buffers until the
+  // consumers have split it into planes; the schedule's scratch is the first two.
+  static constexpr int S0B = DK * DV * 4, OS0 = 2 * BUF;
+  static constexpr int RINGB = NBUF * BUF > OS0 + S0B ? NBUF * BUF : OS0 + S0B;
+  static constexpr int LDS = RINGB + SLOTB;
+  static_assert(LDS <= kLdsBytes, "LDS layout does not fit");
+  static_assert(S0B % 1024 == 0, "S0 is staged in whole DMA blocks");
   // LDS-DMA instructions per tile (q|k, v, alpha_t, beta_t, then per record k_j, a_j)
   static constexpr int OPT = QKB / 1024 + VB / 1024 + AB / 1024 + 1 + T * (RKB / 1024 + AB / 1024);
   static_assert(QKB % 1024 == 0 && VB % 1024 == 0 && AB % 1024 == 0 && RKB % 1024 == 0,
@@ -149,8 +154,8 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   constexpr int EPL = G::EPL;
   constexpr int TT = T > 0 ? T : 1;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
-  u32x4* s_tab = reinterpret_cast<u32x4*>(smem + G::NBUF * G::BUF);
-  int* s_slot3 = reinterpret_cast<int*>(smem + G::NBUF * G::BUF + kMaxChunkF * 16);
+  u32x4* s_tab = reinterpret_cast<u32x4*>(smem + G::RINGB);
+  int* s_slot3 = reinterpret_cast<int*>(smem + G::RINGB + kMaxChunkF * 16);
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -166,14 +171,31 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   const int nb = b_end - b_begin;
   const int ntiles = (nb + G::TB - 1) / G::TB;
 
-  // Barriers: P (schedule table written), A (tile 0 resident), then
+  // Barriers: Q (t > 0: the schedule's loads have arrived), P (schedule
+  // table written), S (S0 staged in LDS), A (tile 0 resident), then
   // 0 .. ntiles.  Between barrier i and i + 1 the consumers finish tile i and
   // prepare tile i + 1, and a DMA wave refills the buffer of tile i - 1.
 
   if (w >= G::WDMA) {
     // ============================================================ DMA waves
     const int dw = w - G::WDMA;
-    if (T > 0 && dw == 0) build_schedule<T>(a, r, h, b_begin, nb, lane, G::SORT_CAP, smem, s_tab, s_slot3);
+    // S0[r, h] into LDS (wave 1), after the schedule's loads have gone out
+    auto stage_s0 = [&] {
+      const float* S = a.S + ((size_t)r * a.H + h) * DK * DV;
+#pragma unroll
+      for (int m = 0; m < G::S0B / 1024; ++m) dma16(S + m * 256 + lane * 4, smem + G::OS0 + m * 1024);
+    };
+    if (T > 0) {
+      if (dw == 0) {
+        build_schedule<T>(a, r, h, b_begin, nb, lane, G::OS0, smem, s_tab, s_slot3,
+                          [] { lds_barrier(); });  // Q inside, once its loads have arrived
+      } else {
+        lds_barrier();  // Q
+        stage_s0();
+      }
+    } else if (dw == 1) {
+      stage_s0();
+    }
 
     auto dma_tile = [&](int p) {
       uint8_t* buf = smem + (p % G::NBUF) * G::BUF;
@@ -212,10 +234,18 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
 
     auto later = [&](int q, int last) { return last > q ? (last - q) / 2 : 0; };
     lds_barrier();  // P
+    // tiles 0 and 1 first, on their own; the other prologue tiles follow A,
+    // once S0 has left LDS
     const int npro = min(G::NBUF - 1, ntiles);
-    for (int p = dw; p < npro; p += 2) dma_tile(p);
-    if (dw == 0) wait_tiles<G::OPT, 2>(later(0, npro - 1));  // tile 0 resident
-    lds_barrier();                                          // A
+    if (dw < npro) dma_tile(dw);
+    if (dw == 1) {
+      if (npro > 1) wait_vm<G::OPT>();  // S0 staged; tile 1 may still be in flight
+      else wait_vm<0>();
+    }
+    lds_barrier();              // S
+    if (dw == 0) wait_vm<0>();  // tile 0 resident
+    lds_barrier();              // A
+    for (int p = 2 + dw; p < npro; p += 2) dma_tile(p);
     if (dw == 1) wait_tiles<G::OPT, 2>(later(1, npro - 1));  // tile 1 resident
     lds_barrier();                                          // 0
     for (int i = 0; i < ntiles; ++i) {
@@ -330,17 +360,9 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   const int c = lane & 15;
   const int bb = c & 7;     // beam of this lane within the tile
   const int side = c >> 3;  // 0: q column, 1: k column
-  u32x4 As[KS][2];
-  {
-    const float* S = a.S + ((size_t)r * a.H + h) * DK * DV;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = S[(size_t)(s * 32 + g * 8 + e) * DV + w * 16 + c];
-      split_planes<2>(x, As[s]);
-    }
-  }
+  // A DMA wave stages S0 in LDS; the planes are formed between barriers S
+  // and A.
+  if (T > 0) lds_barrier();  // Q
   const int row0 = w * 16 + 4 * g;
   const int so = a.H * DV * 4;
   const size_t tok0 = ((size_t)r * a.Wt + b_begin) * a.H + h;
@@ -363,7 +385,19 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   lds_barrier();  // P
   f32x4 dnext[TT];
   load_deltas(0, dnext);
-  lds_barrier();  // A
+  lds_barrier();  // S: S0 staged
+  u32x4 As[KS][2];
+  {
+    const float* S = reinterpret_cast<const float*>(smem + G::OS0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = S[(s * 32 + g * 8 + e) * DV + w * 16 + c];
+      split_planes<2>(x, As[s]);
+    }
+  }
+  lds_barrier();  // A: tile 0 resident
   prep(0);
   lds_barrier();  // 0
 
