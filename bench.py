@@ -185,15 +185,38 @@ def sequence_row(B, torch, dev, stream, wl):
     d = _queued(torch, stream, calls)
     dec_us = [float(np.mean([x for x, k in zip(d, kinds) if k == j])) for j in range(wl.M)]
     merge_us = float(np.mean([x for x, k in zip(d, kinds) if k == -1]))
+
+    # the same tokens with the merge fused into the decode that fills the log
+    fstore = B.Store(wl.R, 1, wl.H, wl.dk, wl.dv, wl.M, channel_decay=wl.channel_decay,
+                     S=torch.from_numpy(seq["S0"]).to(dev))
+
+    def fused(i):
+        d = toks[i]
+        args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        if i % wl.M == wl.M - 1:
+            B.decode_merge_step(fstore, i % wl.M, *args, o=o, stream=stream)
+        else:
+            B.decode_step(fstore, i % wl.M, 1, zero, *args, o=o, stream=stream)
+
+    df = _queued(torch, stream, [(lambda i=i: fused(i)) for i in range(wl.T)])
+    fdec_us = [float(np.mean(df[j::wl.M])) for j in range(wl.M)]
     dec_b = [accounting.sequence_token_bytes(R=wl.R, H=wl.H, dk=wl.dk, dv=wl.dv, log_len=j,
                                              channel_decay=wl.channel_decay) for j in range(wl.M)]
     mrg_b = accounting.merge_bytes(R=wl.R, H=wl.H, dk=wl.dk, dv=wl.dv, n_rec=wl.M, channel_decay=wl.channel_decay)
     cycle_us = sum(dec_us) + merge_us
-    return {"workload": wl.name, "sequence_steps_per_s": wl.R * wl.M / (cycle_us * 1e-6),
-            "us_per_token_amortised": cycle_us / wl.M,
-            "decode": {**_bw(float(np.mean(dec_b)), float(np.mean(dec_us))), "us_by_log_length": dec_us},
-            "merge": _bw(mrg_b, merge_us),
-            "cycle": _bw(sum(dec_b) + mrg_b, cycle_us)}
+    fdm_b = accounting.decode_merge_bytes(R=wl.R, H=wl.H, dk=wl.dk, dv=wl.dv, log_len=wl.M - 1,
+                                          channel_decay=wl.channel_decay)
+    fcycle_us = sum(fdec_us)
+    fcycle_b = sum(dec_b[:-1]) + fdm_b
+    return {"workload": wl.name,
+            "sequence_steps_per_s": wl.R * wl.M / (fcycle_us * 1e-6),
+            "us_per_token_amortised": fcycle_us / wl.M,
+            "fused_cycle": {**_bw(fcycle_b, fcycle_us), "us_by_log_length": fdec_us,
+                            "decode_merge": _bw(fdm_b, fdec_us[-1])},
+            "separate": {"sequence_steps_per_s": wl.R * wl.M / (cycle_us * 1e-6),
+                         "decode": {**_bw(float(np.mean(dec_b)), float(np.mean(dec_us))), "us_by_log_length": dec_us},
+                         "merge": _bw(mrg_b, merge_us),
+                         "cycle": _bw(sum(dec_b) + mrg_b, cycle_us)}}
 
 
 def materialize_row(B, torch, dev, stream, wl, n_items, reps):

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GDN_BEAM_ABI_VERSION 1
+#define GDN_BEAM_ABI_VERSION 2
 
 /* status codes */
 #define GDN_OK 0
@@ -118,6 +118,27 @@ int gdn_beam_decode_step(const gdn_shape* shape, const gdn_store* store, int32_t
                          int32_t W_t, const int32_t* parent, const uint16_t* q,
                          const uint16_t* k, const uint16_t* v, const float* alpha,
                          const float* beta, float* o, void* stream);
+
+/*
+ * Bounded-log decoding with the merge in the same pass (DeltaLog Figure 4: the
+ * logical state is written into the dense base when the log is full; Figure 5
+ * caption: the merge path has the structure of the append decode and writes
+ * back base tiles).  For independent sequences (W_max == 1 only): decode
+ * token t exactly as gdn_beam_decode_step(shape, store, t, 1, NULL, ...) does,
+ * appending its record at log slot t, then fold log records 0..t into S in
+ * place, S <- alpha_j S + k_j delta_j^T in log order (channel decay:
+ * diag(a_j) S + ...), from the base values the step has already read.  The
+ * result equals that decode step followed by gdn_log_merge(shape, store,
+ * t + 1, 0); the caller then restarts at t = 0.
+ *   t        current log length, 0 <= t < L_max
+ *   q, k     bf16 [R][1][H][dk];  v  bf16 [R][1][H][dv]
+ *   alpha    FP32 [R][1][H][A];   beta FP32 [R][1][H]
+ *   o        FP32 [R][1][H][dv] (output)
+ * Returns GDN_EUNSUPPORTED when W_max != 1.
+ */
+int gdn_decode_merge_step(const gdn_shape* shape, const gdn_store* store, int32_t t,
+                          const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const float* alpha, const float* beta, float* o, void* stream);
 
 /*
  * Dense states after step t of n beams (the conceptual S_{t,b} of OneLA §3.1,

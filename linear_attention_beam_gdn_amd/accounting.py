@@ -85,6 +85,15 @@ def merge_bytes(*, R, H, dk, dv, n_rec, channel_decay=False):
     return R * H * (2 * 4 * dk * dv + n_rec * record_bytes(dk, dv, channel_decay))
 
 
+def decode_merge_bytes(*, R, H, dk, dv, log_len, channel_decay=False):
+    """The decode that fills the log with the merge in the same pass: the
+    token's bytes (base read once), the base written back, and the log's
+    log_len + 1 records read by the fold."""
+    rec = record_bytes(dk, dv, channel_decay)
+    return (sequence_token_bytes(R=R, H=H, dk=dk, dv=dv, log_len=log_len, channel_decay=channel_decay)
+            + R * H * (4 * dk * dv + (log_len + 1) * rec))
+
+
 def onela_fig8b(*, R, W, H, K, V, O, record_bytes_per_head):
     """Capacity and write figures as OneLA §4.4 counts them.
 

@@ -55,6 +55,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_materialize.restype = ctypes.c_int
         L.gdn_log_merge.argtypes = [ctypes.POINTER(GdnShape), ctypes.POINTER(GdnStore), I32, I32, P]
         L.gdn_log_merge.restype = ctypes.c_int
+        L.gdn_decode_merge_step.argtypes = [ctypes.POINTER(GdnShape), ctypes.POINTER(GdnStore), I32,
+                                            P, P, P, P, P, P, P]
+        L.gdn_decode_merge_step.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -158,6 +161,25 @@ def materialize(store: Store, t, rb, out=None, stream=None):
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_materialize")
     return out
+
+
+def decode_merge_step(store: Store, t, q, k, v, alpha, beta, o=None, stream=None):
+    """Decode token t of independent sequences and fold the full log into the
+    base in the same pass (gdn_decode_merge_step); returns o [R,1,H,dv] FP32."""
+    R, H, dk, dv = store.R, store.H, store.dk, store.dv
+    _check(q, "q", _BF16, (R, 1, H, dk))
+    _check(k, "k", _BF16, (R, 1, H, dk))
+    _check(v, "v", _BF16, (R, 1, H, dv))
+    _check(alpha, "alpha", (torch.float32,), (R, 1, H, dk) if store.channel_decay else (R, 1, H))
+    _check(beta, "beta", (torch.float32,), (R, 1, H))
+    if o is None:
+        o = torch.empty(R, 1, H, dv, dtype=torch.float32, device=q.device)
+    _check(o, "o", (torch.float32,), (R, 1, H, dv))
+    rc = lib().gdn_decode_merge_step(ctypes.byref(store.shape), ctypes.byref(store.cstore), t, _ptr(q), _ptr(k),
+                                     _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_decode_merge_step")
+    return o
 
 
 def log_merge(store: Store, n_rec, beam=0, stream=None):

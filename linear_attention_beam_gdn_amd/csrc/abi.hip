@@ -71,8 +71,23 @@ int gdn_beam_decode_step(const gdn_shape* shape, const gdn_store* store, int32_t
     return GDN_EINVAL;
   const gdn::StepIO io{parent, q, k, v, alpha, beta, o};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (shape->W_max == 1) return gdn::launch_seq_decode(*shape, *store, t, io, s);
+  if (shape->W_max == 1) return gdn::launch_seq_decode(*shape, *store, t, false, io, s);
   return gdn::launch_beam_decode(*shape, *store, t, W_t, io, s);
+}
+
+int gdn_decode_merge_step(const gdn_shape* shape, const gdn_store* store, int32_t t, const uint16_t* q,
+                          const uint16_t* k, const uint16_t* v, const float* alpha, const float* beta,
+                          float* o, void* stream) {
+  int rc = check_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if ((rc = check_store(store)) != GDN_OK) return rc;
+  if (shape->W_max != 1) return GDN_EUNSUPPORTED;
+  if (t < 0 || t >= shape->L_max) return GDN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 16) ||
+      !aligned(beta, 16) || !aligned(o, 16))
+    return GDN_EINVAL;
+  const gdn::StepIO io{nullptr, q, k, v, alpha, beta, o};
+  return gdn::launch_seq_decode(*shape, *store, t, true, io, reinterpret_cast<hipStream_t>(stream));
 }
 
 int gdn_materialize(const gdn_shape* shape, const gdn_store* store, int32_t t, const int32_t* rb,

@@ -57,6 +57,17 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, co
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// One record applied to four entries of a state row, a s + k d, with the
+// rounding spelled out (k d fused onto the rounded a s) so that every kernel
+// that folds records (materialise, merge, the merge path of the sequence
+// decode) produces the same bits.
+__device__ __forceinline__ f32x4 apply_record(const f32x4& s, float a, float k, const f32x4& d) {
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = __builtin_fmaf(k, d[e], a * s[e]);
+  return r;
+}
+
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 }  // namespace gdn

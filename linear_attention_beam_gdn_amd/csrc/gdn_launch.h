@@ -39,7 +39,8 @@ int launch_beam_fused_kda(const gdn_shape& sh, const gdn_store& st, int t, int W
                           hipStream_t stream);
 
 // One beam per request (W_max == 1): bounded-log decoding of sequences.
-int launch_seq_decode(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io,
+// With `merge`, the step also folds log records 0..t into S and writes it.
+int launch_seq_decode(const gdn_shape& sh, const gdn_store& st, int t, bool merge, const StepIO& io,
                       hipStream_t stream);
 
 // Fold chains of records onto dense states.  Item i is the (request, beam)

@@ -76,7 +76,7 @@ __global__ __launch_bounds__((FoldGeom<DK, DV>::NT)) void k_fold(FoldArgs a) {
       const int row = rg * G::RPG + i;
       const float kj = bf16_at(a.rec_k[rj * DK + row]);
       const float aj = CH ? a.rec_alpha[rj * A + row] : aj0;
-      st[i] = aj * st[i] + kj * dj;
+      st[i] = apply_record(st[i], aj, kj, dj);
     }
   }
 #pragma unroll

@@ -6,6 +6,13 @@
 // [d_k][d_v] FP32 base once with 16-byte loads, forms the two projections
 // base^T x_q and base^T x_k with FP32 FMAs, reduces them across row groups in
 // LDS, replays the log on them, and appends the new record.
+//
+// The merge path (DeltaLog Figure 5 caption: the same structure, writing back
+// dense-base tiles; Figure 4: the log is folded into the base when it is
+// full) is the same kernel with MRG set: after the token's append, each
+// thread folds records 0..t (the new one included) into the base rows it
+// already holds, S <- alpha_j S + k_j delta_j^T in log order, and writes them
+// back, so a merge costs no second read of the base.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -14,6 +21,7 @@ namespace {
 
 struct SeqArgs {
   const float* S;
+  float* S_out;  // the base written back by the merge path
   float* rec_delta;
   uint16_t* rec_k;
   float* rec_alpha;
@@ -39,7 +47,7 @@ struct SeqGeom {
   static constexpr int NWV = (NT + 63) / 64;             // waves
 };
 
-template <int DK, int DV, bool CH>
+template <int DK, int DV, bool CH, bool MRG>
 __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a) {
   using G = SeqGeom<DK, DV>;
   constexpr int A = CH ? DK : 1;
@@ -57,6 +65,7 @@ __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a)
   __shared__ float probe_q[DK], probe_k[DK];
   __shared__ float red_q[G::NRG][DV], red_k[G::NRG][DV];
   __shared__ float dots_q[GDN_MAX_STEPS], dots_k[GDN_MAX_STEPS], dot_qk;
+  __shared__ float d_new[MRG ? DV : 1];
 
   // stream this thread's rows of the base first
   const float* S = a.S + tok * DK * DV;
@@ -142,6 +151,7 @@ __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a)
     const float d = bt * (vv - at * uk);
     a.o[tok * DV + col] = at * uq + d * dot_qk;
     a.rec_delta[rec_t * DV + col] = d;
+    if constexpr (MRG) d_new[col] = d;
   }
   for (int kk = tid; kk < DK; kk += G::NT) {
     a.rec_k[rec_t * DK + kk] = a.k[tok * DK + kk];
@@ -150,12 +160,37 @@ __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a)
   if constexpr (!CH)
     if (tid == 0) a.rec_alpha[rec_t] = at;
   if (h == 0 && tid < t) a.anc[(((size_t)t * a.R + r) * 1 + 0) * a.L + tid] = 0;
+
+  if constexpr (MRG) {
+    // fold the full log into this thread's rows of the base: records 0..t-1
+    // from the store, record t (this token's) from its inputs and d_new; the
+    // same update, in the same order, as the stand-alone merge
+    __syncthreads();
+    for (int j = 0; j <= t; ++j) {
+      const size_t rj = rec_at(j);
+      const f32x4 dj = j < t ? *reinterpret_cast<const f32x4*>(a.rec_delta + rj * DV + c4 * 4)
+                             : *reinterpret_cast<const f32x4*>(&d_new[c4 * 4]);
+      const float aj0 = CH ? 0.f : (j < t ? a.rec_alpha[rj] : at);
+#pragma unroll
+      for (int i = 0; i < G::RPG; ++i) {
+        const int row = rg * G::RPG + i;
+        const float kj = bf16_at(j < t ? a.rec_k[rj * DK + row] : a.k[tok * DK + row]);
+        const float aj = CH ? (j < t ? a.rec_alpha[rj * A + row] : a.alpha[tok * DK + row]) : aj0;
+        st[i] = apply_record(st[i], aj, kj, dj);
+      }
+    }
+    float* Sw = a.S_out + tok * DK * DV;
+#pragma unroll
+    for (int i = 0; i < G::RPG; ++i)
+      *reinterpret_cast<f32x4*>(Sw + (size_t)(rg * G::RPG + i) * DV + c4 * 4) = st[i];
+  }
 }
 
-template <int DK, int DV, bool CH>
+template <int DK, int DV, bool CH, bool MRG>
 int launch(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io, hipStream_t stream) {
   SeqArgs a;
   a.S = st.S;
+  a.S_out = st.S;
   a.rec_delta = st.rec_delta;
   a.rec_k = st.rec_k;
   a.rec_alpha = st.rec_alpha;
@@ -172,20 +207,24 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io, hi
   a.t = t;
   const long grid = (long)sh.R * sh.H;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
-  hipLaunchKernelGGL((k_seq_decode<DK, DV, CH>), dim3((unsigned)grid), dim3(SeqGeom<DK, DV>::NT), 0,
+  hipLaunchKernelGGL((k_seq_decode<DK, DV, CH, MRG>), dim3((unsigned)grid), dim3(SeqGeom<DK, DV>::NT), 0,
                      stream, a);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
 }  // namespace
 
-int launch_seq_decode(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io,
+int launch_seq_decode(const gdn_shape& sh, const gdn_store& st, int t, bool merge, const StepIO& io,
                       hipStream_t stream) {
   const bool ch = sh.decay_kind == GDN_DECAY_CHANNEL;
-#define GDN_CASE(DK_, DV_)                                                       \
-  if (sh.dk == DK_ && sh.dv == DV_)                                              \
-    return ch ? launch<DK_, DV_, true>(sh, st, t, io, stream)                    \
-              : launch<DK_, DV_, false>(sh, st, t, io, stream);
+#define GDN_CASE(DK_, DV_)                                                                         \
+  if (sh.dk == DK_ && sh.dv == DV_) {                                                              \
+    if (merge)                                                                                     \
+      return ch ? launch<DK_, DV_, true, true>(sh, st, t, io, stream)                              \
+                : launch<DK_, DV_, false, true>(sh, st, t, io, stream);                            \
+    return ch ? launch<DK_, DV_, true, false>(sh, st, t, io, stream)                               \
+              : launch<DK_, DV_, false, false>(sh, st, t, io, stream);                             \
+  }
   GDN_CASE(16, 16)
   GDN_CASE(32, 32)
   GDN_CASE(64, 64)

@@ -38,8 +38,8 @@ def decode(L, sh=None, st=None, t=1, W_t=4, parent=FAKE, q=FAKE, k=FAKE, v=FAKE,
 
 def test_exports_every_header_function(L):
     names = B.header_functions()
-    assert set(names) == {"gdn_beam_decode_step", "gdn_materialize", "gdn_log_merge",
-                          "gdn_status_string", "gdn_abi_version"}
+    assert set(names) == {"gdn_beam_decode_step", "gdn_decode_merge_step", "gdn_materialize",
+                          "gdn_log_merge", "gdn_status_string", "gdn_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
@@ -49,7 +49,7 @@ def test_exports_every_header_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gdn_abi_version() == 1
+    assert L.gdn_abi_version() == 2
     for s in (B.GDN_OK, B.GDN_EINVAL, B.GDN_EUNSUPPORTED, B.GDN_EHIP, 12345):
         assert isinstance(B.status_string(s), str) and B.status_string(s)
 
@@ -109,3 +109,22 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(1, 1, 1, 16, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="device tensor"):
         B.decode_step(st, 0, 1, None, x, x, x, torch.zeros(1, 1, 1), torch.zeros(1, 1, 1))
+
+
+def test_decode_merge_validation(L):
+    E, U = B.GDN_EINVAL, B.GDN_EUNSUPPORTED
+    seq = shape(W_max=1)
+
+    def dm(sh=seq, st=None, t=3, q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, o=FAKE):
+        st = store() if st is None else st
+        return L.gdn_decode_merge_step(ctypes.byref(sh), ctypes.byref(st), t, q, k, v, alpha, beta, o, None)
+
+    assert dm(sh=shape(W_max=8)) == U  # beams: merge with gdn_log_merge instead
+    assert dm(sh=shape(W_max=1, dk=96, dv=96)) == U
+    assert dm(t=-1) == E
+    assert dm(t=4) == E
+    for name in ("q", "k", "v", "alpha", "beta", "o"):
+        assert dm(**{name: None}) == E, name
+        assert dm(**{name: FAKE + 8}) == E, name
+    for name in ("S", "rec_delta", "rec_k", "rec_alpha", "anc"):
+        assert dm(st=store(**{name: None})) == E, name

@@ -46,3 +46,19 @@ def test_unique_ancestors():
     row = np.array([[0, 1], [0, 1], [0, 2], [3, 2]])
     assert A.unique_ancestors(row, 4) == 2 + 2
     assert A.unique_ancestors(row, 2) == 1 + 1
+
+
+def test_bounded_log_run_bytes():
+    # 128 sequences, H/d_k/d_v = 32/128/128, log capacity M = 8 (DeltaLog
+    # Table 3), 64 tokens: 8 full cycles of log lengths 0..7.  A merge cycle
+    # either merges separately (base read + written + 8 records) or folds the
+    # log in the decode that fills it (base written + 8 records, no second
+    # base read).
+    kw = dict(R=128, H=32, dk=128, dv=128)
+    tokens = 8 * sum(A.sequence_token_bytes(log_len=j, **kw) for j in range(8))
+    separate = tokens + 8 * A.merge_bytes(n_rec=8, **kw)
+    fused = 8 * (sum(A.sequence_token_bytes(log_len=j, **kw) for j in range(7))
+                 + A.decode_merge_bytes(log_len=7, **kw))
+    assert separate == 22_925_541_376
+    assert fused == 20_778_057_728
+    assert separate - fused == 8 * 128 * 32 * 4 * 128 * 128  # one base read per cycle

@@ -115,6 +115,39 @@ def test_sequences_small(channel):
             assert rel_states(S, ref["bases"][i // M][:, None]) <= TOL
 
 
+@pytest.mark.parametrize("channel", [False, True])
+def test_decode_merge_step(channel):
+    """The merge path fused into the decode that fills the log: matches the
+    oracle's merged bases and outputs, and equals decode-then-merge exactly."""
+    R, H, dk, dv, T, M = 5, 3, 64, 64, 12, 4
+    seq = synth.make_sequence_inputs(R=R, H=H, dk=dk, dv=dv, T=T, s0_std=0.1, seed=11,
+                                     channel_decay=channel)
+    ref = O.sequence_decode(seq["S0"], seq["tokens"], M)
+    S0 = torch.from_numpy(seq["S0"]).cuda()
+    fused = B.Store(R, 1, H, dk, dv, M, channel_decay=channel, S=S0.clone())
+    split = B.Store(R, 1, H, dk, dv, M, channel_decay=channel, S=S0.clone())
+    zero = torch.zeros(R, 1, dtype=torch.int32, device="cuda")
+    for i in range(T):
+        t = i % M
+        d = B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")})
+        args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        if t == M - 1:
+            o_f = B.decode_merge_step(fused, t, *args)
+        else:
+            o_f = B.decode_step(fused, t, 1, zero, *args)
+        o_s = B.decode_step(split, t, 1, zero, *args)
+        if t == M - 1:
+            B.log_merge(split, M, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(o_f, o_s), i
+        assert rel_slices(o_f[:, 0].cpu().numpy().reshape(R * H, dv), ref["o"][i]) <= TOL
+        if t == M - 1:
+            assert torch.equal(fused.S, split.S), i
+            S = fused.S.cpu().numpy().reshape(R * H, 1, dk, dv)
+            assert rel_states(S, ref["bases"][i // M][:, None]) <= TOL
+    log(f"[parity] decode+merge fused ch={channel}: equal to decode-then-merge")
+
+
 # ---------------------------------------------------------------- edge cases
 
 def test_single_beam_in_wide_store():
