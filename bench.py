@@ -14,6 +14,7 @@ workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import multiprocessing as mp
 import os
@@ -219,6 +220,20 @@ def sequence_row(B, torch, dev, stream, wl):
                          "cycle": _bw(sum(dec_b) + mrg_b, cycle_us)}}
 
 
+def merge_interval_row(B, torch, dev, stream, wl, intervals):
+    """The bounded-log workload at several log capacities M (DeltaLog Figure 9
+    sweeps M = 4 and 8): amortised time per token and bandwidth of one merge
+    cycle, merge fused into the decode that fills the log and separate."""
+    out = {}
+    for m in intervals:
+        r = sequence_row(B, torch, dev, stream, dataclasses.replace(wl, M=m))
+        out[f"M={m}"] = {"us_per_token_amortised": r["us_per_token_amortised"],
+                         "achieved_GBps": r["fused_cycle"]["achieved_GBps"],
+                         "frac_of_peak": r["fused_cycle"]["frac_of_peak"],
+                         "separate_us_per_token_amortised": r["separate"]["cycle"]["us"] / m}
+    return out
+
+
 def materialize_row(B, torch, dev, stream, wl, n_items, reps):
     """Dense states of n_items beams after the last step of a beam workload."""
     inp = wl.inputs()
@@ -368,6 +383,7 @@ def main():
             "single_request_beam_decode": beam_row(B, torch, dev, stream, configs.SINGLE, reps),
             "channel_decay_beam_decode": beam_row(B, torch, dev, stream, configs.KDA, reps),
             "bounded_log_decode_and_merge": sequence_row(B, torch, dev, stream, configs.DELTALOG),
+            "bounded_log_merge_interval": merge_interval_row(B, torch, dev, stream, configs.DELTALOG, (4, 8, 16)),
             "materialize": materialize_row(B, torch, dev, stream, WORKLOAD, 64, reps),
         }
     print(json.dumps(line), flush=True)

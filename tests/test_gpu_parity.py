@@ -56,13 +56,14 @@ def test_kda_workload_sampled():
     check_beam(configs.KDA.inputs(), True, requests=[0, 15], heads=[0, 31], label="kda")
 
 
-def test_deltalog_workload():
+@pytest.mark.parametrize("fused", [False, True])
+def test_deltalog_workload(fused):
     w = configs.DELTALOG
     seq = w.inputs()
     pairs = [(0, 0), (0, 31), (17, 5), (64, 16), (101, 30), (127, 0), (127, 31), (90, 9)]
     rs = np.array([p[0] for p in pairs])
     hs = np.array([p[1] for p in pairs])
-    log(f"[parity] deltalog R={w.R} H={w.H} T={w.T} M={w.M}")
+    log(f"[parity] deltalog R={w.R} H={w.H} T={w.T} M={w.M} fused merge={fused}")
     ref = O.sequence_decode(seq["S0"], seq["tokens"], w.M, pairs=pairs)
     store = B.Store(w.R, 1, w.H, w.dk, w.dv, w.M, S=torch.from_numpy(seq["S0"]).cuda())
     zero = torch.zeros(w.R, 1, dtype=torch.int32, device="cuda")
@@ -72,12 +73,16 @@ def test_deltalog_workload():
     for i in range(w.T):
         t = i % w.M
         d = B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")})
-        o = B.decode_step(store, t, 1, zero, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        if fused and t == w.M - 1:
+            o = B.decode_merge_step(store, t, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        else:
+            o = B.decode_step(store, t, 1, zero, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
         o_s = o[rs_d, 0, hs_d].cpu().numpy()
         d_s = store.rec_delta[t, rs_d, 0, hs_d].cpu().numpy()
         worst = max(worst, rel_slices(o_s, ref["o"][i]), rel_slices(d_s, ref["delta"][i]))
         if t == w.M - 1:
-            B.log_merge(store, w.M, 0)
+            if not fused:
+                B.log_merge(store, w.M, 0)
             S_s = store.S[rs_d, hs_d].cpu().numpy()
             worst = max(worst, rel_states(S_s[:, None], ref["bases"][i // w.M][:, None]))
         assert worst <= TOL, (i, worst)
