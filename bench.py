@@ -201,6 +201,30 @@ def sequence_row(B, torch, dev, stream, wl):
 
     df = _queued(torch, stream, [(lambda i=i: fused(i)) for i in range(wl.T)])
     fdec_us = [float(np.mean(df[j::wl.M])) for j in range(wl.M)]
+
+    # one merge cycle of the fused path captured in a HIP graph and replayed
+    # (the replays keep decoding the cycle's M tokens on the evolving base)
+    gstore = B.Store(wl.R, 1, wl.H, wl.dk, wl.dv, wl.M, channel_decay=wl.channel_decay,
+                     S=torch.from_numpy(seq["S0"]).to(dev))
+    gout = torch.empty_like(o)
+
+    def gcycle():
+        for i in range(wl.M):
+            d = toks[i]
+            args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+            if i == wl.M - 1:
+                B.decode_merge_step(gstore, i, *args, o=gout)
+            else:
+                B.decode_step(gstore, i, 1, zero, *args, o=gout)
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gcycle()
+    graph.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, wl.T // wl.M)
+    graph_cycle_us = float(np.mean(_queued(torch, stream, [graph.replay] * n_rep)))
     dec_b = [accounting.sequence_token_bytes(R=wl.R, H=wl.H, dk=wl.dk, dv=wl.dv, log_len=j,
                                              channel_decay=wl.channel_decay) for j in range(wl.M)]
     mrg_b = accounting.merge_bytes(R=wl.R, H=wl.H, dk=wl.dk, dv=wl.dv, n_rec=wl.M, channel_decay=wl.channel_decay)
@@ -214,6 +238,7 @@ def sequence_row(B, torch, dev, stream, wl):
             "us_per_token_amortised": fcycle_us / wl.M,
             "fused_cycle": {**_bw(fcycle_b, fcycle_us), "us_by_log_length": fdec_us,
                             "decode_merge": _bw(fdm_b, fdec_us[-1])},
+            "fused_cycle_graph_replay": _bw(fcycle_b, graph_cycle_us),
             "separate": {"sequence_steps_per_s": wl.R * wl.M / (cycle_us * 1e-6),
                          "decode": {**_bw(float(np.mean(dec_b)), float(np.mean(dec_us))), "us_by_log_length": dec_us},
                          "merge": _bw(mrg_b, merge_us),
