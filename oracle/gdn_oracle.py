@@ -26,7 +26,10 @@ is stored as its transpose, an array [d_k, d_v], so the same recurrence reads
 For per-channel decay (the KDA row of DeltaLog Table 1: transform
 D(lambda_t) S_{t-1}, update pair (k_t, beta_t (v_t - k_t^T S_{t-1})), diagonal
 decay), alpha_t is a d_k vector that scales the rows of S before the delta
-correction.
+correction.  The RWKV6 row of the same table keeps the diagonal decay but its
+update pair is (k_t, v_t): no delta correction, so S_t = D(a_t) S_{t-1} +
+k_t v_t^T, the record's update vector is v_t itself and beta is not used
+(``rule="plain"`` below; the readout stays o_t = S_t^T q_t).
 
 Every array is converted to float64 exactly (bf16 bit patterns and FP32 values
 widen without rounding) and all arithmetic is FP64.  Batching over beams uses
@@ -82,15 +85,22 @@ def readout(S, x):
     return np.matmul(x[:, None, :], S)[:, 0, :]
 
 
-def transition(S, k, v, alpha, beta):
-    """One eager GDN step on a batch of states; returns (S_t, delta_t).
+def transition(S, k, v, alpha, beta, rule="delta"):
+    """One eager step on a batch of states; returns (S_t, delta_t).
 
-    The decayed state is corrected towards v along k (the delta rule), and the
-    transition record's update vector is delta_t = beta_t (v_t - decayed^T k_t)
-    (OneLA §3.2, GTR equation), so that S_t = decayed + k_t delta_t^T.
+    rule "delta" (GDN, KDA): the decayed state is corrected towards v along k,
+    and the transition record's update vector is delta_t = beta_t (v_t -
+    decayed^T k_t) (OneLA §3.2, GTR equation), so that S_t = decayed +
+    k_t delta_t^T.  rule "plain" (RWKV6 row of DeltaLog Table 1): the update
+    pair is (k_t, v_t), so delta_t = v_t and S_t = decayed + k_t v_t^T.
     """
     S_dec = decay(S, alpha)
-    delta = beta[:, None] * (v - readout(S_dec, k))
+    if rule == "plain":
+        delta = np.array(v, dtype=np.float64, copy=True)
+    elif rule == "delta":
+        delta = beta[:, None] * (v - readout(S_dec, k))
+    else:
+        raise ValueError(rule)
     return S_dec + k[:, :, None] * delta[:, None, :], delta
 
 
@@ -129,7 +139,7 @@ def _anc_of(steps):
 # eager dense decode of beams (the reference for o_t, delta_t and S_{t,b})
 # --------------------------------------------------------------------------
 
-def _eager_chain(S0, steps, anc, t, r, h, beams):
+def _eager_chain(S0, steps, anc, t, r, h, beams, rule="delta"):
     """Dense states and delta_t of ``beams`` of request r, head h after step t.
 
     Starts from the shared state S0[r, h] and applies, in order, the inputs of
@@ -141,13 +151,13 @@ def _eager_chain(S0, steps, anc, t, r, h, beams):
     for j in range(t):
         slot = anc[t][r, beams, j]
         _, k, v, alpha, beta = _token(steps[j], r, slot, h)
-        S, _ = transition(S, k, v, alpha, beta)
+        S, _ = transition(S, k, v, alpha, beta, rule)
     q, k, v, alpha, beta = _token(steps[t], r, beams, h)
-    S, delta = transition(S, k, v, alpha, beta)
+    S, delta = transition(S, k, v, alpha, beta, rule)
     return S, delta, q
 
 
-def beam_decode(S0, steps, *, requests=None, heads=None):
+def beam_decode(S0, steps, *, requests=None, heads=None, rule="delta"):
     """Eager reference for every decode step.
 
     S0: FP32 [R, H, d_k, d_v]; steps: list of per-step input dicts (see the
@@ -166,7 +176,7 @@ def beam_decode(S0, steps, *, requests=None, heads=None):
         d = np.full((R, Wt, H, dv), np.nan)
         for r in requests:
             for h in heads:
-                S, delta, q = _eager_chain(S0, steps, anc, t, r, h, np.arange(Wt))
+                S, delta, q = _eager_chain(S0, steps, anc, t, r, h, np.arange(Wt), rule)
                 o[r, :, h] = readout(S, q)
                 d[r, :, h] = delta
         o_all.append(o)
@@ -174,7 +184,7 @@ def beam_decode(S0, steps, *, requests=None, heads=None):
     return dict(anc=anc, o=o_all, delta=d_all)
 
 
-def beam_states(S0, steps, t, pairs, *, heads=None):
+def beam_states(S0, steps, t, pairs, *, heads=None, rule="delta"):
     """Dense states S_{t,b} [n, H, d_k, d_v] (float64) for (r, b) ``pairs``."""
     R, H, dk, dv = S0.shape
     anc = _anc_of(steps)
@@ -182,7 +192,7 @@ def beam_states(S0, steps, t, pairs, *, heads=None):
     out = np.full((len(pairs), H, dk, dv), np.nan)
     for i, (r, b) in enumerate(pairs):
         for h in heads:
-            S, _, _ = _eager_chain(S0, steps, anc, t, r, h, [b])
+            S, _, _ = _eager_chain(S0, steps, anc, t, r, h, [b], rule)
             out[i, h] = S[0]
     return out
 
@@ -192,7 +202,7 @@ def beam_states(S0, steps, t, pairs, *, heads=None):
 # replay and eager agree; KDA: the decay moves onto the d_k-side probe
 # --------------------------------------------------------------------------
 
-def beam_decode_replay(S0, steps, *, requests=None, heads=None):
+def beam_decode_replay(S0, steps, *, requests=None, heads=None, rule="delta"):
     """Projection replay over records (alpha_j, delta_j, k_j), in FP64.
 
     Scalar decay follows OneLA's recursion: u^(-1) = S_ctx^T x,
@@ -200,7 +210,8 @@ def beam_decode_replay(S0, steps, *, requests=None, heads=None):
     delta_t = beta_t (v_t - alpha_t u_k^(t-1)), o_t = alpha_t u_q^(t-1) +
     delta_t (k_t . q_t).  Channel decay unrolls S_j^T y = S_{j-1}^T (a_j * y) +
     delta_j (k_j . y) from the current step down to S_ctx.  Records are the
-    replay's own deltas of earlier steps.
+    replay's own deltas of earlier steps.  With the plain rule the update
+    vector is v_t itself (no projection of k_t is needed).
     """
     R, H, _, dv = S0.shape
     anc = _anc_of(steps)
@@ -225,7 +236,7 @@ def beam_decode_replay(S0, steps, *, requests=None, heads=None):
                     for a_j, delta_j, k_j in chain:
                         u_q = a_j[:, None] * u_q + delta_j * np.sum(k_j * q, 1)[:, None]
                         u_k = a_j[:, None] * u_k + delta_j * np.sum(k_j * k, 1)[:, None]
-                    delta = beta[:, None] * (v - alpha[:, None] * u_k)
+                    delta = v if rule == "plain" else beta[:, None] * (v - alpha[:, None] * u_k)
                     o_t = alpha[:, None] * u_q + delta * np.sum(k * q, 1)[:, None]
                 else:
                     def project(x):
@@ -235,7 +246,7 @@ def beam_decode_replay(S0, steps, *, requests=None, heads=None):
                             acc += delta_j * np.sum(k_j * y, 1)[:, None]
                             y = a_j * y
                         return acc + y @ S_ctx
-                    delta = beta[:, None] * (v - project(k))
+                    delta = v if rule == "plain" else beta[:, None] * (v - project(k))
                     o_t = project(q) + delta * np.sum(k * q, 1)[:, None]
                 o[r, :, h] = o_t
                 d[r, :, h] = delta
@@ -248,7 +259,7 @@ def beam_decode_replay(S0, steps, *, requests=None, heads=None):
 # independent sequences, token by token (DeltaLog reference)
 # --------------------------------------------------------------------------
 
-def sequence_decode(S0, tokens, merge_every, *, pairs=None):
+def sequence_decode(S0, tokens, merge_every, *, pairs=None, rule="delta"):
     """Eager decoding of independent sequences.
 
     S0: FP32 [R, H, d_k, d_v]; tokens: dict of arrays with a leading token axis
@@ -272,7 +283,7 @@ def sequence_decode(S0, tokens, merge_every, *, pairs=None):
         v = bf16_to_f64(tokens["v"][i][rs, hs])
         alpha = np.asarray(tokens["alpha"][i][rs, hs], dtype=np.float64)
         beta = np.asarray(tokens["beta"][i][rs, hs], dtype=np.float64)
-        S, delta = transition(S, k, v, alpha, beta)
+        S, delta = transition(S, k, v, alpha, beta, rule)
         o.append(readout(S, q))
         d.append(delta)
         if (i + 1) % merge_every == 0:

@@ -282,6 +282,94 @@ def pin_bruteforce_tiny():
         assert rel(S[0, 1], Sx) < 1e-12
 
 
+# ------------------------------------------------ plain update (RWKV6 row)
+
+def _plain_unrolled_state(inp, t, r, b, h):
+    """S_t = D(a_t)...D(a_0) S0 + sum_j D(a_t)...D(a_{j+1}) k_j v_j^T, written
+    out with dense diagonal matrices from the raw inputs (DeltaLog Table 1,
+    RWKV6 row: transform D(lambda_t) S_{t-1}, update pair (k_t, v_t))."""
+    S0 = inp["S0"][r, h].astype(np.float64)
+    slots = _chain_slots(inp, t, r, b)
+    D = [np.diag(inp["steps"][j]["alpha"][r, s, h].astype(np.float64)) for j, s in enumerate(slots)]
+    KV = [np.outer(f64(inp["steps"][j]["k"][r, s, h]), f64(inp["steps"][j]["v"][r, s, h]))
+          for j, s in enumerate(slots)]
+    total = np.eye(S0.shape[0])
+    for Dj in D:
+        total = Dj @ total
+    S = total @ S0
+    for j in range(len(D)):
+        tail = np.eye(S0.shape[0])
+        for Di in D[j + 1:]:
+            tail = Di @ tail
+        S = S + tail @ KV[j]
+    return S
+
+
+def pin_plain_unrolled_closed_form():
+    inp = small(channel=True, seed=71)
+    ref = O.beam_decode(inp["S0"], inp["steps"], rule="plain")
+    R, H = inp["S0"].shape[:2]
+    for t in range(len(inp["steps"])):
+        pairs = [(r, b) for r in range(R) for b in (0, 2, 4)]
+        states = O.beam_states(inp["S0"], inp["steps"], t, pairs, rule="plain")
+        for i, (r, b) in enumerate(pairs):
+            for h in range(H):
+                Sx = _plain_unrolled_state(inp, t, r, b, h)
+                assert rel(states[i, h], Sx) < 1e-12
+                q = f64(inp["steps"][t]["q"][r, b, h])
+                assert rel(ref["o"][t][r, b, h], q @ Sx) < 1e-12
+                # the update vector is the token's own v
+                assert np.array_equal(ref["delta"][t][r, b, h], f64(inp["steps"][t]["v"][r, b, h]))
+
+
+def pin_plain_replay_equals_eager():
+    for channel in (True, False):
+        inp = small(channel=channel, seed=73)
+        a = O.beam_decode(inp["S0"], inp["steps"], rule="plain")
+        b = O.beam_decode_replay(inp["S0"], inp["steps"], rule="plain")
+        for t in range(len(inp["steps"])):
+            assert rel(b["o"][t], a["o"][t]) < 1e-12
+            assert rel(b["delta"][t], a["delta"][t]) < 1e-12
+
+
+def pin_plain_linear_retrieval():
+    """Unit decays, zero S0, orthonormal keys: plain linear attention, so a
+    query equal to an earlier key returns that step's v exactly."""
+    inp = _basis_inputs(True)
+    ref = O.beam_decode(inp["S0"], inp["steps"], rule="plain")
+    R, H = inp["S0"].shape[:2]
+    for t, st in enumerate(inp["steps"]):
+        for r, b, h in itertools.product(range(R), range(st["q"].shape[1]), range(H)):
+            j = t // 2
+            slot = _chain_slots(inp, t, r, b)[j]
+            assert np.array_equal(ref["o"][t][r, b, h], f64(inp["steps"][j]["v"][r, slot, h]))
+
+
+def pin_plain_sequence_equals_single_beam():
+    R, H, dk, dv, M = 3, 2, 8, 6, 4
+    seq = synth.make_sequence_inputs(R=R, H=H, dk=dk, dv=dv, T=M, s0_std=0.3, seed=75, channel_decay=True)
+    ref = O.sequence_decode(seq["S0"], seq["tokens"], M, rule="plain")
+    steps = []
+    for i in range(M):
+        st = {n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")}
+        if i:
+            st["parent"] = np.zeros((R, 1), np.int32)
+        steps.append(st)
+    beam = O.beam_decode(seq["S0"], steps, rule="plain")
+    for i in range(M):
+        assert rel(ref["o"][i], beam["o"][i][:, 0].reshape(R * H, dv)) < 1e-14
+    S = O.beam_states(seq["S0"], steps, M - 1, [(r, 0) for r in range(R)], rule="plain")
+    assert rel(ref["bases"][0], S.reshape(R * H, dk, dv)) < 1e-14
+
+
+def pin_plain_differs_from_delta():
+    """The two update rules give different states on the same inputs."""
+    inp = small(channel=True, seed=77)
+    a = O.beam_decode(inp["S0"], inp["steps"], rule="plain")
+    b = O.beam_decode(inp["S0"], inp["steps"])
+    assert rel(a["o"][2], b["o"][2]) > 1e-3
+
+
 ALL_PINS = {
     "hand_worked": pin_hand_worked,
     "ancestry_walk": pin_ancestry_walk,
@@ -299,4 +387,9 @@ ALL_PINS = {
     "replay_channel": lambda: pin_replay_equals_eager(True),
     "kda_uniform_scalar": pin_kda_uniform_equals_scalar,
     "sequence_single_beam": pin_sequence_equals_single_beam,
+    "plain_unrolled": pin_plain_unrolled_closed_form,
+    "plain_replay": pin_plain_replay_equals_eager,
+    "plain_linear_retrieval": pin_plain_linear_retrieval,
+    "plain_sequence_single_beam": pin_plain_sequence_equals_single_beam,
+    "plain_differs_from_delta": pin_plain_differs_from_delta,
 }

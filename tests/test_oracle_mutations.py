@@ -9,14 +9,20 @@ import pytest
 import oracle.gdn_oracle as O
 import pins
 
+_transition = O.transition  # the oracle's own, for the rule a mutant leaves alone
 
-def _sign(S, k, v, alpha, beta):
+
+def _sign(S, k, v, alpha, beta, rule="delta"):
+    if rule != "delta":
+        return _transition(S, k, v, alpha, beta, rule)
     S_dec = O.decay(S, alpha)
     delta = beta[:, None] * (v + O.readout(S_dec, k))
     return S_dec + k[:, :, None] * delta[:, None, :], delta
 
 
-def _transposed(S, k, v, alpha, beta):
+def _transposed(S, k, v, alpha, beta, rule="delta"):
+    if rule != "delta":
+        return _transition(S, k, v, alpha, beta, rule)
     S_dec = O.decay(S, alpha)
     if S.shape[1] != S.shape[2]:
         raise ValueError("transposed read-out only type-checks for square states")
@@ -24,18 +30,24 @@ def _transposed(S, k, v, alpha, beta):
     return S_dec + k[:, :, None] * delta[:, None, :], delta
 
 
-def _undecayed_prediction(S, k, v, alpha, beta):
+def _undecayed_prediction(S, k, v, alpha, beta, rule="delta"):
+    if rule != "delta":
+        return _transition(S, k, v, alpha, beta, rule)
     delta = beta[:, None] * (v - O.readout(S, k))
     return O.decay(S, alpha) + k[:, :, None] * delta[:, None, :], delta
 
 
-def _no_beta(S, k, v, alpha, beta):
+def _no_beta(S, k, v, alpha, beta, rule="delta"):
+    if rule != "delta":
+        return _transition(S, k, v, alpha, beta, rule)
     S_dec = O.decay(S, alpha)
     delta = v - O.readout(S_dec, k)
     return S_dec + k[:, :, None] * delta[:, None, :], delta
 
 
-def _decay_after_write(S, k, v, alpha, beta):
+def _decay_after_write(S, k, v, alpha, beta, rule="delta"):
+    if rule != "delta":
+        return _transition(S, k, v, alpha, beta, rule)
     delta = beta[:, None] * (v - O.readout(S, k))
     return O.decay(S + k[:, :, None] * delta[:, None, :], alpha), delta
 
@@ -54,16 +66,33 @@ def _no_scalar_decay(S, alpha):
     return alpha[:, :, None] * S
 
 
-def _readout_before_write(S0, steps, anc, t, r, h, beams):
+def _readout_before_write(S0, steps, anc, t, r, h, beams, rule="delta"):
     beams = np.asarray(beams, dtype=np.int64)
     S = np.repeat(S0[r, h][None].astype(np.float64), len(beams), axis=0)
     for j in range(t):
         slot = anc[t][r, beams, j]
         _, k, v, alpha, beta = O._token(steps[j], r, slot, h)
-        S, _ = O.transition(S, k, v, alpha, beta)
+        S, _ = O.transition(S, k, v, alpha, beta, rule)
     q, k, v, alpha, beta = O._token(steps[t], r, beams, h)
-    S_new, delta = O.transition(S, k, v, alpha, beta)
+    S_new, delta = O.transition(S, k, v, alpha, beta, rule)
     return S, delta, q
+
+
+def _plain_scaled_by_beta(S, k, v, alpha, beta, rule="delta"):
+    if rule != "plain":
+        return _transition(S, k, v, alpha, beta, rule)
+    delta = beta[:, None] * v
+    return O.decay(S, alpha) + k[:, :, None] * delta[:, None, :], delta
+
+
+def _plain_decay_after_write(S, k, v, alpha, beta, rule="delta"):
+    if rule != "plain":
+        return _transition(S, k, v, alpha, beta, rule)
+    return O.decay(S + k[:, :, None] * v[:, None, :], alpha), v
+
+
+def _plain_with_delta_correction(S, k, v, alpha, beta, rule="delta"):
+    return _transition(S, k, v, alpha, beta, "delta")
 
 
 def _anc_child_index(parents, R, W0):
@@ -105,6 +134,9 @@ MUTANTS = {
     "readout_before_write": ("_eager_chain", _readout_before_write),
     "ancestry_child_index": ("ancestry", _anc_child_index),
     "ancestry_depth_order": ("ancestry", _anc_depth_swapped),
+    "plain_update_scaled_by_beta": ("transition", _plain_scaled_by_beta),
+    "plain_decay_after_write": ("transition", _plain_decay_after_write),
+    "plain_with_delta_correction": ("transition", _plain_with_delta_correction),
 }
 
 
