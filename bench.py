@@ -166,7 +166,7 @@ def sequence_row(B, torch, dev, stream, wl):
     (log length token mod M) and the merge after every M tokens."""
     seq = wl.inputs()
     store = B.Store(wl.R, 1, wl.H, wl.dk, wl.dv, wl.M, channel_decay=wl.channel_decay,
-                    S=torch.from_numpy(seq["S0"]).to(dev))
+                    S=torch.from_numpy(seq["S0"]).to(dev), plain_update=wl.plain_update)
     toks = [B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")}, dev)
             for i in range(wl.T)]
     zero = torch.zeros(wl.R, 1, dtype=torch.int32, device=dev)
@@ -189,7 +189,7 @@ def sequence_row(B, torch, dev, stream, wl):
 
     # the same tokens with the merge fused into the decode that fills the log
     fstore = B.Store(wl.R, 1, wl.H, wl.dk, wl.dv, wl.M, channel_decay=wl.channel_decay,
-                     S=torch.from_numpy(seq["S0"]).to(dev))
+                     S=torch.from_numpy(seq["S0"]).to(dev), plain_update=wl.plain_update)
 
     def fused(i):
         d = toks[i]
@@ -205,7 +205,7 @@ def sequence_row(B, torch, dev, stream, wl):
     # one merge cycle of the fused path captured in a HIP graph and replayed
     # (the replays keep decoding the cycle's M tokens on the evolving base)
     gstore = B.Store(wl.R, 1, wl.H, wl.dk, wl.dv, wl.M, channel_decay=wl.channel_decay,
-                     S=torch.from_numpy(seq["S0"]).to(dev))
+                     S=torch.from_numpy(seq["S0"]).to(dev), plain_update=wl.plain_update)
     gout = torch.empty_like(o)
 
     def gcycle():
@@ -409,6 +409,7 @@ def main():
             "channel_decay_beam_decode": beam_row(B, torch, dev, stream, configs.KDA, reps),
             "bounded_log_decode_and_merge": sequence_row(B, torch, dev, stream, configs.DELTALOG),
             "bounded_log_merge_interval": merge_interval_row(B, torch, dev, stream, configs.DELTALOG, (4, 8, 16)),
+            "rwkv6_bounded_log": sequence_row(B, torch, dev, stream, configs.RWKV6),
             "materialize": materialize_row(B, torch, dev, stream, WORKLOAD, 64, reps),
         }
     print(json.dumps(line), flush=True)

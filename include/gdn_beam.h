@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GDN_BEAM_ABI_VERSION 2
+#define GDN_BEAM_ABI_VERSION 3
 
 /* status codes */
 #define GDN_OK 0
@@ -54,14 +54,21 @@ extern "C" {
 #define GDN_EUNSUPPORTED (-2) /* (d_k, d_v) pair or decay kind not built in */
 #define GDN_EHIP (-3)         /* the HIP runtime rejected a kernel launch */
 
-/* decay kinds */
+/* decay kinds (and update rules) */
 #define GDN_DECAY_SCALAR 0  /* GDN: one alpha per (beam, head, step)      */
 #define GDN_DECAY_CHANNEL 1 /* KDA: one alpha per key channel (A = d_k)   */
+/* RWKV6 row of DeltaLog Table 1: one alpha per key channel (A = d_k) and the
+ * update pair (k_t, v_t), no delta correction: S_t = diag(a_t) S_{t-1} +
+ * k_t v_t^T, so the record's update vector is delta_t = v_t and beta is
+ * ignored.  Bounded-log (independent sequence, W_max == 1) decoding, merge
+ * and materialisation only; gdn_beam_decode_step with W_max > 1 returns
+ * GDN_EUNSUPPORTED. */
+#define GDN_DECAY_CHANNEL_PLAIN 2
 
 /* largest L_max (records per chain / log capacity) */
 #define GDN_MAX_STEPS 16
 
-/* Geometry of a store.  A = 1 for GDN_DECAY_SCALAR, A = dk for _CHANNEL.
+/* Geometry of a store.  A = 1 for GDN_DECAY_SCALAR, A = dk otherwise.
  * Built-in (dk, dv): (16,16) (32,32) (64,64) (128,128). */
 typedef struct gdn_shape {
   int32_t R;          /* requests (W_max == 1: independent sequences)  >= 1 */
@@ -70,7 +77,7 @@ typedef struct gdn_shape {
   int32_t dk;         /* key head dim                                        */
   int32_t dv;         /* value head dim                                      */
   int32_t L_max;      /* steps held (1 .. GDN_MAX_STEPS)                     */
-  int32_t decay_kind; /* GDN_DECAY_SCALAR or GDN_DECAY_CHANNEL               */
+  int32_t decay_kind; /* GDN_DECAY_SCALAR, _CHANNEL or _CHANNEL_PLAIN        */
 } gdn_shape;
 
 /* The record / ancestry store (caller-allocated device memory). */

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG, "libgdnbeam.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "gdn_beam.h")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP = 0, -1, -2, -3
-GDN_DECAY_SCALAR, GDN_DECAY_CHANNEL = 0, 1
+GDN_DECAY_SCALAR, GDN_DECAY_CHANNEL, GDN_DECAY_CHANNEL_PLAIN = 0, 1, 2
 GDN_MAX_STEPS = 16
 
 
@@ -107,9 +107,13 @@ class Store:
     rec_alpha [L,R,W,H,A] FP32, anc [L,R,W,L] int32.
     """
 
-    def __init__(self, R, W_max, H, dk, dv, L_max, channel_decay=False, device="cuda", S=None):
+    def __init__(self, R, W_max, H, dk, dv, L_max, channel_decay=False, device="cuda", S=None,
+                 plain_update=False):
         self.R, self.W_max, self.H, self.dk, self.dv, self.L_max = R, W_max, H, dk, dv, L_max
+        if plain_update and not channel_decay:
+            raise ValueError("the plain (RWKV6) update rule comes with per-channel decay")
         self.channel_decay = bool(channel_decay)
+        self.plain_update = bool(plain_update)
         self.A = dk if channel_decay else 1
         f32 = dict(dtype=torch.float32, device=device)
         if S is None:
@@ -121,8 +125,8 @@ class Store:
         self.rec_k = torch.zeros(L_max, R, W_max, H, dk, dtype=torch.bfloat16, device=device)
         self.rec_alpha = torch.zeros(L_max, R, W_max, H, self.A, **f32)
         self.anc = torch.zeros(L_max, R, W_max, L_max, dtype=torch.int32, device=device)
-        self.shape = GdnShape(R, W_max, H, dk, dv, L_max,
-                              GDN_DECAY_CHANNEL if channel_decay else GDN_DECAY_SCALAR)
+        kind = GDN_DECAY_CHANNEL_PLAIN if plain_update else (GDN_DECAY_CHANNEL if channel_decay else GDN_DECAY_SCALAR)
+        self.shape = GdnShape(R, W_max, H, dk, dv, L_max, kind)
         self.cstore = GdnStore(_ptr(self.S), _ptr(self.rec_delta), _ptr(self.rec_k),
                                _ptr(self.rec_alpha), _ptr(self.anc))
 

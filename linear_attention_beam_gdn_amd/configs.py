@@ -1,9 +1,9 @@
-"""The five synthetic workloads the path is checked and measured on.
+"""The synthetic workloads the path is checked and measured on.
 
 Shapes follow the OneLA operator suite (§4.1: R requests, W beams, T decode
 steps, H heads, K = d_k, V = d_v) and the DeltaLog recurrent-kernel table
-(Table 3: H/d_k/d_v = 32/128/128, FP32 state, BF16 K / FP32 U log, M = 8).
-Seeds: the tiny workload uses seed 0; the others use their index.
+(Table 3: H/d_k/d_v = 32/128/128, FP32 state; GDN log with M = 8, RWKV6 log
+with M = 4).  Seeds: the tiny workload uses seed 0; the others use their index.
 """
 
 from __future__ import annotations
@@ -53,6 +53,11 @@ class SequenceWorkload:
     s0_std: float
     seed: int
     channel_decay: bool = False
+    plain_update: bool = False  # the RWKV6 update pair (k_t, v_t); implies channel decay
+
+    @property
+    def rule(self) -> str:
+        return "plain" if self.plain_update else "delta"
 
     @property
     def sequence_steps(self) -> int:
@@ -76,5 +81,8 @@ DELTALOG = SequenceWorkload("deltalog_bounded_log", R=128, H=32, dk=128, dv=128,
 KDA = BeamWorkload("kda_channel_decay_beam", R=16, H=32, dk=128, dv=128, W=256, L=4,
                    s0_std=0.05, seed=4, parents="topk", channel_decay=True)
 
-ALL = (TINY, SINGLE, LARGE, DELTALOG, KDA)
+RWKV6 = SequenceWorkload("rwkv6_bounded_log", R=128, H=32, dk=128, dv=128, T=64, M=4,
+                         s0_std=0.05, seed=5, channel_decay=True, plain_update=True)
+
+ALL = (TINY, SINGLE, LARGE, DELTALOG, KDA, RWKV6)
 BY_NAME = {w.name: w for w in ALL}

@@ -23,7 +23,9 @@ int check_shape(const gdn_shape* s) {
   if (s == nullptr) return GDN_EINVAL;
   if (s->R < 1 || s->W_max < 1 || s->H < 1 || s->L_max < 1 || s->L_max > GDN_MAX_STEPS)
     return GDN_EINVAL;
-  if (s->decay_kind != GDN_DECAY_SCALAR && s->decay_kind != GDN_DECAY_CHANNEL) return GDN_EUNSUPPORTED;
+  if (s->decay_kind != GDN_DECAY_SCALAR && s->decay_kind != GDN_DECAY_CHANNEL &&
+      s->decay_kind != GDN_DECAY_CHANNEL_PLAIN)
+    return GDN_EUNSUPPORTED;
   if (!gdn::dims_supported(s->dk, s->dv)) return GDN_EUNSUPPORTED;
   // element counts of the largest arrays must stay far from 2^63
   const double recs = (double)s->L_max * s->R * s->W_max * s->H * (s->dk > s->dv ? s->dk : s->dv);
@@ -63,6 +65,7 @@ int gdn_beam_decode_step(const gdn_shape* shape, const gdn_store* store, int32_t
   int rc = check_shape(shape);
   if (rc != GDN_OK) return rc;
   if ((rc = check_store(store)) != GDN_OK) return rc;
+  if (shape->decay_kind == GDN_DECAY_CHANNEL_PLAIN && shape->W_max != 1) return GDN_EUNSUPPORTED;
   if (t < 0 || t >= shape->L_max) return GDN_EINVAL;
   if (W_t < 1 || W_t > shape->W_max) return GDN_EINVAL;
   if (t > 0 && !aligned(parent, 4)) return GDN_EINVAL;

@@ -113,7 +113,7 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, const int32_t* rb, i
 
 int launch_fold(const gdn_shape& sh, const gdn_store& st, int t, const int32_t* rb, int beam, int n,
                 const float* src, float* dst, bool dst_per_item, hipStream_t stream) {
-  const bool ch = sh.decay_kind == GDN_DECAY_CHANNEL;
+  const bool ch = sh.decay_kind != GDN_DECAY_SCALAR;  // the fold is the same for both channel rules
 #define GDN_CASE(DK_, DV_)                                                           \
   if (sh.dk == DK_ && sh.dv == DV_)                                                  \
     return ch ? launch<DK_, DV_, true>(sh, st, t, rb, beam, n, src, dst, dst_per_item, stream) \

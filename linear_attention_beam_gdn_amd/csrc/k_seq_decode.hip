@@ -47,8 +47,11 @@ struct SeqGeom {
   static constexpr int NWV = (NT + 63) / 64;             // waves
 };
 
-template <int DK, int DV, bool CH, bool MRG>
+// PLAIN: the RWKV6 update pair (k_t, v_t) (channel decay, no delta
+// correction): delta_t = v_t, and no projection of k_t is formed.
+template <int DK, int DV, bool CH, bool MRG, bool PLAIN>
 __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a) {
+  static_assert(CH || !PLAIN, "the plain update rule comes with channel decay");
   using G = SeqGeom<DK, DV>;
   constexpr int A = CH ? DK : 1;
   const int tid = threadIdx.x;
@@ -82,7 +85,7 @@ __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a)
       for (int j = 0; j < t; ++j) cq *= a.rec_alpha[rec_at(j) * A + kk];
     }
     probe_q[kk] = cq * bf16_at(a.q[tok * DK + kk]);
-    probe_k[kk] = cq * bf16_at(a.k[tok * DK + kk]);
+    if constexpr (!PLAIN) probe_k[kk] = cq * bf16_at(a.k[tok * DK + kk]);
   }
   // dot products of the replay: wave wv takes log entries j = wv, wv + NWV, ..
   // (entry t is k_t . q_t); channel decay weights them by prod_{i=j+1..t} a_i
@@ -99,7 +102,7 @@ __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a)
           for (int i = j + 1; i < t; ++i) y *= a.rec_alpha[rec_at(i) * A + kk];
         }
         pq += y * qv;
-        pk += y * bf16_at(a.k[tok * DK + kk]);
+        if constexpr (!PLAIN) pk += y * bf16_at(a.k[tok * DK + kk]);
       }
     }
     pq = wave_sum(pq);
@@ -120,10 +123,10 @@ __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a)
   for (int i = 0; i < G::RPG; ++i) {
     const int row = rg * G::RPG + i;
     pq += st[i] * probe_q[row];
-    pk += st[i] * probe_k[row];
+    if constexpr (!PLAIN) pk += st[i] * probe_k[row];
   }
   *reinterpret_cast<f32x4*>(&red_q[rg][c4 * 4]) = pq;
-  *reinterpret_cast<f32x4*>(&red_k[rg][c4 * 4]) = pk;
+  if constexpr (!PLAIN) *reinterpret_cast<f32x4*>(&red_k[rg][c4 * 4]) = pk;
   __syncthreads();
 
   const float at = CH ? 1.f : a.alpha[tok];
@@ -134,7 +137,7 @@ __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a)
 #pragma unroll 8
     for (int g = 0; g < G::NRG; ++g) {
       uq += red_q[g][col];
-      uk += red_k[g][col];
+      if constexpr (!PLAIN) uk += red_k[g][col];
     }
     for (int j = 0; j < t; ++j) {
       const float dj = a.rec_delta[rec_at(j) * DV + col];
@@ -144,11 +147,11 @@ __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a)
         uk = aj * uk + dj * dots_k[j];
       } else {
         uq += dj * dots_q[j];
-        uk += dj * dots_k[j];
+        if constexpr (!PLAIN) uk += dj * dots_k[j];
       }
     }
     const float vv = bf16_at(a.v[tok * DV + col]);
-    const float d = bt * (vv - at * uk);
+    const float d = PLAIN ? vv : bt * (vv - at * uk);
     a.o[tok * DV + col] = at * uq + d * dot_qk;
     a.rec_delta[rec_t * DV + col] = d;
     if constexpr (MRG) d_new[col] = d;
@@ -186,7 +189,7 @@ __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a)
   }
 }
 
-template <int DK, int DV, bool CH, bool MRG>
+template <int DK, int DV, bool CH, bool MRG, bool PLAIN = false>
 int launch(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io, hipStream_t stream) {
   SeqArgs a;
   a.S = st.S;
@@ -207,8 +210,8 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io, hi
   a.t = t;
   const long grid = (long)sh.R * sh.H;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
-  hipLaunchKernelGGL((k_seq_decode<DK, DV, CH, MRG>), dim3((unsigned)grid), dim3(SeqGeom<DK, DV>::NT), 0,
-                     stream, a);
+  hipLaunchKernelGGL((k_seq_decode<DK, DV, CH, MRG, PLAIN>), dim3((unsigned)grid), dim3(SeqGeom<DK, DV>::NT),
+                     0, stream, a);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
@@ -217,8 +220,12 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io, hi
 int launch_seq_decode(const gdn_shape& sh, const gdn_store& st, int t, bool merge, const StepIO& io,
                       hipStream_t stream) {
   const bool ch = sh.decay_kind == GDN_DECAY_CHANNEL;
+  const bool plain = sh.decay_kind == GDN_DECAY_CHANNEL_PLAIN;
 #define GDN_CASE(DK_, DV_)                                                                         \
   if (sh.dk == DK_ && sh.dv == DV_) {                                                              \
+    if (plain)                                                                                     \
+      return merge ? launch<DK_, DV_, true, true, true>(sh, st, t, io, stream)                     \
+                   : launch<DK_, DV_, true, false, true>(sh, st, t, io, stream);                   \
     if (merge)                                                                                     \
       return ch ? launch<DK_, DV_, true, true>(sh, st, t, io, stream)                              \
                 : launch<DK_, DV_, false, true>(sh, st, t, io, stream);                            \

@@ -49,7 +49,7 @@ def test_exports_every_header_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gdn_abi_version() == 2
+    assert L.gdn_abi_version() == 3
     for s in (B.GDN_OK, B.GDN_EINVAL, B.GDN_EUNSUPPORTED, B.GDN_EHIP, 12345):
         assert isinstance(B.status_string(s), str) and B.status_string(s)
 
@@ -67,7 +67,8 @@ def test_decode_validation(L):
     assert decode(L, sh=shape(L_max=B.GDN_MAX_STEPS + 1)) == E
     assert decode(L, sh=shape(dk=96, dv=96)) == U
     assert decode(L, sh=shape(dk=128, dv=64)) == U
-    assert decode(L, sh=shape(decay_kind=2)) == U
+    assert decode(L, sh=shape(decay_kind=2)) == U  # the plain (RWKV6) rule: sequences only
+    assert decode(L, sh=shape(decay_kind=3)) == U
     assert decode(L, t=-1) == E
     assert decode(L, t=4) == E
     assert decode(L, W_t=0) == E

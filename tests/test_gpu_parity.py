@@ -56,16 +56,17 @@ def test_kda_workload_sampled():
     check_beam(configs.KDA.inputs(), True, requests=[0, 15], heads=[0, 31], label="kda")
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_deltalog_workload(fused):
-    w = configs.DELTALOG
+@pytest.mark.parametrize("wname,fused", [("DELTALOG", False), ("DELTALOG", True), ("RWKV6", True)])
+def test_deltalog_workload(wname, fused):
+    w = getattr(configs, wname)
     seq = w.inputs()
     pairs = [(0, 0), (0, 31), (17, 5), (64, 16), (101, 30), (127, 0), (127, 31), (90, 9)]
     rs = np.array([p[0] for p in pairs])
     hs = np.array([p[1] for p in pairs])
-    log(f"[parity] deltalog R={w.R} H={w.H} T={w.T} M={w.M} fused merge={fused}")
-    ref = O.sequence_decode(seq["S0"], seq["tokens"], w.M, pairs=pairs)
-    store = B.Store(w.R, 1, w.H, w.dk, w.dv, w.M, S=torch.from_numpy(seq["S0"]).cuda())
+    log(f"[parity] {w.name} R={w.R} H={w.H} T={w.T} M={w.M} fused merge={fused}")
+    ref = O.sequence_decode(seq["S0"], seq["tokens"], w.M, pairs=pairs, rule=w.rule)
+    store = B.Store(w.R, 1, w.H, w.dk, w.dv, w.M, channel_decay=w.channel_decay, plain_update=w.plain_update,
+                    S=torch.from_numpy(seq["S0"]).cuda())
     zero = torch.zeros(w.R, 1, dtype=torch.int32, device="cuda")
     rs_d = torch.from_numpy(rs).cuda()
     hs_d = torch.from_numpy(hs).cuda()
@@ -100,13 +101,14 @@ def test_ragged_widths(dims, channel):
     check_beam(inp, channel, label=f"ragged dk={dk} ch={channel}")
 
 
-@pytest.mark.parametrize("channel", [False, True])
-def test_sequences_small(channel):
+@pytest.mark.parametrize("kind", ["scalar", "channel", "plain"])
+def test_sequences_small(kind):
+    channel, plain = kind != "scalar", kind == "plain"
     R, H, dk, dv, T, M = 5, 3, 64, 64, 12, 4
     seq = synth.make_sequence_inputs(R=R, H=H, dk=dk, dv=dv, T=T, s0_std=0.1, seed=7,
                                      channel_decay=channel)
-    ref = O.sequence_decode(seq["S0"], seq["tokens"], M)
-    store = B.Store(R, 1, H, dk, dv, M, channel_decay=channel,
+    ref = O.sequence_decode(seq["S0"], seq["tokens"], M, rule="plain" if plain else "delta")
+    store = B.Store(R, 1, H, dk, dv, M, channel_decay=channel, plain_update=plain,
                     S=torch.from_numpy(seq["S0"]).cuda())
     zero = torch.zeros(R, 1, dtype=torch.int32, device="cuda")
     for i in range(T):
@@ -120,17 +122,18 @@ def test_sequences_small(channel):
             assert rel_states(S, ref["bases"][i // M][:, None]) <= TOL
 
 
-@pytest.mark.parametrize("channel", [False, True])
-def test_decode_merge_step(channel):
+@pytest.mark.parametrize("kind", ["scalar", "channel", "plain"])
+def test_decode_merge_step(kind):
     """The merge path fused into the decode that fills the log: matches the
     oracle's merged bases and outputs, and equals decode-then-merge exactly."""
+    channel, plain = kind != "scalar", kind == "plain"
     R, H, dk, dv, T, M = 5, 3, 64, 64, 12, 4
     seq = synth.make_sequence_inputs(R=R, H=H, dk=dk, dv=dv, T=T, s0_std=0.1, seed=11,
                                      channel_decay=channel)
-    ref = O.sequence_decode(seq["S0"], seq["tokens"], M)
+    ref = O.sequence_decode(seq["S0"], seq["tokens"], M, rule="plain" if plain else "delta")
     S0 = torch.from_numpy(seq["S0"]).cuda()
-    fused = B.Store(R, 1, H, dk, dv, M, channel_decay=channel, S=S0.clone())
-    split = B.Store(R, 1, H, dk, dv, M, channel_decay=channel, S=S0.clone())
+    fused = B.Store(R, 1, H, dk, dv, M, channel_decay=channel, plain_update=plain, S=S0.clone())
+    split = B.Store(R, 1, H, dk, dv, M, channel_decay=channel, plain_update=plain, S=S0.clone())
     zero = torch.zeros(R, 1, dtype=torch.int32, device="cuda")
     for i in range(T):
         t = i % M
@@ -150,7 +153,7 @@ def test_decode_merge_step(channel):
             assert torch.equal(fused.S, split.S), i
             S = fused.S.cpu().numpy().reshape(R * H, 1, dk, dv)
             assert rel_states(S, ref["bases"][i // M][:, None]) <= TOL
-    log(f"[parity] decode+merge fused ch={channel}: equal to decode-then-merge")
+    log(f"[parity] decode+merge fused {kind}: equal to decode-then-merge")
 
 
 # ---------------------------------------------------------------- edge cases
