@@ -289,6 +289,8 @@ def main():
     ap.add_argument("--cpu-workers", type=int, default=0)
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other path rows (channel decay, bounded log, materialise)")
+    ap.add_argument("--rows", default="",
+                    help="comma-separated subset of the rows to run (default: all of them)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the warm-up, run a plain device copy of this many MiB three times "
                          "(a known-size reference for HBM byte counters)")
@@ -404,14 +406,20 @@ def main():
     }
     if not args.no_rows:
         reps = max(3, min(args.steps, 10))
-        line["rows"] = {
-            "single_request_beam_decode": beam_row(B, torch, dev, stream, configs.SINGLE, reps),
-            "channel_decay_beam_decode": beam_row(B, torch, dev, stream, configs.KDA, reps),
-            "bounded_log_decode_and_merge": sequence_row(B, torch, dev, stream, configs.DELTALOG),
-            "bounded_log_merge_interval": merge_interval_row(B, torch, dev, stream, configs.DELTALOG, (4, 8, 16)),
-            "rwkv6_bounded_log": sequence_row(B, torch, dev, stream, configs.RWKV6),
-            "materialize": materialize_row(B, torch, dev, stream, WORKLOAD, 64, reps),
+        rows = {
+            "single_request_beam_decode": lambda: beam_row(B, torch, dev, stream, configs.SINGLE, reps),
+            "channel_decay_beam_decode": lambda: beam_row(B, torch, dev, stream, configs.KDA, reps),
+            "bounded_log_decode_and_merge": lambda: sequence_row(B, torch, dev, stream, configs.DELTALOG),
+            "bounded_log_merge_interval": lambda: merge_interval_row(B, torch, dev, stream, configs.DELTALOG,
+                                                                     (4, 8, 16)),
+            "rwkv6_bounded_log": lambda: sequence_row(B, torch, dev, stream, configs.RWKV6),
+            "materialize": lambda: materialize_row(B, torch, dev, stream, WORKLOAD, 64, reps),
         }
+        pick = [r for r in args.rows.split(",") if r] or list(rows)
+        unknown = [r for r in pick if r not in rows]
+        if unknown:
+            sys.exit(f"unknown rows {unknown}; choose from {sorted(rows)}")
+        line["rows"] = {name: rows[name]() for name in pick}
     print(json.dumps(line), flush=True)
 
 
