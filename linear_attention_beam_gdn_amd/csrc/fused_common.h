@@ -82,7 +82,8 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // h_t(b, j) = h_{T-1}(parent, j)), orders the beams depth-first in the beam
 // tree when the chunk holds the whole step (a counting sort of the beams by
 // their parent's position in the previous step's order), and writes
-//   s_tab[position]  = {beam, slot_0, slot_1, slot_2}, s_slot3[position] = slot_3,
+//   s_tab[position]  = {beam, slot_0, slot_1, slot_2},
+//   s_slot_hi[(j - 3) * kMaxChunkF + position] = slot_j for 3 <= j < T,
 //   anc row T of every beam (h == 0 workgroups), with the beam's position in
 //   the unused last entry for the next step.
 // The order only decides which lanes compute a beam, never its result.
@@ -95,7 +96,7 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // counts and the staged block and is free for other use afterwards.
 template <int T, class Mid>
 __device__ __forceinline__ void build_schedule(const BeamArgs& a, int r, int h, int b_begin, int nb, int lane,
-                                               int scratch_bytes, uint8_t* scratch, u32x4* s_tab, int* s_slot3,
+                                               int scratch_bytes, uint8_t* scratch, u32x4* s_tab, int* s_slot_hi,
                                                Mid mid) {
   constexpr int TT = T > 0 ? T : 1;
   constexpr int QMAX = kMaxChunkF / 64;
@@ -189,7 +190,8 @@ __device__ __forceinline__ void build_schedule(const BeamArgs& a, int r, int h, 
     if (i < nb) {
       s_tab[pos[qi]] = u32x4{(uint32_t)i, (uint32_t)slot[qi][0], (uint32_t)slot[qi][T > 1 ? 1 : 0],
                              (uint32_t)slot[qi][T > 2 ? 2 : 0]};
-      if constexpr (T > 3) s_slot3[pos[qi]] = slot[qi][3];
+#pragma unroll
+      for (int j = 3; j < T; ++j) s_slot_hi[(j - 3) * kMaxChunkF + pos[qi]] = slot[qi][j];
       if (h == 0) {
         int32_t* crow = a.anc + (((size_t)T * a.R + r) * a.Wm + b_begin + i) * a.L;
 #pragma unroll

@@ -27,7 +27,7 @@ int launch_beam_decode(const gdn_shape& sh, const gdn_store& st, int t, int Wt,
 
 // Scalar-decay beams with (d_k, d_v) in {32, 64, 128} and chains of at most
 // kFusedMaxSteps records: loader/consumer pipeline through LDS.
-constexpr int kFusedMaxSteps = 4;
+constexpr int kFusedMaxSteps = 6;
 bool beam_fused_supported(const gdn_shape& sh, int t);
 int launch_beam_fused(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
                       hipStream_t stream);

@@ -75,7 +75,7 @@ struct FusedGeom {
   static constexpr int OQ = 0, OKK = QB, OV = 2 * QB, OS = 2 * QB + VB, OW = OS + SMB, ORK = OW + WTB;
   static constexpr int BUF = ORK + T * RKB;
   // schedule table: per position {beam, slot_0, slot_1, slot_2}, plus slot_3
-  static constexpr int SLOTB = T > 0 ? kMaxChunkF * 16 + (T > 3 ? kMaxChunkF * 4 : 0) : 0;
+  static constexpr int SLOTB = T > 0 ? kMaxChunkF * 16 + (T > 3 ? (T - 3) * kMaxChunkF * 4 : 0) : 0;
   static constexpr int NBUF0 = (kLdsBytes - SLOTB) / BUF;
   static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
   static_assert(NBUF >= 3, "tile buffers do not fit in LDS");
@@ -91,7 +91,7 @@ struct FusedGeom {
   static constexpr int OPT = 2 * (QB / 1024) + VB / 1024 + NSM + T * (RKB / 1024);
   static_assert(QB % 1024 == 0 && VB % 1024 == 0, "tile arrays must be whole DMA blocks");
   static_assert((2 + T) * 16 <= 128, "too many record depths for the small-value block");
-  static_assert(T <= 4, "the schedule table holds at most four record depths");
+  static_assert(T <= 6, "at most six record depths (the small-value block holds 2 + T groups of 16)");
 };
 
 template <int DK, int DV, int T>
@@ -102,7 +102,7 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   constexpr int TT = T > 0 ? T : 1;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
   u32x4* s_tab = reinterpret_cast<u32x4*>(smem + G::RINGB);                    // [position]
-  int* s_slot3 = reinterpret_cast<int*>(smem + G::RINGB + kMaxChunkF * 16);  // T == 4
+  int* s_slot_hi = reinterpret_cast<int*>(smem + G::RINGB + kMaxChunkF * 16);  // depths 3 .. T-1
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     };
     if (T > 0) {
       if (dw == 0) {
-        build_schedule<T>(a, r, h, b_begin, nb, lane, G::OS0, smem, s_tab, s_slot3,
+        build_schedule<T>(a, r, h, b_begin, nb, lane, G::OS0, smem, s_tab, s_slot_hi,
                           [] { lds_barrier(); });  // Q inside, once its loads have arrived
       } else {
         lds_barrier();  // Q
@@ -153,14 +153,15 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     auto dma_tile = [&](int p) {
       uint8_t* buf = smem + (p % G::NBUF) * G::BUF;
       const int posi = min(p * 16 + (lane & 15), nb - 1);  // positions past the chunk repeat its last
-      int ib = posi, sl[4] = {0, 0, 0, 0};
+      int ib = posi, sl[TT > 3 ? TT : 3] = {};
       if constexpr (T > 0) {
         const u32x4 e = lds_read128_opaque(&s_tab[posi]);
         ib = (int)e[0];
         sl[0] = (int)e[1];
         sl[1] = (int)e[2];
         sl[2] = (int)e[3];
-        if constexpr (T > 3) sl[3] = lds_read_opaque(&s_slot3[posi]);
+#pragma unroll
+        for (int j = 3; j < T; ++j) sl[j] = lds_read_opaque(&s_slot_hi[(j - 3) * kMaxChunkF + posi]);
       }
       const size_t tok = ((size_t)r * a.Wt + b_begin + ib) * a.H + h;
       const uint16_t* qrow = a.q + tok * DK;
@@ -302,7 +303,9 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     if constexpr (T > 0) {
       const int posi = min(p * 16 + c, nb - 1);
       const u32x4 e = s_tab[posi];
-      const int sl[4] = {(int)e[1], (int)e[2], (int)e[3], T > 3 ? s_slot3[posi] : 0};
+      int sl[TT > 3 ? TT : 3] = {(int)e[1], (int)e[2], (int)e[3]};
+#pragma unroll
+      for (int j = 3; j < T; ++j) sl[j] = s_slot_hi[(j - 3) * kMaxChunkF + posi];
 #pragma unroll
       for (int j = 0; j < T; ++j) {
         const size_t rj = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + h;
@@ -439,6 +442,8 @@ int launch_dims(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const S
     case 2: return launch<DK, DV, 2>(sh, st, Wt, io, stream);
     case 3: return launch<DK, DV, 3>(sh, st, Wt, io, stream);
     case 4: return launch<DK, DV, 4>(sh, st, Wt, io, stream);
+    case 5: return launch<DK, DV, 5>(sh, st, Wt, io, stream);
+    case 6: return launch<DK, DV, 6>(sh, st, Wt, io, stream);
     default: return GDN_EUNSUPPORTED;
   }
 }

@@ -73,7 +73,8 @@ struct KdaGeom {
   static constexpr int OQK = 0, OV = QKB, OA = OV + VB, OLO = OA, OS = OA + AB, OW = OS + SMB, ORK = OW + WTB,
                        ORA = ORK + T * RKB;
   static constexpr int BUF = ORA + T * AB;
-  static constexpr int SLOTB = T > 0 ? kMaxChunkF * 16 + (T > 3 ? kMaxChunkF * 4 : 0) : 0;
+  static_assert(T <= 3, "the channel-decay kernel takes at most three record depths");
+  static constexpr int SLOTB = T > 0 ? kMaxChunkF * 16 : 0;
   static constexpr int NBUF0 = (kLdsBytes - SLOTB) / BUF;
   static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
   static_assert(NBUF >= 3, "tile buffers do not fit in LDS");
@@ -155,7 +156,7 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   constexpr int TT = T > 0 ? T : 1;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
   u32x4* s_tab = reinterpret_cast<u32x4*>(smem + G::RINGB);
-  int* s_slot3 = reinterpret_cast<int*>(smem + G::RINGB + kMaxChunkF * 16);
+  int* s_slot_hi = reinterpret_cast<int*>(smem + G::RINGB + kMaxChunkF * 16);  // unused: T <= 3
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -187,7 +188,7 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     };
     if (T > 0) {
       if (dw == 0) {
-        build_schedule<T>(a, r, h, b_begin, nb, lane, G::OS0, smem, s_tab, s_slot3,
+        build_schedule<T>(a, r, h, b_begin, nb, lane, G::OS0, smem, s_tab, s_slot_hi,
                           [] { lds_barrier(); });  // Q inside, once its loads have arrived
       } else {
         lds_barrier();  // Q
@@ -200,14 +201,13 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     auto dma_tile = [&](int p) {
       uint8_t* buf = smem + (p % G::NBUF) * G::BUF;
       const int posi = min(p * G::TB + (lane & 7), nb - 1);  // positions past the chunk repeat its last
-      int ib = posi, sl[4] = {0, 0, 0, 0};
+      int ib = posi, sl[3] = {0, 0, 0};
       if constexpr (T > 0) {
         const u32x4 e = lds_read128_opaque(&s_tab[posi]);
         ib = (int)e[0];
         sl[0] = (int)e[1];
         sl[1] = (int)e[2];
         sl[2] = (int)e[3];
-        if constexpr (T > 3) sl[3] = lds_read_opaque(&s_slot3[posi]);
       }
       const size_t tok = ((size_t)r * a.Wt + b_begin + ib) * a.H + h;
       // q|k: rows 0-7 the q rows, rows 8-15 the k rows of the tile's beams
@@ -373,7 +373,7 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     if constexpr (T > 0) {
       const int posi = min(p * G::TB + bb, nb - 1);
       const u32x4 e = s_tab[posi];
-      const int sl[4] = {(int)e[1], (int)e[2], (int)e[3], T > 3 ? s_slot3[posi] : 0};
+      const int sl[3] = {(int)e[1], (int)e[2], (int)e[3]};
 #pragma unroll
       for (int j = 0; j < T; ++j) {
         const size_t rj = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + h;

@@ -101,6 +101,16 @@ def test_ragged_widths(dims, channel):
     check_beam(inp, channel, label=f"ragged dk={dk} ch={channel}")
 
 
+@pytest.mark.parametrize("dims", [(32, 32), (64, 64), (128, 128)])
+def test_chains_up_to_six_records(dims):
+    """Steps t = 5, 6 (the longest chains of the OneLA operator suite, T = 6)
+    on the fused kernel, with ragged widths."""
+    dk, dv = dims
+    inp = synth.make_inputs(R=2, H=2, dk=dk, dv=dv, W=37, L=7, s0_std=0.1, seed=200 + dk,
+                            parents="topk", widths=[37, 29, 37, 20, 33, 37, 17])
+    check_beam(inp, False, label=f"L=7 dk={dk}")
+
+
 @pytest.mark.parametrize("kind", ["scalar", "channel", "plain"])
 def test_sequences_small(kind):
     channel, plain = kind != "scalar", kind == "plain"
