@@ -111,6 +111,16 @@ def test_chains_up_to_six_records(dims):
     check_beam(inp, False, label=f"L=7 dk={dk}")
 
 
+@pytest.mark.parametrize("channel", [False, True])
+def test_beams_wider_than_one_workgroup(channel):
+    """W = 1030 beams: each (request, head) is split over several workgroups
+    (chunk order instead of the depth-first schedule, chunk offsets in every
+    store window), with a ragged last chunk."""
+    inp = synth.make_inputs(R=1, H=2, dk=64, dv=64, W=1030, L=3, s0_std=0.1, seed=300,
+                            parents="topk", channel_decay=channel)
+    check_beam(inp, channel, label=f"W=1030 ch={channel}")
+
+
 @pytest.mark.parametrize("kind", ["scalar", "channel", "plain"])
 def test_sequences_small(kind):
     channel, plain = kind != "scalar", kind == "plain"
