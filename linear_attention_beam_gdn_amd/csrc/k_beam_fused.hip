@@ -5,14 +5,17 @@
 // Work split.  A workgroup takes one (request r, head h) and a chunk of its
 // beams, 16 beams (one MFMA N block) per tile, and runs three kinds of wave:
 //
-// * Two DMA waves, taking alternate tiles.  They build the chunk's ancestry
-//   slot table in LDS, then stream every tile's q, k, v, alpha, beta and, for
-//   each beam, the keys and decays of its T ancestral records straight from
-//   HBM into a ring of NBUF LDS buffers with LDS-DMA loads (global_load_lds,
-//   no register round trip).  They keep tiles in flight (a wave holds at most
-//   63 memory operations, so two waves double the depth) and, before each
-//   barrier, the owner of the tile the dot wave takes next waits for it alone
-//   (counted vmcnt waits).
+// * Two DMA waves, taking alternate tiles.  Wave 0 builds the chunk's
+//   ancestry slot table in LDS (its inputs in one batch of loads, barrier Q,
+//   then the sort, barrier P); wave 1 meanwhile stages S0[r, h] into LDS,
+//   which the consumers split into planes between barriers S and A.  Both
+//   then stream every tile's q, k, v, alpha, beta and, for each beam, the
+//   keys and decays of its T ancestral records straight from HBM into a ring
+//   of NBUF LDS buffers with LDS-DMA loads (global_load_lds, no register
+//   round trip): tiles 0 and 1 first, the rest of the prologue after A.  They
+//   keep tiles in flight (a wave holds at most 63 memory operations, so two
+//   waves double the depth) and, before each barrier, the owner of the tile
+//   the dot wave takes next waits for it alone (counted vmcnt waits).
 // * Dot wave.  One tile ahead of the consumers, forms for every beam the
 //   replay's dot products k_j . q_t, k_j . k_t and k_t . q_t (bf16 dot2
 //   products reduced over four lane groups) and folds the scalar decays of
