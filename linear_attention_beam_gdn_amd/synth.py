@@ -58,10 +58,13 @@ def _softplus(x: np.ndarray) -> np.ndarray:
     return np.logaddexp(0.0, x)
 
 
-def _draw_token_inputs(rng, lead, dk, dv, channel_decay):
-    """q, k, v, alpha, beta for a block of tokens with leading shape ``lead``."""
-    q = bf16_bits(_unit_rows(rng.standard_normal(lead + (dk,))))
-    k = bf16_bits(_unit_rows(rng.standard_normal(lead + (dk,))))
+def _draw_token_inputs(rng, lead, dk, dv, channel_decay, Hk=None):
+    """q, k, v, alpha, beta for a block of tokens with leading shape ``lead``
+    (its last axis the value heads); q and k get ``Hk`` key heads instead
+    when given."""
+    lead_k = lead if Hk is None else lead[:-1] + (Hk,)
+    q = bf16_bits(_unit_rows(rng.standard_normal(lead_k + (dk,))))
+    k = bf16_bits(_unit_rows(rng.standard_normal(lead_k + (dk,))))
     v = bf16_bits(rng.standard_normal(lead + (dv,)))
     a_shape = lead + ((dk,) if channel_decay else ())
     alpha = np.exp(-_softplus(rng.standard_normal(a_shape))).astype(np.float32)
@@ -95,7 +98,7 @@ def _select_parents(rng, mode, R, W_prev, W, score, expand, hot_frac):
 
 def make_inputs(*, R, H, dk, dv, W, L, s0_std, seed, parents="topk",
                 channel_decay=False, expand=8, hot_frac=0.3, widths=None,
-                alpha_const=None, beta_const=None):
+                alpha_const=None, beta_const=None, Hk=None):
     """Inputs for an L-step beam decode.
 
     Returns a dict with ``S0`` (FP32 [R,H,dk,dv]) and ``steps``: a list of L
@@ -104,8 +107,11 @@ def make_inputs(*, R, H, dk, dv, W, L, s0_std, seed, parents="topk",
     [R,W_t,H]) and, for t >= 1, ``parent`` (int32 [R,W_t]).  ``widths`` gives a
     per-step beam width W_t (default: W at every step).  ``alpha_const`` and
     ``beta_const`` replace the drawn gates by constants (the draws still
-    happen, so the other inputs are unchanged).
+    happen, so the other inputs are unchanged).  ``Hk`` (a divisor of H) gives
+    q and k that many key heads, shared by H / Hk value heads each.
     """
+    if Hk is not None and (Hk < 1 or H % Hk):
+        raise ValueError("Hk must divide H")
     rng = np.random.default_rng(seed)
     widths = list(widths) if widths is not None else [W] * L
     if len(widths) != L:
@@ -115,7 +121,7 @@ def make_inputs(*, R, H, dk, dv, W, L, s0_std, seed, parents="topk",
     score = np.zeros((R, widths[0]), np.float64)
     for t in range(L):
         Wt = widths[t]
-        q, k, v, alpha, beta = _draw_token_inputs(rng, (R, Wt, H), dk, dv, channel_decay)
+        q, k, v, alpha, beta = _draw_token_inputs(rng, (R, Wt, H), dk, dv, channel_decay, Hk)
         if alpha_const is not None:
             alpha = np.full_like(alpha, alpha_const)
         if beta_const is not None:
@@ -128,17 +134,20 @@ def make_inputs(*, R, H, dk, dv, W, L, s0_std, seed, parents="topk",
     return dict(S0=S0, steps=steps)
 
 
-def make_sequence_inputs(*, R, H, dk, dv, T, s0_std, seed, channel_decay=False):
+def make_sequence_inputs(*, R, H, dk, dv, T, s0_std, seed, channel_decay=False, Hk=None):
     """Inputs for T tokens of R independent sequences (no beams).
 
     ``S0`` is the FP32 dense base [R,H,dk,dv]; ``tokens`` holds q, k, v, alpha,
-    beta with a leading token axis: q/k [T,R,H,dk], v [T,R,H,dv], ...
+    beta with a leading token axis: q/k [T,R,Hk,dk] (Hk = H by default),
+    v [T,R,H,dv], ...
     """
+    if Hk is not None and (Hk < 1 or H % Hk):
+        raise ValueError("Hk must divide H")
     rng = np.random.default_rng(seed)
     S0 = (rng.standard_normal((R, H, dk, dv)) * s0_std).astype(np.float32)
     cols = {n: [] for n in ("q", "k", "v", "alpha", "beta")}
     for _ in range(T):
-        q, k, v, alpha, beta = _draw_token_inputs(rng, (R, H), dk, dv, channel_decay)
+        q, k, v, alpha, beta = _draw_token_inputs(rng, (R, H), dk, dv, channel_decay, Hk)
         for n, a in zip(cols, (q, k, v, alpha, beta)):
             cols[n].append(a)
     return dict(S0=S0, tokens={n: np.stack(a) for n, a in cols.items()})

@@ -56,10 +56,19 @@ def bf16_to_f64(bits) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def _key_head(step, h):
+    """Key head of value head h.  With H_K key heads and H_V = g H_K value
+    heads (OneLA §4.1 geometries), value heads g*i .. g*i + g-1 share key
+    head i: q and k carry H_K heads, everything else H_V."""
+    H, Hk = step["v"].shape[2], step["q"].shape[2]
+    return h // (H // Hk)
+
+
 def _token(step, r, rows, h):
-    """(q, k, v, alpha, beta) of request r, beam slots ``rows``, head h."""
-    q = bf16_to_f64(step["q"][r, rows, h])
-    k = bf16_to_f64(step["k"][r, rows, h])
+    """(q, k, v, alpha, beta) of request r, beam slots ``rows``, value head h."""
+    hk = _key_head(step, h)
+    q = bf16_to_f64(step["q"][r, rows, hk])
+    k = bf16_to_f64(step["k"][r, rows, hk])
     v = bf16_to_f64(step["v"][r, rows, h])
     alpha = np.asarray(step["alpha"][r, rows, h], dtype=np.float64)
     beta = np.asarray(step["beta"][r, rows, h], dtype=np.float64)
@@ -274,12 +283,13 @@ def sequence_decode(S0, tokens, merge_every, *, pairs=None, rule="delta"):
         pairs = [(r, h) for r in range(R) for h in range(H)]
     rs = np.array([p[0] for p in pairs])
     hs = np.array([p[1] for p in pairs])
+    hks = hs // (tokens["v"].shape[2] // tokens["q"].shape[2])  # key head of each value head
     S = S0[rs, hs].astype(np.float64)
     T = tokens["q"].shape[0]
     o, d, bases = [], [], []
     for i in range(T):
-        q = bf16_to_f64(tokens["q"][i][rs, hs])
-        k = bf16_to_f64(tokens["k"][i][rs, hs])
+        q = bf16_to_f64(tokens["q"][i][rs, hks])
+        k = bf16_to_f64(tokens["k"][i][rs, hks])
         v = bf16_to_f64(tokens["v"][i][rs, hs])
         alpha = np.asarray(tokens["alpha"][i][rs, hs], dtype=np.float64)
         beta = np.asarray(tokens["beta"][i][rs, hs], dtype=np.float64)

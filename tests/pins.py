@@ -370,6 +370,42 @@ def pin_plain_differs_from_delta():
     assert rel(a["o"][2], b["o"][2]) > 1e-3
 
 
+# ------------------------------------------- value heads sharing key heads
+
+def pin_shared_key_heads_equal_duplicated_keys():
+    """H_V = g H_K: decoding with shared key heads equals decoding with every
+    key head's q and k copied to its g value heads (OneLA §4.1 geometries)."""
+    for channel, rule in ((False, "delta"), (True, "delta"), (True, "plain")):
+        inp = small(channel=channel, seed=81, H=4, Hk=2)
+        dup = {"S0": inp["S0"], "steps": []}
+        for st in inp["steps"]:
+            s2 = dict(st)
+            s2["q"] = np.repeat(st["q"], 2, axis=2)
+            s2["k"] = np.repeat(st["k"], 2, axis=2)
+            dup["steps"].append(s2)
+        a = O.beam_decode(inp["S0"], inp["steps"], rule=rule)
+        b = O.beam_decode(dup["S0"], dup["steps"], rule=rule)
+        for t in range(len(inp["steps"])):
+            assert np.array_equal(a["o"][t], b["o"][t]) and np.array_equal(a["delta"][t], b["delta"][t])
+    seq = synth.make_sequence_inputs(R=2, H=6, dk=8, dv=6, T=6, s0_std=0.3, seed=83, Hk=3)
+    dtok = dict(seq["tokens"])
+    dtok["q"] = np.repeat(seq["tokens"]["q"], 2, axis=2)
+    dtok["k"] = np.repeat(seq["tokens"]["k"], 2, axis=2)
+    a = O.sequence_decode(seq["S0"], seq["tokens"], 3)
+    b = O.sequence_decode(seq["S0"], dtok, 3)
+    assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["bases"], b["bases"])
+
+
+def pin_key_heads_matter():
+    """Different key heads give different outputs (the mapping is not moot)."""
+    inp = small(seed=85, H=4, Hk=2)
+    a = O.beam_decode(inp["S0"], inp["steps"])
+    swapped = {"S0": inp["S0"], "steps": [dict(st, q=st["q"][:, :, ::-1].copy(), k=st["k"][:, :, ::-1].copy())
+                                          for st in inp["steps"]]}
+    b = O.beam_decode(swapped["S0"], swapped["steps"])
+    assert rel(a["o"][2], b["o"][2]) > 1e-3
+
+
 ALL_PINS = {
     "hand_worked": pin_hand_worked,
     "ancestry_walk": pin_ancestry_walk,
@@ -392,4 +428,6 @@ ALL_PINS = {
     "plain_linear_retrieval": pin_plain_linear_retrieval,
     "plain_sequence_single_beam": pin_plain_sequence_equals_single_beam,
     "plain_differs_from_delta": pin_plain_differs_from_delta,
+    "shared_key_heads": pin_shared_key_heads_equal_duplicated_keys,
+    "key_heads_matter": pin_key_heads_matter,
 }

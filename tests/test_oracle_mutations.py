@@ -95,6 +95,10 @@ def _plain_with_delta_correction(S, k, v, alpha, beta, rule="delta"):
     return _transition(S, k, v, alpha, beta, "delta")
 
 
+def _key_head_by_value_head(step, h):
+    return min(h, step["q"].shape[2] - 1)
+
+
 def _anc_child_index(parents, R, W0):
     anc = [np.zeros((R, W0, 0), dtype=np.int64)]
     for t in range(1, len(parents)):
@@ -137,6 +141,7 @@ MUTANTS = {
     "plain_update_scaled_by_beta": ("transition", _plain_scaled_by_beta),
     "plain_decay_after_write": ("transition", _plain_decay_after_write),
     "plain_with_delta_correction": ("transition", _plain_with_delta_correction),
+    "key_head_indexed_by_value_head": ("_key_head", _key_head_by_value_head),
 }
 
 
