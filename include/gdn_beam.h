@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GDN_BEAM_ABI_VERSION 3
+#define GDN_BEAM_ABI_VERSION 4
 
 /* status codes */
 #define GDN_OK 0
@@ -73,18 +73,23 @@ extern "C" {
 typedef struct gdn_shape {
   int32_t R;          /* requests (W_max == 1: independent sequences)  >= 1 */
   int32_t W_max;      /* beam slots per step                            >= 1 */
-  int32_t H;          /* heads                                          >= 1 */
+  int32_t H;          /* (value) heads                                  >= 1 */
   int32_t dk;         /* key head dim                                        */
   int32_t dv;         /* value head dim                                      */
   int32_t L_max;      /* steps held (1 .. GDN_MAX_STEPS)                     */
   int32_t decay_kind; /* GDN_DECAY_SCALAR, _CHANNEL or _CHANNEL_PLAIN        */
+  int32_t H_k;        /* key heads: 0 (= H) or a divisor of H.  With H_k < H,
+                         value heads g*i .. g*i + g-1 (g = H / H_k) share key
+                         head i (the OneLA §4.1 geometries, H_V a multiple of
+                         H_K): q, k and the record keys have H_k heads, every
+                         other array H                                       */
 } gdn_shape;
 
 /* The record / ancestry store (caller-allocated device memory). */
 typedef struct gdn_store {
   float* S;          /* [R][H][dk][dv]  FP32 shared state (dense base)       */
   float* rec_delta;  /* [L_max][R][W_max][H][dv]  FP32 update vectors delta  */
-  uint16_t* rec_k;   /* [L_max][R][W_max][H][dk]  bf16 keys (bit copies)     */
+  uint16_t* rec_k;   /* [L_max][R][W_max][H_k][dk]  bf16 keys (bit copies)   */
   float* rec_alpha;  /* [L_max][R][W_max][H][A]   FP32 decays                */
   int32_t* anc;      /* [L_max][R][W_max][L_max]  ancestry: anc[t][r][b][j] =
                         h_t(b, j), j < t.  The decode step may keep in the
@@ -115,7 +120,7 @@ typedef struct gdn_store {
  *           (may be NULL) at t == 0.  Precondition: 0 <= parent < W_{t-1}.
  *           Out-of-range values are clamped into [0, W_max) so no access
  *           leaves the store, but the result is then meaningless.
- *   q, k    bf16 [R][W_t][H][dk];  v  bf16 [R][W_t][H][dv]
+ *   q, k    bf16 [R][W_t][H_k][dk];  v  bf16 [R][W_t][H][dv]
  *   alpha   FP32 [R][W_t][H][A];   beta FP32 [R][W_t][H]
  *   o       FP32 [R][W_t][H][dv] (output)
  * With W_max == 1 this is one token of DeltaLog-style decoding of R
@@ -138,7 +143,7 @@ int gdn_beam_decode_step(const gdn_shape* shape, const gdn_store* store, int32_t
  * result equals that decode step followed by gdn_log_merge(shape, store,
  * t + 1, 0); the caller then restarts at t = 0.
  *   t        current log length, 0 <= t < L_max
- *   q, k     bf16 [R][1][H][dk];  v  bf16 [R][1][H][dv]
+ *   q, k     bf16 [R][1][H_k][dk];  v  bf16 [R][1][H][dv]
  *   alpha    FP32 [R][1][H][A];   beta FP32 [R][1][H]
  *   o        FP32 [R][1][H][dv] (output)
  * Returns GDN_EUNSUPPORTED when W_max != 1.

@@ -23,7 +23,7 @@ GDN_MAX_STEPS = 16
 
 
 class GdnShape(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("R", "W_max", "H", "dk", "dv", "L_max", "decay_kind")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("R", "W_max", "H", "dk", "dv", "L_max", "decay_kind", "H_k")]
 
 
 class GdnStore(ctypes.Structure):
@@ -103,13 +103,16 @@ _BF16 = (torch.bfloat16, torch.int16)
 class Store:
     """Caller-owned record / ancestry store (device memory from PyTorch).
 
-    S [R,H,dk,dv] FP32, rec_delta [L,R,W,H,dv] FP32, rec_k [L,R,W,H,dk] bf16,
+    S [R,H,dk,dv] FP32, rec_delta [L,R,W,H,dv] FP32, rec_k [L,R,W,Hk,dk] bf16,
     rec_alpha [L,R,W,H,A] FP32, anc [L,R,W,L] int32.
     """
 
     def __init__(self, R, W_max, H, dk, dv, L_max, channel_decay=False, device="cuda", S=None,
-                 plain_update=False):
+                 plain_update=False, Hk=None):
         self.R, self.W_max, self.H, self.dk, self.dv, self.L_max = R, W_max, H, dk, dv, L_max
+        self.Hk = H if Hk is None else Hk
+        if self.Hk < 1 or H % self.Hk:
+            raise ValueError("Hk (key heads) must divide H")
         if plain_update and not channel_decay:
             raise ValueError("the plain (RWKV6) update rule comes with per-channel decay")
         self.channel_decay = bool(channel_decay)
@@ -122,11 +125,11 @@ class Store:
             _check(S, "S", (torch.float32,), (R, H, dk, dv))
             self.S = S
         self.rec_delta = torch.zeros(L_max, R, W_max, H, dv, **f32)
-        self.rec_k = torch.zeros(L_max, R, W_max, H, dk, dtype=torch.bfloat16, device=device)
+        self.rec_k = torch.zeros(L_max, R, W_max, self.Hk, dk, dtype=torch.bfloat16, device=device)
         self.rec_alpha = torch.zeros(L_max, R, W_max, H, self.A, **f32)
         self.anc = torch.zeros(L_max, R, W_max, L_max, dtype=torch.int32, device=device)
         kind = GDN_DECAY_CHANNEL_PLAIN if plain_update else (GDN_DECAY_CHANNEL if channel_decay else GDN_DECAY_SCALAR)
-        self.shape = GdnShape(R, W_max, H, dk, dv, L_max, kind)
+        self.shape = GdnShape(R, W_max, H, dk, dv, L_max, kind, self.Hk)
         self.cstore = GdnStore(_ptr(self.S), _ptr(self.rec_delta), _ptr(self.rec_k),
                                _ptr(self.rec_alpha), _ptr(self.anc))
 
@@ -134,8 +137,8 @@ class Store:
 def decode_step(store: Store, t, W_t, parent, q, k, v, alpha, beta, o=None, stream=None):
     """One decode step (gdn_beam_decode_step); returns o [R,W_t,H,dv] FP32."""
     R, H, dk, dv = store.R, store.H, store.dk, store.dv
-    _check(q, "q", _BF16, (R, W_t, H, dk))
-    _check(k, "k", _BF16, (R, W_t, H, dk))
+    _check(q, "q", _BF16, (R, W_t, store.Hk, dk))
+    _check(k, "k", _BF16, (R, W_t, store.Hk, dk))
     _check(v, "v", _BF16, (R, W_t, H, dv))
     a_shape = (R, W_t, H, dk) if store.channel_decay else (R, W_t, H)
     _check(alpha, "alpha", (torch.float32,), a_shape)
@@ -171,8 +174,8 @@ def decode_merge_step(store: Store, t, q, k, v, alpha, beta, o=None, stream=None
     """Decode token t of independent sequences and fold the full log into the
     base in the same pass (gdn_decode_merge_step); returns o [R,1,H,dv] FP32."""
     R, H, dk, dv = store.R, store.H, store.dk, store.dv
-    _check(q, "q", _BF16, (R, 1, H, dk))
-    _check(k, "k", _BF16, (R, 1, H, dk))
+    _check(q, "q", _BF16, (R, 1, store.Hk, dk))
+    _check(k, "k", _BF16, (R, 1, store.Hk, dk))
     _check(v, "v", _BF16, (R, 1, H, dv))
     _check(alpha, "alpha", (torch.float32,), (R, 1, H, dk) if store.channel_decay else (R, 1, H))
     _check(beta, "beta", (torch.float32,), (R, 1, H))

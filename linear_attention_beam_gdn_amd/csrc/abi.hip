@@ -27,6 +27,7 @@ int check_shape(const gdn_shape* s) {
       s->decay_kind != GDN_DECAY_CHANNEL_PLAIN)
     return GDN_EUNSUPPORTED;
   if (!gdn::dims_supported(s->dk, s->dv)) return GDN_EUNSUPPORTED;
+  if (s->H_k < 0 || (s->H_k > 0 && s->H % s->H_k != 0)) return GDN_EINVAL;
   // element counts of the largest arrays must stay far from 2^63
   const double recs = (double)s->L_max * s->R * s->W_max * s->H * (s->dk > s->dv ? s->dk : s->dv);
   const double anc = (double)s->L_max * s->R * s->W_max * s->L_max;

@@ -23,6 +23,9 @@ struct BeamArgs {
   float* o;
   int R, Wm, H, L, t, Wt;
   int chunk, nchunk;
+  // key heads: q, k and the record keys have Hk heads; value head h uses key
+  // head h / gq (gq = H / Hk)
+  int Hk, gq;
 };
 
 template <int DK, int DV>

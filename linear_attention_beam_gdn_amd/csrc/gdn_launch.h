@@ -21,6 +21,9 @@ struct StepIO {
 
 bool dims_supported(int dk, int dv);
 
+// Key heads of a shape (H_k == 0 means one per value head).
+inline int key_heads(const gdn_shape& sh) { return sh.H_k > 0 ? sh.H_k : sh.H; }
+
 // Beams sharing one state per request (W_max > 1).
 int launch_beam_decode(const gdn_shape& sh, const gdn_store& st, int t, int Wt,
                        const StepIO& io, hipStream_t stream);

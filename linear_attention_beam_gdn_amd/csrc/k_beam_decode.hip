@@ -66,12 +66,17 @@ __global__ __launch_bounds__((BeamGeom<DK, DV>::NW * 64)) void k_beam_decode(Bea
   }
 
   const bool anc_writer = (h == 0) && (w == 0) && (g == 0);
+  const int hk = h / a.gq;
+  const bool key_writer = h % a.gq == 0;
 
   for (int b0 = b_begin; b0 < b_end; b0 += 16) {
     const int b = b0 + c;
     const bool valid = b < b_end;
     const size_t tok = ((size_t)r * a.Wt + (valid ? b : 0)) * a.H + h;
     const size_t rec_t = (((size_t)t * a.R + r) * a.Wm + (valid ? b : 0)) * a.H + h;
+    // the key head's q and k, and its record key (one writer per key head)
+    const size_t tok_k = ((size_t)r * a.Wt + (valid ? b : 0)) * a.Hk + hk;
+    const size_t rec_tk = (((size_t)t * a.R + r) * a.Wm + (valid ? b : 0)) * a.Hk + hk;
 
     // ---- ancestry (§3.3): parent slot and the parent's own ancestry row
     int par = 0;
@@ -84,6 +89,9 @@ __global__ __launch_bounds__((BeamGeom<DK, DV>::NW * 64)) void k_beam_decode(Bea
     auto rec_at = [&](int j, int slot) -> size_t {
       return (((size_t)j * a.R + r) * a.Wm + slot) * a.H + h;
     };
+    auto rec_at_k = [&](int j, int slot) -> size_t {
+      return (((size_t)j * a.R + r) * a.Wm + slot) * a.Hk + hk;
+    };
 
     // ---- current q and k (B operand chunks)
     u32x4 qf[G::KS], kf[G::KS];
@@ -91,8 +99,8 @@ __global__ __launch_bounds__((BeamGeom<DK, DV>::NW * 64)) void k_beam_decode(Bea
     for (int s = 0; s < G::KS; ++s) {
       const int k0 = kchunk<DK>(g, s);
       const bool ld = valid && klive<DK>(g);
-      qf[s] = ld ? *reinterpret_cast<const u32x4*>(a.q + tok * DK + k0) : u32x4{0, 0, 0, 0};
-      kf[s] = ld ? *reinterpret_cast<const u32x4*>(a.k + tok * DK + k0) : u32x4{0, 0, 0, 0};
+      qf[s] = ld ? *reinterpret_cast<const u32x4*>(a.q + tok_k * DK + k0) : u32x4{0, 0, 0, 0};
+      kf[s] = ld ? *reinterpret_cast<const u32x4*>(a.k + tok_k * DK + k0) : u32x4{0, 0, 0, 0};
     }
 
     // current decay: scalar, or this lane's key channels of the vector
@@ -190,7 +198,7 @@ __global__ __launch_bounds__((BeamGeom<DK, DV>::NW * 64)) void k_beam_decode(Bea
 #pragma unroll
         for (int s = 0; s < G::KS; ++s) {
           const bool ld = valid && klive<DK>(g);
-          const u32x4 kj = ld ? *reinterpret_cast<const u32x4*>(a.rec_k + rj * DK + kchunk<DK>(g, s))
+          const u32x4 kj = ld ? *reinterpret_cast<const u32x4*>(a.rec_k + rec_at_k(j, slot) * DK + kchunk<DK>(g, s))
                               : u32x4{0, 0, 0, 0};
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -227,7 +235,7 @@ __global__ __launch_bounds__((BeamGeom<DK, DV>::NW * 64)) void k_beam_decode(Bea
 #pragma unroll
         for (int s = 0; s < G::KS; ++s) {
           const bool ld = valid && klive<DK>(g);
-          const u32x4 kj = ld ? *reinterpret_cast<const u32x4*>(a.rec_k + rj * DK + kchunk<DK>(g, s))
+          const u32x4 kj = ld ? *reinterpret_cast<const u32x4*>(a.rec_k + rec_at_k(j, slot) * DK + kchunk<DK>(g, s))
                               : u32x4{0, 0, 0, 0};
           float aj[8];
           if (ld) load_f32x8(a.rec_alpha + rj * A + kchunk<DK>(g, s), aj);
@@ -290,7 +298,7 @@ __global__ __launch_bounds__((BeamGeom<DK, DV>::NW * 64)) void k_beam_decode(Bea
 #pragma unroll
         for (int s = 0; s < G::KS; ++s) {
           const int k0 = kchunk<DK>(g, s);
-          *reinterpret_cast<u32x4*>(a.rec_k + rec_t * DK + k0) = kf[s];
+          if (key_writer) *reinterpret_cast<u32x4*>(a.rec_k + rec_tk * DK + k0) = kf[s];
           if constexpr (CH) {
             *reinterpret_cast<f32x4*>(a.rec_alpha + rec_t * A + k0) =
                 f32x4{acur[8 * s], acur[8 * s + 1], acur[8 * s + 2], acur[8 * s + 3]};
@@ -328,6 +336,8 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO
   a.L = sh.L_max;
   a.t = t;
   a.Wt = Wt;
+  a.Hk = key_heads(sh);
+  a.gq = sh.H / a.Hk;
   a.chunk = pick_chunk(sh.R * sh.H, Wt, 1 << 30, 2048);
   a.nchunk = (Wt + a.chunk - 1) / a.chunk;
   const long grid = (long)sh.R * sh.H * a.nchunk;

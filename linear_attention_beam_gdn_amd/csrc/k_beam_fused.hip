@@ -167,8 +167,9 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
         for (int j = 3; j < T; ++j) sl[j] = lds_read_opaque(&s_slot_hi[(j - 3) * kMaxChunkF + posi]);
       }
       const size_t tok = ((size_t)r * a.Wt + b_begin + ib) * a.H + h;
-      const uint16_t* qrow = a.q + tok * DK;
-      const uint16_t* krow = a.k + tok * DK;
+      const size_t tok_k = ((size_t)r * a.Wt + b_begin + ib) * a.Hk + h / a.gq;  // its key head
+      const uint16_t* qrow = a.q + tok_k * DK;
+      const uint16_t* krow = a.k + tok_k * DK;
       const uint16_t* vrow = a.v + tok * DV;
 #pragma unroll
       for (int m = 0; m < G::QB / 1024; ++m) dma16(qrow + (m * 4 + cg) * 8, buf + G::OQ + m * 1024);
@@ -183,7 +184,8 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
       for (int j = 0; j < T; ++j)
 #pragma unroll
         for (int m = 0; m < G::RKB / 1024; ++m)
-          dma16(a.rec_k + rj[j] * DK + (m * 4 + cg) * 8, buf + G::ORK + j * G::RKB + m * 1024);
+          dma16(a.rec_k + ((((size_t)j * a.R + r) * a.Wm + sl[j]) * a.Hk + h / a.gq) * DK + (m * 4 + cg) * 8,
+                buf + G::ORK + j * G::RKB + m * 1024);
       // dword block: group 0 alpha_t, 1 beta_t, 2 + j alpha_j (16 beams each)
 #pragma unroll
       for (int n = 0; n < G::NSM; ++n) {
@@ -291,12 +293,15 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
 
   // Store windows over the chunk's beams [b_begin, b_end): a lane whose beam
   // is past the chunk (last tile) lands outside its window.
-  const int so = a.H * DV * 4, sk = a.H * DK * 2, sa = a.H * 4;  // bytes between beams
+  const int so = a.H * DV * 4, sk = a.Hk * DK * 2, sa = a.H * 4;  // bytes between beams
   const size_t tok0 = ((size_t)r * a.Wt + b_begin) * a.H + h;
   const size_t rec0 = (((size_t)T * a.R + r) * a.Wm + b_begin) * a.H + h;
   const __amdgpu_buffer_rsrc_t w_o = store_window(a.o + tok0 * DV, (nb - 1) * so + DV * 4);
   const __amdgpu_buffer_rsrc_t w_d = store_window(a.rec_delta + rec0 * DV, (nb - 1) * so + DV * 4);
-  const __amdgpu_buffer_rsrc_t w_k = store_window(a.rec_k + rec0 * DK, (nb - 1) * sk + DK * 2);
+  // the record key lives per key head: one of its value heads writes it
+  const size_t rec0k = (((size_t)T * a.R + r) * a.Wm + b_begin) * a.Hk + h / a.gq;
+  const bool key_writer = h % a.gq == 0;
+  const __amdgpu_buffer_rsrc_t w_k = store_window(a.rec_k + rec0k * DK, (nb - 1) * sk + DK * 2);
   const __amdgpu_buffer_rsrc_t w_a = store_window(a.rec_alpha + rec0, (nb - 1) * sa + 4);
   // this wave's share of the appended key row: 4 channels per lane
   const int ks = w >> 1, kh = w & 1;
@@ -398,7 +403,8 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     for (int s = 1; s < KS; ++s)
       if (ks == s) kk = kf[s];
     __builtin_amdgcn_raw_buffer_store_b64(kh ? u32x2{kk[2], kk[3]} : u32x2{kk[0], kk[1]}, w_k,
-                                          live ? ib * sk + (ks * 32 + g * 8 + kh * 4) * 2 : kOutside, 0, 0);
+                                          live && key_writer ? ib * sk + (ks * 32 + g * 8 + kh * 4) * 2 : kOutside,
+                                          0, 0);
     const float at = *reinterpret_cast<const float*>(buf + G::OS + c * 4);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(at), w_a,
                                           (live && w == G::NC - 1 && g == 0) ? ib * sa : kOutside, 0, 0);
@@ -428,6 +434,8 @@ int launch(const gdn_shape& sh, const gdn_store& st, int Wt, const StepIO& io, h
   a.L = sh.L_max;
   a.t = T;
   a.Wt = Wt;
+  a.Hk = key_heads(sh);
+  a.gq = sh.H / a.Hk;
   // one workgroup per compute unit: the tile ring takes most of its LDS
   a.chunk = pick_chunk(sh.R * sh.H, Wt, kMaxChunkF, cu_count());
   a.nchunk = (Wt + a.chunk - 1) / a.chunk;

@@ -211,7 +211,8 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       }
       const size_t tok = ((size_t)r * a.Wt + b_begin + ib) * a.H + h;
       // q|k: rows 0-7 the q rows, rows 8-15 the k rows of the tile's beams
-      const uint16_t* qkrow = ((lane & 8) ? a.k : a.q) + tok * DK;
+      const size_t tok_k = ((size_t)r * a.Wt + b_begin + ib) * a.Hk + h / a.gq;  // its key head
+      const uint16_t* qkrow = ((lane & 8) ? a.k : a.q) + tok_k * DK;
 #pragma unroll
       for (int m = 0; m < G::QKB / 1024; ++m) dma16(qkrow + (m * 4 + (lane >> 4)) * 8, buf + G::OQK + m * 1024);
 #pragma unroll
@@ -223,9 +224,10 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
 #pragma unroll
       for (int j = 0; j < T; ++j) {
         const size_t rj = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + h;
+        const size_t rjk = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.Hk + h / a.gq;
 #pragma unroll
         for (int m = 0; m < G::RKB / 1024; ++m)
-          dma16(a.rec_k + rj * DK + (m * 8 + (lane >> 3)) * 8, buf + G::ORK + j * G::RKB + m * 1024);
+          dma16(a.rec_k + rjk * DK + (m * 8 + (lane >> 3)) * 8, buf + G::ORK + j * G::RKB + m * 1024);
 #pragma unroll
         for (int m = 0; m < G::AB / 1024; ++m)
           dma16(a.rec_alpha + rj * DK + (m * 8 + (lane >> 3)) * 4, buf + G::ORA + j * G::AB + m * 1024);
@@ -261,8 +263,11 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   // ============================================================ consumers
   // record-store windows over the chunk's beams (appends at step T)
   const size_t rec0 = (((size_t)T * a.R + r) * a.Wm + b_begin) * a.H + h;
-  const int sk = a.H * DK * 2, sa = a.H * DK * 4;  // bytes between beams
-  const __amdgpu_buffer_rsrc_t w_k = store_window(a.rec_k + rec0 * DK, (nb - 1) * sk + DK * 2);
+  const int sk = a.Hk * DK * 2, sa = a.H * DK * 4;  // bytes between beams
+  // the record key lives per key head: one of its value heads writes it
+  const size_t rec0k = (((size_t)T * a.R + r) * a.Wm + b_begin) * a.Hk + h / a.gq;
+  const bool key_writer = h % a.gq == 0;
+  const __amdgpu_buffer_rsrc_t w_k = store_window(a.rec_k + rec0k * DK, (nb - 1) * sk + DK * 2);
   const __amdgpu_buffer_rsrc_t w_a = store_window(a.rec_alpha + rec0 * DK, (nb - 1) * sa + DK * 4);
 
   // Preparation of beams w * BPW .. w * BPW + BPW - 1 of tile p.  Lane
@@ -314,12 +319,14 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       const bool live = posi < nb;
       const int ib = T > 0 ? (int)s_tab[min(posi, nb - 1)][0] : posi;  // read unconditionally: no branch
       if constexpr (EPL == 4) {
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{kw[0], kw[1]}, w_k, live && ps ? ib * sk + e0 * 2 : kOutside,
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{kw[0], kw[1]}, w_k,
+                                              live && ps && key_writer ? ib * sk + e0 * 2 : kOutside,
                                               0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{at[0], at[1], at[2], at[3]}), w_a,
                                                live && !ps ? ib * sa + e0 * 4 : kOutside, 0, 0);
       } else {
-        __builtin_amdgcn_raw_buffer_store_b32(kw[0], w_k, live && ps ? ib * sk + e0 * 2 : kOutside, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(kw[0], w_k, live && ps && key_writer ? ib * sk + e0 * 2 : kOutside,
+                                              0, 0);
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(at[0]), __float_as_uint(at[1])}, w_a,
                                               live && !ps ? ib * sa + e0 * 4 : kOutside, 0, 0);
       }
@@ -492,6 +499,8 @@ int launch(const gdn_shape& sh, const gdn_store& st, int Wt, const StepIO& io, h
   a.L = sh.L_max;
   a.t = T;
   a.Wt = Wt;
+  a.Hk = key_heads(sh);
+  a.gq = sh.H / a.Hk;
   // one workgroup per compute unit: the tile ring takes most of its LDS
   a.chunk = pick_chunk(sh.R * sh.H, Wt, kMaxChunkF, cu_count());
   a.nchunk = (Wt + a.chunk - 1) / a.chunk;

@@ -26,6 +26,7 @@ struct FoldArgs {
   const int32_t* anc;
   const int32_t* rb;
   int R, Wm, H, L, t, beam;
+  int Hk, gq;  // key heads; value head h uses key head h / gq
   int dst_per_item;
 };
 
@@ -69,12 +70,13 @@ __global__ __launch_bounds__((FoldGeom<DK, DV>::NT)) void k_fold(FoldArgs a) {
   for (int j = 0; j <= t; ++j) {
     const int slot = j < t ? clampi(arow[j], 0, a.Wm - 1) : b;
     const size_t rj = (((size_t)j * a.R + r) * a.Wm + slot) * a.H + h;
+    const size_t rjk = (((size_t)j * a.R + r) * a.Wm + slot) * a.Hk + h / a.gq;
     const f32x4 dj = *reinterpret_cast<const f32x4*>(a.rec_delta + rj * DV + c4 * 4);
     const float aj0 = CH ? 0.f : a.rec_alpha[rj];
 #pragma unroll
     for (int i = 0; i < G::RPG; ++i) {
       const int row = rg * G::RPG + i;
-      const float kj = bf16_at(a.rec_k[rj * DK + row]);
+      const float kj = bf16_at(a.rec_k[rjk * DK + row]);
       const float aj = CH ? a.rec_alpha[rj * A + row] : aj0;
       st[i] = apply_record(st[i], aj, kj, dj);
     }
@@ -101,6 +103,8 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, const int32_t* rb, i
   a.L = sh.L_max;
   a.t = t;
   a.beam = beam;
+  a.Hk = key_heads(sh);
+  a.gq = sh.H / a.Hk;
   a.dst_per_item = dst_per_item ? 1 : 0;
   const long grid = (long)n * sh.H;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;

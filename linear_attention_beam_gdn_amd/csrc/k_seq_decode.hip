@@ -33,6 +33,7 @@ struct SeqArgs {
   const float* beta;
   float* o;
   int R, H, L, t;
+  int Hk, gq;  // key heads; value head h uses key head h / gq
 };
 
 template <int DK, int DV>
@@ -64,6 +65,10 @@ __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a)
   const int t = a.t;
   const size_t tok = (size_t)r * a.H + h;                 // (r, beam 0, h)
   auto rec_at = [&](int j) -> size_t { return ((size_t)j * a.R + r) * a.H + h; };
+  // the key head's q, k and record keys (one value head writes the record key)
+  const size_t tk = (size_t)r * a.Hk + h / a.gq;
+  auto rec_at_k = [&](int j) -> size_t { return ((size_t)j * a.R + r) * a.Hk + h / a.gq; };
+  const bool key_writer = h % a.gq == 0;
 
   __shared__ float probe_q[DK], probe_k[DK];
   __shared__ float red_q[G::NRG][DV], red_k[G::NRG][DV];
@@ -84,25 +89,25 @@ __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a)
       cq = a.alpha[tok * DK + kk];
       for (int j = 0; j < t; ++j) cq *= a.rec_alpha[rec_at(j) * A + kk];
     }
-    probe_q[kk] = cq * bf16_at(a.q[tok * DK + kk]);
-    if constexpr (!PLAIN) probe_k[kk] = cq * bf16_at(a.k[tok * DK + kk]);
+    probe_q[kk] = cq * bf16_at(a.q[tk * DK + kk]);
+    if constexpr (!PLAIN) probe_k[kk] = cq * bf16_at(a.k[tk * DK + kk]);
   }
   // dot products of the replay: wave wv takes log entries j = wv, wv + NWV, ..
   // (entry t is k_t . q_t); channel decay weights them by prod_{i=j+1..t} a_i
   for (int j = wv; j <= t; j += G::NWV) {
     float pq = 0.f, pk = 0.f;
     for (int kk = lane; kk < DK; kk += 64) {
-      const float qv = bf16_at(a.q[tok * DK + kk]);
+      const float qv = bf16_at(a.q[tk * DK + kk]);
       if (j == t) {
-        pq += bf16_at(a.k[tok * DK + kk]) * qv;
+        pq += bf16_at(a.k[tk * DK + kk]) * qv;
       } else {
-        float y = bf16_at(a.rec_k[rec_at(j) * DK + kk]);
+        float y = bf16_at(a.rec_k[rec_at_k(j) * DK + kk]);
         if constexpr (CH) {
           y *= a.alpha[tok * DK + kk];
           for (int i = j + 1; i < t; ++i) y *= a.rec_alpha[rec_at(i) * A + kk];
         }
         pq += y * qv;
-        if constexpr (!PLAIN) pk += y * bf16_at(a.k[tok * DK + kk]);
+        if constexpr (!PLAIN) pk += y * bf16_at(a.k[tk * DK + kk]);
       }
     }
     pq = wave_sum(pq);
@@ -157,7 +162,7 @@ __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a)
     if constexpr (MRG) d_new[col] = d;
   }
   for (int kk = tid; kk < DK; kk += G::NT) {
-    a.rec_k[rec_t * DK + kk] = a.k[tok * DK + kk];
+    if (key_writer) a.rec_k[rec_at_k(t) * DK + kk] = a.k[tk * DK + kk];
     if constexpr (CH) a.rec_alpha[rec_t * A + kk] = a.alpha[tok * DK + kk];
   }
   if constexpr (!CH)
@@ -177,7 +182,7 @@ __global__ __launch_bounds__((SeqGeom<DK, DV>::NT)) void k_seq_decode(SeqArgs a)
 #pragma unroll
       for (int i = 0; i < G::RPG; ++i) {
         const int row = rg * G::RPG + i;
-        const float kj = bf16_at(j < t ? a.rec_k[rj * DK + row] : a.k[tok * DK + row]);
+        const float kj = bf16_at(j < t ? a.rec_k[rec_at_k(j) * DK + row] : a.k[tk * DK + row]);
         const float aj = CH ? (j < t ? a.rec_alpha[rj * A + row] : a.alpha[tok * DK + row]) : aj0;
         st[i] = apply_record(st[i], aj, kj, dj);
       }
@@ -208,6 +213,8 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io, hi
   a.H = sh.H;
   a.L = sh.L_max;
   a.t = t;
+  a.Hk = key_heads(sh);
+  a.gq = sh.H / a.Hk;
   const long grid = (long)sh.R * sh.H;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
   hipLaunchKernelGGL((k_seq_decode<DK, DV, CH, MRG, PLAIN>), dim3((unsigned)grid), dim3(SeqGeom<DK, DV>::NT),

@@ -50,7 +50,8 @@ def run_beam(inp, channel=False, L_max=None, W_max=None, S=None):
     W_max = W_max or max(widths)
     L_max = L_max or len(inp["steps"])
     S_dev = torch.from_numpy(np.ascontiguousarray(S0)).cuda() if S is None else S
-    store = B.Store(R, W_max, H, dk, dv, L_max, channel_decay=channel, S=S_dev)
+    Hk = inp["steps"][0]["q"].shape[2]  # key heads (== H unless value heads share them)
+    store = B.Store(R, W_max, H, dk, dv, L_max, channel_decay=channel, S=S_dev, Hk=Hk)
     outs = []
     for t, st in enumerate(inp["steps"]):
         d = B.upload(st)
@@ -62,7 +63,7 @@ def run_beam(inp, channel=False, L_max=None, W_max=None, S=None):
 
 
 def step_records(store, t, W_t):
-    """(delta [R,W_t,H,dv], k bits [R,W_t,H,dk], alpha, anc [R,W_t,t]) at step t."""
+    """(delta [R,W_t,H,dv], k bits [R,W_t,Hk,dk], alpha, anc [R,W_t,t]) at step t."""
     d = store.rec_delta[t, :, :W_t].cpu().numpy()
     k = store.rec_k[t, :, :W_t].view(torch.int16).cpu().numpy().view(np.uint16)
     a = store.rec_alpha[t, :, :W_t].cpu().numpy()

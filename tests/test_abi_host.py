@@ -17,7 +17,7 @@ def L():
 
 
 def shape(**kw):
-    d = dict(R=2, W_max=8, H=2, dk=128, dv=128, L_max=4, decay_kind=0)
+    d = dict(R=2, W_max=8, H=2, dk=128, dv=128, L_max=4, decay_kind=0, H_k=0)
     d.update(kw)
     return B.GdnShape(**d)
 
@@ -49,7 +49,7 @@ def test_exports_every_header_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gdn_abi_version() == 3
+    assert L.gdn_abi_version() == 4
     for s in (B.GDN_OK, B.GDN_EINVAL, B.GDN_EUNSUPPORTED, B.GDN_EHIP, 12345):
         assert isinstance(B.status_string(s), str) and B.status_string(s)
 
@@ -69,6 +69,8 @@ def test_decode_validation(L):
     assert decode(L, sh=shape(dk=128, dv=64)) == U
     assert decode(L, sh=shape(decay_kind=2)) == U  # the plain (RWKV6) rule: sequences only
     assert decode(L, sh=shape(decay_kind=3)) == U
+    assert decode(L, sh=shape(H=4, H_k=3)) == E  # key heads must divide the value heads
+    assert decode(L, sh=shape(H_k=-1)) == E
     assert decode(L, t=-1) == E
     assert decode(L, t=4) == E
     assert decode(L, W_t=0) == E
@@ -106,7 +108,7 @@ def test_materialize_and_merge_validation(L):
 def test_binding_refuses_host_tensors():
     import torch
     st = B.Store.__new__(B.Store)
-    st.R, st.H, st.dk, st.dv, st.channel_decay = 1, 1, 16, 16, False
+    st.R, st.H, st.Hk, st.dk, st.dv, st.channel_decay = 1, 1, 1, 16, 16, False
     x = torch.zeros(1, 1, 1, 16, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="device tensor"):
         B.decode_step(st, 0, 1, None, x, x, x, torch.zeros(1, 1, 1), torch.zeros(1, 1, 1))

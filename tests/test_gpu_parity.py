@@ -121,6 +121,52 @@ def test_beams_wider_than_one_workgroup(channel):
     check_beam(inp, channel, label=f"W=1030 ch={channel}")
 
 
+@pytest.mark.parametrize("dims,channel,Hk", [((16, 16), False, 2), ((64, 64), False, 2), ((128, 128), False, 1),
+                                             ((64, 64), True, 2), ((128, 128), True, 1), ((32, 32), True, 2)])
+def test_value_heads_sharing_key_heads(dims, channel, Hk):
+    """H = 4 value heads on Hk key heads (OneLA §4.1 geometries): the general
+    (d = 16), scalar-decay and channel-decay kernels read each value head's
+    key head, and the record keys are written once per key head."""
+    dk, dv = dims
+    inp = synth.make_inputs(R=2, H=4, dk=dk, dv=dv, W=37, L=4, s0_std=0.1, seed=400 + dk + Hk,
+                            parents="topk", channel_decay=channel, widths=[37, 29, 37, 20], Hk=Hk)
+    store, _, _ = check_beam(inp, channel, label=f"H=4 Hk={Hk} dk={dk} ch={channel}")
+    assert store.rec_k.shape[3] == Hk
+    pairs = np.array([[0, 3], [1, 19]], np.int32)
+    S = B.materialize(store, 3, torch.from_numpy(pairs).cuda()).cpu().numpy()
+    ref = O.beam_states(inp["S0"], inp["steps"], 3, [tuple(p) for p in pairs])
+    assert rel_states(S, ref) <= TOL
+
+
+@pytest.mark.parametrize("kind", ["scalar", "channel", "plain"])
+def test_sequences_with_shared_key_heads(kind):
+    """Bounded-log decoding, fused merge path and fold with H = 6 value heads
+    on 3 key heads."""
+    channel, plain = kind != "scalar", kind == "plain"
+    R, H, Hk, dk, dv, T, M = 3, 6, 3, 64, 64, 8, 4
+    seq = synth.make_sequence_inputs(R=R, H=H, dk=dk, dv=dv, T=T, s0_std=0.1, seed=17,
+                                     channel_decay=channel, Hk=Hk)
+    ref = O.sequence_decode(seq["S0"], seq["tokens"], M, rule="plain" if plain else "delta")
+    S0 = torch.from_numpy(seq["S0"]).cuda()
+    fused = B.Store(R, 1, H, dk, dv, M, channel_decay=channel, plain_update=plain, S=S0.clone(), Hk=Hk)
+    split = B.Store(R, 1, H, dk, dv, M, channel_decay=channel, plain_update=plain, S=S0.clone(), Hk=Hk)
+    zero = torch.zeros(R, 1, dtype=torch.int32, device="cuda")
+    for i in range(T):
+        t = i % M
+        d = B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")})
+        args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        o_f = B.decode_merge_step(fused, t, *args) if t == M - 1 else B.decode_step(fused, t, 1, zero, *args)
+        o_s = B.decode_step(split, t, 1, zero, *args)
+        if t == M - 1:
+            B.log_merge(split, M, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(o_f, o_s), i
+        assert rel_slices(o_f[:, 0].cpu().numpy().reshape(R * H, dv), ref["o"][i]) <= TOL
+        if t == M - 1:
+            assert torch.equal(fused.S, split.S), i
+            assert rel_states(fused.S.cpu().numpy().reshape(R * H, 1, dk, dv), ref["bases"][i // M][:, None]) <= TOL
+
+
 @pytest.mark.parametrize("kind", ["scalar", "channel", "plain"])
 def test_sequences_small(kind):
     channel, plain = kind != "scalar", kind == "plain"
