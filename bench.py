@@ -134,7 +134,7 @@ def beam_row(B, torch, dev, stream, wl, reps):
     inp = wl.inputs()
     steps = [B.upload(st, dev) for st in inp["steps"]]
     store = B.Store(wl.R, wl.W, wl.H, wl.dk, wl.dv, wl.L, channel_decay=wl.channel_decay,
-                    S=torch.from_numpy(inp["S0"]).to(dev))
+                    S=torch.from_numpy(inp["S0"]).to(dev), Hk=wl.Hk)
     outs = [torch.empty(wl.R, wl.W, wl.H, wl.dv, dtype=torch.float32, device=dev) for _ in range(wl.L)]
 
     def launch(t):
@@ -154,7 +154,7 @@ def beam_row(B, torch, dev, stream, wl, reps):
     for t in range(wl.L):
         uniq = sum(accounting.unique_ancestors(anc[t, r, :, :t], wl.W) for r in range(wl.R))
         nbytes = accounting.beam_step_bytes(R=wl.R, H=wl.H, dk=wl.dk, dv=wl.dv, W_t=wl.W, t=t,
-                                            channel_decay=wl.channel_decay, unique_records=uniq)
+                                            channel_decay=wl.channel_decay, unique_records=uniq, Hk=wl.Hk)
         per.append(_bw(nbytes, us[t]))
     tot_b, tot_us = sum(p["bytes"] for p in per), sum(us)
     return {"workload": wl.name, "beam_steps_per_s": wl.R * wl.W * wl.L / (tot_us * 1e-6),
@@ -263,7 +263,7 @@ def materialize_row(B, torch, dev, stream, wl, n_items, reps):
     """Dense states of n_items beams after the last step of a beam workload."""
     inp = wl.inputs()
     store = B.Store(wl.R, wl.W, wl.H, wl.dk, wl.dv, wl.L, channel_decay=wl.channel_decay,
-                    S=torch.from_numpy(inp["S0"]).to(dev))
+                    S=torch.from_numpy(inp["S0"]).to(dev), Hk=wl.Hk)
     for t, st in enumerate(inp["steps"]):
         d = B.upload(st, dev)
         B.decode_step(store, t, wl.W, d.get("parent"), d["q"], d["k"], d["v"], d["alpha"], d["beta"], stream=stream)
@@ -409,6 +409,8 @@ def main():
         rows = {
             "single_request_beam_decode": lambda: beam_row(B, torch, dev, stream, configs.SINGLE, reps),
             "channel_decay_beam_decode": lambda: beam_row(B, torch, dev, stream, configs.KDA, reps),
+            "shared_key_heads_beam_decode": lambda: beam_row(B, torch, dev, stream, configs.SHARED_KEYS, reps),
+            "wide_state_beam_decode": lambda: beam_row(B, torch, dev, stream, configs.WIDE, reps),
             "bounded_log_decode_and_merge": lambda: sequence_row(B, torch, dev, stream, configs.DELTALOG),
             "bounded_log_merge_interval": lambda: merge_interval_row(B, torch, dev, stream, configs.DELTALOG,
                                                                      (4, 8, 16)),

@@ -69,7 +69,12 @@ extern "C" {
 #define GDN_MAX_STEPS 16
 
 /* Geometry of a store.  A = 1 for GDN_DECAY_SCALAR, A = dk otherwise.
- * Built-in (dk, dv): (16,16) (32,32) (64,64) (128,128). */
+ * Built-in (dk, dv): (16,16) (32,32) (64,64) (128,128) for every decay kind;
+ * and the wider recurrent geometries of the OneLA §4.1 operator suite, dk in
+ * {128, 256} x dv in {128, 256, 512}: GDN_DECAY_SCALAR for all six,
+ * GDN_DECAY_CHANNEL with dk = 128.  Other pairs, and the wider pairs with
+ * another decay kind, make every entry point return GDN_EUNSUPPORTED, as
+ * does gdn_decode_merge_step for any non-square pair. */
 typedef struct gdn_shape {
   int32_t R;          /* requests (W_max == 1: independent sequences)  >= 1 */
   int32_t W_max;      /* beam slots per step                            >= 1 */
@@ -146,7 +151,8 @@ int gdn_beam_decode_step(const gdn_shape* shape, const gdn_store* store, int32_t
  *   q, k     bf16 [R][1][H_k][dk];  v  bf16 [R][1][H][dv]
  *   alpha    FP32 [R][1][H][A];   beta FP32 [R][1][H]
  *   o        FP32 [R][1][H][dv] (output)
- * Returns GDN_EUNSUPPORTED when W_max != 1.
+ * Returns GDN_EUNSUPPORTED when W_max != 1 or (dk, dv) is not one of the
+ * square pairs.
  */
 int gdn_decode_merge_step(const gdn_shape* shape, const gdn_store* store, int32_t t,
                           const uint16_t* q, const uint16_t* k, const uint16_t* v,

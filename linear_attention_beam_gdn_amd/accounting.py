@@ -52,18 +52,22 @@ def unique_ancestors(anc_row, W_t):
     return int(sum(len(np.unique(anc_row[:W_t, j])) for j in range(t)))
 
 
-def beam_step_bytes(*, R, H, dk, dv, W_t, t, channel_decay=False, unique_records=None):
+def beam_step_bytes(*, R, H, dk, dv, W_t, t, channel_decay=False, unique_records=None, Hk=None):
     """Algorithmic bytes of one decode step (all requests and heads).
 
     ``unique_records``: total distinct ancestor records over requests (the
     unique-record model); ``None`` selects the per-beam-gather model.
+    ``Hk``: key heads when value heads share them (q, k and the record key are
+    stored once per key head); ``None`` means one key head per value head.
     """
-    rec = record_bytes(dk, dv, channel_decay)
-    per_beam = input_bytes(dk, dv, channel_decay) + output_bytes(dv) + rec
+    Hk = H if Hk is None else Hk
+    A = dk if channel_decay else 1
+    rec_v, rec_k = 4 * A + 4 * dv, 2 * dk  # record parts per value head / per key head
+    per_beam = H * (2 * dv + 4 * A + 4 + output_bytes(dv) + rec_v) + Hk * (4 * dk + rec_k)
     chain = (R * W_t * t) if unique_records is None else unique_records
     # parent pointer + parent's t-1 indices read, own t indices written
     ancestry = 4 * R * W_t * 2 * t
-    return R * H * 4 * dk * dv + R * W_t * H * per_beam + chain * H * rec + ancestry
+    return R * H * 4 * dk * dv + R * W_t * per_beam + chain * (H * rec_v + Hk * rec_k) + ancestry
 
 
 def beam_step_flops(*, R, H, dk, dv, W_t, t):

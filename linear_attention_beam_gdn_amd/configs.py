@@ -27,6 +27,7 @@ class BeamWorkload:
     parents: str
     channel_decay: bool = False
     hot_frac: float = 0.3
+    Hk: int | None = None  # key heads shared by the value heads (None: one each)
 
     @property
     def beam_steps(self) -> int:
@@ -35,7 +36,7 @@ class BeamWorkload:
     def inputs(self, **over):
         kw = dict(R=self.R, H=self.H, dk=self.dk, dv=self.dv, W=self.W, L=self.L,
                   s0_std=self.s0_std, seed=self.seed, parents=self.parents,
-                  channel_decay=self.channel_decay, hot_frac=self.hot_frac)
+                  channel_decay=self.channel_decay, hot_frac=self.hot_frac, Hk=self.Hk)
         kw.update(over)
         return synth.make_inputs(**kw)
 
@@ -81,8 +82,16 @@ DELTALOG = SequenceWorkload("deltalog_bounded_log", R=128, H=32, dk=128, dv=128,
 KDA = BeamWorkload("kda_channel_decay_beam", R=16, H=32, dk=128, dv=128, W=256, L=4,
                    s0_std=0.05, seed=4, parents="topk", channel_decay=True)
 
+# 32 value heads reading 16 key heads (two value heads per key head)
+SHARED_KEYS = BeamWorkload("gdn_large_beam_shared_key_heads", R=8, H=32, dk=128, dv=128, W=512, L=4,
+                           s0_std=0.05, seed=6, parents="topk_hot", hot_frac=0.3, Hk=16)
+
+# the widest recurrent state of the operator suite's range: K = 256, V = 512
+WIDE = BeamWorkload("gdn_wide_state_beam", R=8, H=16, dk=256, dv=512, W=512, L=4,
+                    s0_std=0.05, seed=7, parents="topk_hot", hot_frac=0.3)
+
 RWKV6 = SequenceWorkload("rwkv6_bounded_log", R=128, H=32, dk=128, dv=128, T=64, M=4,
                          s0_std=0.05, seed=5, channel_decay=True, plain_update=True)
 
-ALL = (TINY, SINGLE, LARGE, DELTALOG, KDA, RWKV6)
+ALL = (TINY, SINGLE, LARGE, DELTALOG, KDA, RWKV6, SHARED_KEYS, WIDE)
 BY_NAME = {w.name: w for w in ALL}

@@ -8,9 +8,19 @@
 
 namespace gdn {
 
-bool dims_supported(int dk, int dv) {
+bool seq_dims_supported(int dk, int dv) {
   return (dk == 16 && dv == 16) || (dk == 32 && dv == 32) || (dk == 64 && dv == 64) ||
          (dk == 128 && dv == 128);
+}
+
+bool dims_supported(int dk, int dv, int decay_kind) {
+  if (seq_dims_supported(dk, dv)) return true;
+  // the wider beam geometries: d_k in {128, 256} x d_v in {128, 256, 512};
+  // channel decay with d_k = 128 only, the plain rule on the square shapes only
+  const bool wide = (dk == 128 || dk == 256) && (dv == 128 || dv == 256 || dv == 512);
+  if (!wide) return false;
+  if (decay_kind == GDN_DECAY_SCALAR) return true;
+  return decay_kind == GDN_DECAY_CHANNEL && dk == 128;
 }
 
 }  // namespace gdn
@@ -26,7 +36,7 @@ int check_shape(const gdn_shape* s) {
   if (s->decay_kind != GDN_DECAY_SCALAR && s->decay_kind != GDN_DECAY_CHANNEL &&
       s->decay_kind != GDN_DECAY_CHANNEL_PLAIN)
     return GDN_EUNSUPPORTED;
-  if (!gdn::dims_supported(s->dk, s->dv)) return GDN_EUNSUPPORTED;
+  if (!gdn::dims_supported(s->dk, s->dv, s->decay_kind)) return GDN_EUNSUPPORTED;
   if (s->H_k < 0 || (s->H_k > 0 && s->H % s->H_k != 0)) return GDN_EINVAL;
   // element counts of the largest arrays must stay far from 2^63
   const double recs = (double)s->L_max * s->R * s->W_max * s->H * (s->dk > s->dv ? s->dk : s->dv);
@@ -75,7 +85,10 @@ int gdn_beam_decode_step(const gdn_shape* shape, const gdn_store* store, int32_t
     return GDN_EINVAL;
   const gdn::StepIO io{parent, q, k, v, alpha, beta, o};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (shape->W_max == 1) return gdn::launch_seq_decode(*shape, *store, t, false, io, s);
+  // one beam per request takes the sequence kernel where it is built; the
+  // wider geometries run it through the beam kernel (the same step at W = 1)
+  if (shape->W_max == 1 && gdn::seq_dims_supported(shape->dk, shape->dv))
+    return gdn::launch_seq_decode(*shape, *store, t, false, io, s);
   return gdn::launch_beam_decode(*shape, *store, t, W_t, io, s);
 }
 
@@ -85,7 +98,7 @@ int gdn_decode_merge_step(const gdn_shape* shape, const gdn_store* store, int32_
   int rc = check_shape(shape);
   if (rc != GDN_OK) return rc;
   if ((rc = check_store(store)) != GDN_OK) return rc;
-  if (shape->W_max != 1) return GDN_EUNSUPPORTED;
+  if (shape->W_max != 1 || !gdn::seq_dims_supported(shape->dk, shape->dv)) return GDN_EUNSUPPORTED;
   if (t < 0 || t >= shape->L_max) return GDN_EINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 16) ||
       !aligned(beta, 16) || !aligned(o, 16))

@@ -28,17 +28,6 @@ struct BeamArgs {
   int Hk, gq;
 };
 
-template <int DK, int DV>
-struct BeamGeom {
-  static_assert(DK == 16 || DK == 32 || DK % 64 == 0, "d_k must be 16, 32 or a multiple of 64");
-  static_assert(DV % 16 == 0, "d_v must be a multiple of 16");
-  static constexpr int RPW = (DV % 32 == 0) ? 32 : 16;  // value rows per wave
-  static constexpr int NW = DV / RPW;                   // waves per workgroup
-  static constexpr int MT = RPW / 16;                   // 16-row MFMA tiles per wave
-  static constexpr int KS = (DK + 31) / 32;             // 32-deep MFMA steps over d_k
-  static constexpr int VPL = 4 * MT;                    // value rows per lane
-};
-
 // First key channel of the 8 consecutive channels that lane group g feeds to
 // MFMA step s.  Any assignment works as long as the A and B operands use the
 // same one; this one gives each lane 16 (d_k >= 64) contiguous channels.

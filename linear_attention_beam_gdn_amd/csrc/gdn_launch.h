@@ -19,7 +19,9 @@ struct StepIO {
   float* o;
 };
 
-bool dims_supported(int dk, int dv);
+// (d_k, d_v) pairs built for a decay kind, and those of the sequence kernel
+bool dims_supported(int dk, int dv, int decay_kind);
+bool seq_dims_supported(int dk, int dv);
 
 // Key heads of a shape (H_k == 0 means one per value head).
 inline int key_heads(const gdn_shape& sh) { return sh.H_k > 0 ? sh.H_k : sh.H; }

@@ -1,9 +1,11 @@
 // Fused shared-context decode step for beams that share one state per
 // request (OneLA §3.4, Figure 5; replay equations of §3.2; ancestry of §3.3).
 //
-// Work split.  One workgroup takes one (request r, head h) and a chunk of
-// beams.  Its NW waves split the d_v axis (RPW value rows each, the B_V tile
-// of §3.4) and each wave keeps its slice of the shared state S0[r,h] in
+// Work split.  One workgroup takes one (request r, head h), a slice of VS
+// value rows (all of d_v up to 128; wider d_v is cut into slices, since every
+// value row's replay is independent given the per-beam dot products, which
+// each slice forms itself) and a chunk of beams.  Its NW waves split the slice (RPW value rows each, the B_V tile
+// of §3.4) and each wave keeps its part of the shared state S0[r,h] in
 // registers for the whole beam chunk, in the A-operand layout of the gfx950
 // bf16 MFMA (16x16x32): S0 is read from memory once per workgroup and reused
 // by every beam of the chunk.  FP32 S0 is split on chip into NPL bf16 planes
@@ -22,9 +24,30 @@
 namespace gdn {
 namespace {
 
+template <int DK, int DV, bool CH = false>
+struct BeamGeom {
+  static_assert(DK == 16 || DK == 32 || DK % 64 == 0, "d_k must be 16, 32 or a multiple of 64");
+  static_assert(DV % 16 == 0, "d_v must be a multiple of 16");
+  // value rows per wave: 16 for d_k > 128, so that a wave's state slice (three
+  // planes of d_k / 32 MFMA steps) stays within its registers
+  static constexpr int RPW = (DK <= 128 && DV % 32 == 0) ? 32 : 16;
+  // value rows per workgroup: wider d_v is split over NVS workgroups.  Up to
+  // eight waves (two per SIMD, 256 registers each); four (one per SIMD, with
+  // the whole register file) for d_k = 256 and for channel decay, whose
+  // lanes also hold their key channels' decays and probe weights
+  static constexpr int VS0 = DK > 128 ? 64 : (CH ? 128 : 256);
+  static constexpr int VS = DV < VS0 ? DV : VS0;
+  static_assert(DV % VS == 0, "d_v must split evenly over value slices");
+  static constexpr int NVS = DV / VS;                   // value slices
+  static constexpr int NW = VS / RPW;                   // waves per workgroup
+  static constexpr int MT = RPW / 16;                   // 16-row MFMA tiles per wave
+  static constexpr int KS = (DK + 31) / 32;             // 32-deep MFMA steps over d_k
+  static constexpr int VPL = 4 * MT;                    // value rows per lane
+};
+
 template <int DK, int DV, bool CH, int NPL>
-__global__ __launch_bounds__((BeamGeom<DK, DV>::NW * 64)) void k_beam_decode(BeamArgs a) {
-  using G = BeamGeom<DK, DV>;
+__global__ __launch_bounds__((BeamGeom<DK, DV, CH>::NW * 64)) void k_beam_decode(BeamArgs a) {
+  using G = BeamGeom<DK, DV, CH>;
   constexpr int A = CH ? DK : 1;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -37,23 +60,25 @@ __global__ __launch_bounds__((BeamGeom<DK, DV>::NW * 64)) void k_beam_decode(Bea
   const int nblk = gridDim.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
   const int chunk_id = bid % a.nchunk;
-  const int rh = bid / a.nchunk;
+  const int vsl = (bid / a.nchunk) % G::NVS;
+  const int rh = bid / (a.nchunk * G::NVS);
   const int h = rh % a.H;
   const int r = rh / a.H;
   const int b_begin = chunk_id * a.chunk;
   const int b_end = min(b_begin + a.chunk, a.Wt);
   const int t = a.t;
-  const int dv0 = w * G::RPW + g * G::VPL;  // first value row held by this lane
+  const int vs0 = vsl * G::VS;                    // first value row of the slice
+  const int dv0 = vs0 + w * G::RPW + g * G::VPL;  // first value row held by this lane
 
   // ---- this wave's slice of S0[r, h] as bf16 planes in MFMA A layout.
-  // A row m of tile mt is value row w*RPW + (m/4)*VPL + mt*4 + m%4, so that
+  // A row m of tile mt is value row vs0 + w*RPW + (m/4)*VPL + mt*4 + m%4, so that
   // C row 4g+i of tile mt lands on value row dv0 + mt*4 + i.
   u32x4 As[G::MT][G::KS][NPL];
   {
     const float* S = a.S + ((size_t)r * a.H + h) * DK * DV;
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt) {
-      const int col = w * G::RPW + (c >> 2) * G::VPL + mt * 4 + (c & 3);
+      const int col = vs0 + w * G::RPW + (c >> 2) * G::VPL + mt * 4 + (c & 3);
 #pragma unroll
       for (int s = 0; s < G::KS; ++s) {
         const int k0 = kchunk<DK>(g, s);
@@ -65,7 +90,10 @@ __global__ __launch_bounds__((BeamGeom<DK, DV>::NW * 64)) void k_beam_decode(Bea
     }
   }
 
-  const bool anc_writer = (h == 0) && (w == 0) && (g == 0);
+  // the first value slice writes what is not per value row: ancestry, the
+  // record key (once per key head) and the record decay
+  const bool slice_writer = vsl == 0;
+  const bool anc_writer = (h == 0) && slice_writer && (w == 0) && (g == 0);
   const int hk = h / a.gq;
   const bool key_writer = h % a.gq == 0;
 
@@ -294,7 +322,7 @@ __global__ __launch_bounds__((BeamGeom<DK, DV>::NW * 64)) void k_beam_decode(Bea
         *reinterpret_cast<f32x4*>(a.o + tok * DV + dv0 + mt * 4) = out;
         *reinterpret_cast<f32x4*>(a.rec_delta + rec_t * DV + dv0 + mt * 4) = d;
       }
-      if (w == 0 && klive<DK>(g)) {
+      if (slice_writer && w == 0 && klive<DK>(g)) {
 #pragma unroll
         for (int s = 0; s < G::KS; ++s) {
           const int k0 = kchunk<DK>(g, s);
@@ -338,12 +366,13 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO
   a.Wt = Wt;
   a.Hk = key_heads(sh);
   a.gq = sh.H / a.Hk;
-  a.chunk = pick_chunk(sh.R * sh.H, Wt, 1 << 30, 2048);
+  constexpr int NVS = BeamGeom<DK, DV, CH>::NVS;
+  a.chunk = pick_chunk(sh.R * sh.H * NVS, Wt, 1 << 30, 2048);
   a.nchunk = (Wt + a.chunk - 1) / a.chunk;
-  const long grid = (long)sh.R * sh.H * a.nchunk;
+  const long grid = (long)sh.R * sh.H * NVS * a.nchunk;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
   hipLaunchKernelGGL((k_beam_decode<DK, DV, CH, NPL>), dim3((unsigned)grid),
-                     dim3(BeamGeom<DK, DV>::NW * 64), 0, stream, a);
+                     dim3(BeamGeom<DK, DV, CH>::NW * 64), 0, stream, a);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
@@ -365,7 +394,16 @@ int launch_beam_decode(const gdn_shape& sh, const gdn_store& st, int t, int Wt, 
   GDN_CASE(32, 32)
   GDN_CASE(64, 64)
   GDN_CASE(128, 128)
+  GDN_CASE(128, 256)
+  GDN_CASE(128, 512)
 #undef GDN_CASE
+  // d_k = 256: the scalar rule only (channel decay would hold d_k decays and
+  // probe weights per lane on top of the state slice)
+  if (!ch && sh.dk == 256) {
+    if (sh.dv == 128) return launch<256, 128, false>(sh, st, t, Wt, io, stream);
+    if (sh.dv == 256) return launch<256, 256, false>(sh, st, t, Wt, io, stream);
+    if (sh.dv == 512) return launch<256, 512, false>(sh, st, t, Wt, io, stream);
+  }
   return GDN_EUNSUPPORTED;
 }
 

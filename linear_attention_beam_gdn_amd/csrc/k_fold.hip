@@ -7,10 +7,12 @@
 // back into the dense base; Figure 5: the merge writes back base tiles) and
 // the materialisation of any beam's state.
 //
-// One workgroup per (item, head): each thread owns RPG rows x 4 columns of
-// the [d_k][d_v] state in registers, streams them in and out with 16-byte
-// accesses, and applies every record to them; the key entries and decays of
-// a record are the same for a whole row, the update vector for a column.
+// One workgroup per (item, head, row slice): each thread owns RPG rows x 4
+// columns of the [d_k][d_v] state in registers, streams them in and out with
+// 16-byte accesses, and applies every record to them; the key entries and
+// decays of a record are the same for a whole row, the update vector for a
+// column.  States up to 128 x 128 take one slice; wider ones (d_v = 512 or
+// d_k = 256) are cut into NSL slices of d_k rows.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -33,10 +35,14 @@ struct FoldArgs {
 template <int DK, int DV>
 struct FoldGeom {
   static constexpr int C4 = DV / 4;
+  static_assert(C4 <= 256, "d_v of at most 1024");
   static constexpr int NRG0 = 256 / C4;
   static constexpr int NRG = NRG0 < DK ? NRG0 : DK;
   static_assert(DK % NRG == 0, "d_k must split evenly over row groups");
-  static constexpr int RPG = DK / NRG;
+  static constexpr int RPG0 = DK / NRG;
+  static constexpr int RPG = RPG0 < 16 ? RPG0 : 16;  // rows per thread
+  static constexpr int NSL = DK / (NRG * RPG);       // row slices
+  static_assert(NSL * NRG * RPG == DK, "d_k must split evenly over row slices");
   static constexpr int NT = C4 * NRG;
 };
 
@@ -46,9 +52,11 @@ __global__ __launch_bounds__((FoldGeom<DK, DV>::NT)) void k_fold(FoldArgs a) {
   constexpr int A = CH ? DK : 1;
   const int tid = threadIdx.x;
   const int h = blockIdx.x % a.H;
-  const int item = blockIdx.x / a.H;
+  const int sl = (blockIdx.x / a.H) % G::NSL;
+  const int item = blockIdx.x / (a.H * G::NSL);
   const int c4 = tid % G::C4;
   const int rg = tid / G::C4;
+  const int row0 = (sl * G::NRG + rg) * G::RPG;  // this thread's first row
   int r = item, b = a.beam;
   if (a.rb) {
     r = a.rb[2 * item];
@@ -64,7 +72,7 @@ __global__ __launch_bounds__((FoldGeom<DK, DV>::NT)) void k_fold(FoldArgs a) {
   f32x4 st[G::RPG];
 #pragma unroll
   for (int i = 0; i < G::RPG; ++i)
-    st[i] = *reinterpret_cast<const f32x4*>(src + (size_t)(rg * G::RPG + i) * DV + c4 * 4);
+    st[i] = *reinterpret_cast<const f32x4*>(src + (size_t)(row0 + i) * DV + c4 * 4);
 
   const int32_t* arow = a.anc + (((size_t)t * a.R + r) * a.Wm + b) * a.L;
   for (int j = 0; j <= t; ++j) {
@@ -75,7 +83,7 @@ __global__ __launch_bounds__((FoldGeom<DK, DV>::NT)) void k_fold(FoldArgs a) {
     const float aj0 = CH ? 0.f : a.rec_alpha[rj];
 #pragma unroll
     for (int i = 0; i < G::RPG; ++i) {
-      const int row = rg * G::RPG + i;
+      const int row = row0 + i;
       const float kj = bf16_at(a.rec_k[rjk * DK + row]);
       const float aj = CH ? a.rec_alpha[rj * A + row] : aj0;
       st[i] = apply_record(st[i], aj, kj, dj);
@@ -83,7 +91,7 @@ __global__ __launch_bounds__((FoldGeom<DK, DV>::NT)) void k_fold(FoldArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < G::RPG; ++i)
-    *reinterpret_cast<f32x4*>(dst + (size_t)(rg * G::RPG + i) * DV + c4 * 4) = st[i];
+    *reinterpret_cast<f32x4*>(dst + (size_t)(row0 + i) * DV + c4 * 4) = st[i];
 }
 
 template <int DK, int DV, bool CH>
@@ -106,7 +114,7 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, const int32_t* rb, i
   a.Hk = key_heads(sh);
   a.gq = sh.H / a.Hk;
   a.dst_per_item = dst_per_item ? 1 : 0;
-  const long grid = (long)n * sh.H;
+  const long grid = (long)n * sh.H * FoldGeom<DK, DV>::NSL;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
   hipLaunchKernelGGL((k_fold<DK, DV, CH>), dim3((unsigned)grid), dim3(FoldGeom<DK, DV>::NT), 0,
                      stream, a);
@@ -126,7 +134,14 @@ int launch_fold(const gdn_shape& sh, const gdn_store& st, int t, const int32_t* 
   GDN_CASE(32, 32)
   GDN_CASE(64, 64)
   GDN_CASE(128, 128)
+  GDN_CASE(128, 256)
+  GDN_CASE(128, 512)
 #undef GDN_CASE
+  if (!ch && sh.dk == 256) {
+    if (sh.dv == 128) return launch<256, 128, false>(sh, st, t, rb, beam, n, src, dst, dst_per_item, stream);
+    if (sh.dv == 256) return launch<256, 256, false>(sh, st, t, rb, beam, n, src, dst, dst_per_item, stream);
+    if (sh.dv == 512) return launch<256, 512, false>(sh, st, t, rb, beam, n, src, dst, dst_per_item, stream);
+  }
   return GDN_EUNSUPPORTED;
 }
 

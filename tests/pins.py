@@ -206,8 +206,12 @@ def _unrolled_state(inp, t, r, b, h, channel):
     return Sx
 
 
-def pin_unrolled_closed_form(channel=False, square=False):
-    inp = small(channel=channel, seed=31, **(dict(dk=8, dv=8) if square else {}))
+_DIMS = {"rect": {}, "square": dict(dk=8, dv=8), "wide_value": dict(dk=4, dv=12)}
+
+
+def pin_unrolled_closed_form(channel=False, square=False, dims=None):
+    dims = dims or ("square" if square else "rect")
+    inp = small(channel=channel, seed=31, **_DIMS[dims])
     ref = O.beam_decode(inp["S0"], inp["steps"])
     R, H = inp["S0"].shape[:2]
     for t in range(len(inp["steps"])):
@@ -221,8 +225,9 @@ def pin_unrolled_closed_form(channel=False, square=False):
                 assert rel(ref["o"][t][r, b, h], q @ Sx) < 1e-12
 
 
-def pin_replay_equals_eager(channel=False, seed=41, square=False):
-    inp = small(channel=channel, seed=seed, **(dict(dk=8, dv=8) if square else {}))
+def pin_replay_equals_eager(channel=False, seed=41, square=False, dims=None):
+    dims = dims or ("square" if square else "rect")
+    inp = small(channel=channel, seed=seed, **_DIMS[dims])
     a = O.beam_decode(inp["S0"], inp["steps"])
     b = O.beam_decode_replay(inp["S0"], inp["steps"])
     for t in range(len(inp["steps"])):
@@ -421,6 +426,10 @@ ALL_PINS = {
     "replay_scalar": lambda: pin_replay_equals_eager(False),
     "replay_square_channel": lambda: pin_replay_equals_eager(True, square=True),
     "replay_channel": lambda: pin_replay_equals_eager(True),
+    # d_k < d_v, the orientation of the wider suite geometries (d_v up to 512 on d_k = 128)
+    "unrolled_wide_value_scalar": lambda: pin_unrolled_closed_form(False, dims="wide_value"),
+    "unrolled_wide_value_channel": lambda: pin_unrolled_closed_form(True, dims="wide_value"),
+    "replay_wide_value_scalar": lambda: pin_replay_equals_eager(False, dims="wide_value"),
     "kda_uniform_scalar": pin_kda_uniform_equals_scalar,
     "sequence_single_beam": pin_sequence_equals_single_beam,
     "plain_unrolled": pin_plain_unrolled_closed_form,

@@ -67,6 +67,10 @@ def test_decode_validation(L):
     assert decode(L, sh=shape(L_max=B.GDN_MAX_STEPS + 1)) == E
     assert decode(L, sh=shape(dk=96, dv=96)) == U
     assert decode(L, sh=shape(dk=128, dv=64)) == U
+    assert decode(L, sh=shape(dk=256, dv=64)) == U
+    assert decode(L, sh=shape(dk=512, dv=512)) == U
+    assert decode(L, sh=shape(dk=256, dv=128, decay_kind=1)) == U  # channel decay: d_k = 128 only
+    assert decode(L, sh=shape(dk=128, dv=256, decay_kind=2, W_max=1)) == U  # plain: square only
     assert decode(L, sh=shape(decay_kind=2)) == U  # the plain (RWKV6) rule: sequences only
     assert decode(L, sh=shape(decay_kind=3)) == U
     assert decode(L, sh=shape(H=4, H_k=3)) == E  # key heads must divide the value heads
@@ -101,8 +105,8 @@ def test_materialize_and_merge_validation(L):
     assert g(n_rec=5) == E
     assert g(beam=-1) == E
     assert g(beam=8) == E
-    bad = shape(dk=48, dv=48)
-    assert L.gdn_log_merge(ctypes.byref(bad), ctypes.byref(st), 1, 0, None) == B.GDN_EUNSUPPORTED
+    for bad in (shape(dk=48, dv=48), shape(dk=256, dv=256, decay_kind=1)):
+        assert L.gdn_log_merge(ctypes.byref(bad), ctypes.byref(st), 1, 0, None) == B.GDN_EUNSUPPORTED
 
 
 def test_binding_refuses_host_tensors():
@@ -124,6 +128,7 @@ def test_decode_merge_validation(L):
 
     assert dm(sh=shape(W_max=8)) == U  # beams: merge with gdn_log_merge instead
     assert dm(sh=shape(W_max=1, dk=96, dv=96)) == U
+    assert dm(sh=shape(W_max=1, dk=128, dv=256)) == U  # the sequence kernel: square shapes
     assert dm(t=-1) == E
     assert dm(t=4) == E
     for name in ("q", "k", "v", "alpha", "beta", "o"):

@@ -42,6 +42,19 @@ def test_large_beam_step_bytes_per_beam_gather():
     assert tot - anc == 4 * 286_785_536 + 6 * 101_187_584
 
 
+def test_shared_key_heads_step_bytes():
+    # the same beams with 32 value heads on 16 key heads: q, k and the record
+    # key (4 d_k + 2 d_k bytes per beam, 2 d_k per ancestor) counted per key head
+    kw = dict(R=8, H=32, dk=128, dv=128, W_t=512)
+    tot = sum(A.beam_step_bytes(t=t, Hk=16, **kw) for t in range(4))
+    anc = sum(4 * 8 * 512 * 2 * t for t in range(4))
+    assert tot - anc == 4 * 236_453_888 + 6 * 84_410_368
+    for t in range(4):
+        assert A.beam_step_bytes(t=t, Hk=32, **kw) == A.beam_step_bytes(t=t, **kw)
+        assert A.beam_step_bytes(t=t, Hk=32, channel_decay=True, **kw) == \
+            A.beam_step_bytes(t=t, channel_decay=True, **kw)
+
+
 def test_unique_ancestors():
     row = np.array([[0, 1], [0, 1], [0, 2], [3, 2]])
     assert A.unique_ancestors(row, 4) == 2 + 2

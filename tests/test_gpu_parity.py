@@ -52,6 +52,17 @@ def test_large_beam_workload_sampled():
                label="large-beam")
 
 
+def test_shared_key_heads_workload_sampled():
+    # full size, 32 value heads on 16 key heads; heads 0, 1 share key head 0
+    check_beam(configs.SHARED_KEYS.inputs(), False, requests=[0, 7], heads=[0, 1, 17, 30],
+               label="large-beam shared key heads")
+
+
+def test_wide_state_workload_sampled():
+    # full size, d_k = 256, d_v = 512 (four value slices per (request, head))
+    check_beam(configs.WIDE.inputs(), False, requests=[3], heads=[0, 15], label="wide state")
+
+
 def test_kda_workload_sampled():
     check_beam(configs.KDA.inputs(), True, requests=[0, 15], heads=[0, 31], label="kda")
 
@@ -136,6 +147,46 @@ def test_value_heads_sharing_key_heads(dims, channel, Hk):
     S = B.materialize(store, 3, torch.from_numpy(pairs).cuda()).cpu().numpy()
     ref = O.beam_states(inp["S0"], inp["steps"], 3, [tuple(p) for p in pairs])
     assert rel_states(S, ref) <= TOL
+
+
+@pytest.mark.parametrize("dk,dv,channel,Hk", [(128, 256, False, 2), (128, 512, False, 1), (256, 128, False, 2),
+                                               (256, 256, False, 1), (256, 512, False, 1), (128, 256, True, 2),
+                                               (128, 512, True, 1)])
+def test_wider_geometries(dk, dv, channel, Hk):
+    """Operator-suite head dims beyond 128 (OneLA §4.1: K up to 256, V up to
+    512): d_v cut into value slices over workgroups, and the fold's row
+    slices, for materialisation and the in-place merge."""
+    H = 2
+    inp = synth.make_inputs(R=2, H=H, dk=dk, dv=dv, W=37, L=5, s0_std=0.05, seed=500 + dk + dv // 8 + Hk,
+                            parents="topk", channel_decay=channel, widths=[37, 29, 37, 20, 33], Hk=Hk)
+    store, _, _ = check_beam(inp, channel, label=f"dk={dk} dv={dv} Hk={Hk} ch={channel}")
+    pairs = np.array([[0, 3], [1, 19], [1, 32]], np.int32)
+    S = B.materialize(store, 4, torch.from_numpy(pairs).cuda()).cpu().numpy()
+    ref = O.beam_states(inp["S0"], inp["steps"], 4, [tuple(p) for p in pairs])
+    assert rel_states(S, ref) <= TOL
+    B.log_merge(store, 5, 7)  # every request's base folded with beam 7's chain
+    merged = store.S.cpu().numpy()
+    ref = O.beam_states(inp["S0"], inp["steps"], 4, [(0, 7), (1, 7)])
+    assert rel_states(merged, ref) <= TOL
+
+
+def test_wide_state_sequences():
+    """One beam per request with d_k = 256, d_v = 512: the step runs through
+    the beam kernel at W = 1, the log merge through the fold."""
+    R, H, dk, dv, T, M = 3, 2, 256, 512, 7, 3
+    seq = synth.make_sequence_inputs(R=R, H=H, dk=dk, dv=dv, T=T, s0_std=0.05, seed=19)
+    ref = O.sequence_decode(seq["S0"], seq["tokens"], M)
+    store = B.Store(R, 1, H, dk, dv, M, S=torch.from_numpy(seq["S0"]).cuda())
+    zero = torch.zeros(R, 1, dtype=torch.int32, device="cuda")
+    for i in range(T):
+        t = i % M
+        d = B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")})
+        o = B.decode_step(store, t, 1, zero, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        assert rel_slices(o[:, 0].cpu().numpy().reshape(R * H, dv), ref["o"][i]) <= TOL
+        if t == M - 1:
+            B.log_merge(store, M, 0)
+            S = store.S.cpu().numpy().reshape(R * H, 1, dk, dv)
+            assert rel_states(S, ref["bases"][i // M][:, None]) <= TOL
 
 
 @pytest.mark.parametrize("kind", ["scalar", "channel", "plain"])
