@@ -84,8 +84,9 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // their parent's position in the previous step's order), and writes
 //   s_tab[position]  = {beam, slot_0, slot_1, slot_2},
 //   s_slot_hi[(j - 3) * kMaxChunkF + position] = slot_j for 3 <= j < T,
-//   anc row T of every beam (h == 0 workgroups), with the beam's position in
-//   the unused last entry for the next step.
+//   anc row T of every beam (when `anc_writer`: one workgroup per request
+//   and chunk), with the beam's position in the unused last entry for the
+//   next step.
 // The order only decides which lanes compute a beam, never its result.
 //
 // Memory: the parent pointers and, for T >= 2, the whole previous-step
@@ -95,7 +96,7 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // follows.  `scratch` (scratch_bytes, 16-byte aligned) holds the bucket
 // counts and the staged block and is free for other use afterwards.
 template <int T, class Mid>
-__device__ __forceinline__ void build_schedule(const BeamArgs& a, int r, int h, int b_begin, int nb, int lane,
+__device__ __forceinline__ void build_schedule(const BeamArgs& a, int r, bool anc_writer, int b_begin, int nb, int lane,
                                                int scratch_bytes, uint8_t* scratch, u32x4* s_tab, int* s_slot_hi,
                                                Mid mid) {
   constexpr int TT = T > 0 ? T : 1;
@@ -192,7 +193,7 @@ __device__ __forceinline__ void build_schedule(const BeamArgs& a, int r, int h, 
                              (uint32_t)slot[qi][T > 2 ? 2 : 0]};
 #pragma unroll
       for (int j = 3; j < T; ++j) s_slot_hi[(j - 3) * kMaxChunkF + pos[qi]] = slot[qi][j];
-      if (h == 0) {
+      if (anc_writer) {
         int32_t* crow = a.anc + (((size_t)T * a.R + r) * a.Wm + b_begin + i) * a.L;
 #pragma unroll
         for (int j = 0; j < T; ++j) crow[j] = slot[qi][j];

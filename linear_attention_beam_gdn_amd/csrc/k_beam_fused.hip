@@ -2,13 +2,17 @@
 // Figure 5; replay equations of §3.2; ancestry index of §3.3), built as a
 // three-role pipeline for gfx950.
 //
-// Work split.  A workgroup takes one (request r, head h) and a chunk of its
-// beams, 16 beams (one MFMA N block) per tile, and runs three kinds of wave:
+// Work split.  A workgroup takes one (request r, head h), a slice of at most
+// 128 value rows (d_v = 256 and 512 take two and four slices, each forming
+// the per-beam dot products itself) and a chunk of its beams, 16 beams (one
+// MFMA N block) per tile, and runs three kinds of wave:
 //
 // * Two DMA waves, taking alternate tiles.  Wave 0 builds the chunk's
 //   ancestry slot table in LDS (its inputs in one batch of loads, barrier Q,
 //   then the sort, barrier P); wave 1 meanwhile stages S0[r, h] into LDS,
-//   which the consumers split into planes between barriers S and A.  Both
+//   which the consumers split into planes between barriers S and A (with
+//   d_k = 256 the slice does not fit beside the tile ring, and the consumers
+//   load their part of it from HBM at the start instead).  Both
 //   then stream every tile's q, k, v, alpha, beta and, for each beam, the
 //   keys and decays of its T ancestral records straight from HBM into a ring
 //   of NBUF LDS buffers with LDS-DMA loads (global_load_lds, no register
@@ -25,16 +29,17 @@
 //   so the consumers' replay is one FMA per record and value row.  It
 //   publishes c_0, beta_t, k_t . q_t and the 2T record weights in the tile's
 //   LDS buffer.
-// * Consumer waves (d_v / 16 of them, two per SIMD for d_v = 128).  Each holds
-//   its 16-row slice of the shared state S0[r, h] in registers for the whole
-//   chunk as three bf16 planes (hi + mid + lo, each the RNE of the FP32
-//   residual) in the MFMA A layout, so S0 is read once per workgroup and
-//   reused by every beam.  Per tile: S0^T [q | k] on the matrix cores (q and
-//   k are bf16, so every plane product is exact; FP32 accumulation), the
-//   replay on its value rows with the ancestral update vectors delta_j
-//   (loaded into registers one tile ahead, each wave its own rows), then
-//   delta_t and o_t, stored with 64-byte contiguous writes per beam, plus the
-//   appended record.  Two waves per SIMD hide each other's latencies.
+// * Consumer waves (one per 16 value rows of the slice, two per SIMD for
+//   128 rows).  Each holds its 16-row part of the shared state S0[r, h] in
+//   registers for the whole chunk as three bf16 planes (hi + mid + lo, each
+//   the RNE of the FP32 residual; two for d_k = 256) in the MFMA A layout,
+//   so S0 is read once per workgroup and reused by every beam.  Per tile:
+//   S0^T [q | k] on the matrix cores (q and k are bf16, so every plane
+//   product is exact; FP32 accumulation), the replay on its value rows with
+//   the ancestral update vectors delta_j (loaded into registers one tile
+//   ahead, each wave its own rows), then delta_t and o_t, stored with 64-byte
+//   contiguous writes per beam, plus the appended record (by the first value
+//   slice).  Two waves per SIMD hide each other's latencies.
 //
 // Schedule.  With one chunk per (r, h), the beams are taken in the depth-
 // first order of the beam tree (lexicographic in their ancestry rows), so that
@@ -62,14 +67,20 @@ using namespace fused;
 template <int DK, int DV, int T>
 struct FusedGeom {
   static_assert(DK % 32 == 0 && DV % 32 == 0, "the fused kernel needs d_k, d_v multiples of 32");
-  static constexpr int NC = DV / 16;       // consumer waves, 16 value rows each
+  // value rows per workgroup: d_v up to 128 in one slice, wider d_v in NVS
+  // slices of 128 (every value row's replay is independent once the per-beam
+  // dot products are known; each slice's dot wave forms them itself)
+  static constexpr int VS = DV < 128 ? DV : 128;
+  static_assert(DV % VS == 0, "d_v must split evenly over value slices");
+  static constexpr int NVS = DV / VS;
+  static constexpr int NC = VS / 16;       // consumer waves, 16 value rows each
   static constexpr int WDMA = NC;          // wave index of the first DMA wave
   static constexpr int NDMA = 2;           // DMA waves (tile p belongs to DMA wave p % 2)
   static constexpr int WDOT = NC + NDMA;   // wave index of the dot wave
   static constexpr int NT = (NC + NDMA + 1) * 64;
   static constexpr int KS = DK / 32;       // 32-deep MFMA steps over d_k
   static constexpr int QB = 16 * DK * 2;   // bytes of a q (or k) tile
-  static constexpr int VB = 16 * DV * 2;   // bytes of a v tile
+  static constexpr int VB = 16 * VS * 2;   // bytes of a v tile (the slice's value rows)
   static constexpr int NSM = (2 + T) * 16 > 64 ? 2 : 1;  // dword DMAs: alpha_t, beta_t, alpha_j
   static constexpr int SMB = NSM * 256;
   static constexpr int RKB = 16 * DK * 2;  // keys of one record depth
@@ -82,14 +93,18 @@ struct FusedGeom {
   static constexpr int NBUF0 = (kLdsBytes - SLOTB) / BUF;
   static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
   static_assert(NBUF >= 3, "tile buffers do not fit in LDS");
-  // S0[r, h] is staged in LDS past the first two tile buffers (which the
-  // prologue fills first) until the consumers have split it into planes; the
-  // schedule's scratch (bucket counts, staged ancestry rows) is the first two.
-  static constexpr int S0B = DK * DV * 4, OS0 = 2 * BUF;
-  static constexpr int RINGB = NBUF * BUF > OS0 + S0B ? NBUF * BUF : OS0 + S0B;
+  // The slice of S0[r, h] is staged in LDS past the first two tile buffers
+  // (which the prologue fills first) until the consumers have split it into
+  // planes, when it fits (d_k <= 128); with d_k = 256 the consumers load it
+  // from HBM themselves.  The schedule's scratch (bucket counts, staged
+  // ancestry rows) is the first two buffers.
+  static constexpr int S0B = DK * VS * 4, OS0 = 2 * BUF;
+  static constexpr bool S0_LDS = OS0 + S0B + SLOTB <= kLdsBytes;
+  static constexpr int RINGB = (S0_LDS && OS0 + S0B > NBUF * BUF) ? OS0 + S0B : NBUF * BUF;
   static constexpr int LDS = RINGB + SLOTB;
   static_assert(LDS <= kLdsBytes, "LDS layout does not fit");
-  static_assert(S0B % 1024 == 0, "S0 is staged in whole DMA blocks");
+  static_assert(!S0_LDS || S0B % 1024 == 0, "S0 is staged in whole DMA blocks");
+  static_assert(NC == 2 * KS || NC == KS, "the key row is appended by the consumer waves in halves or wholes");
   // LDS-DMA instructions the DMA wave issues per tile
   static constexpr int OPT = 2 * (QB / 1024) + VB / 1024 + NSM + T * (RKB / 1024);
   static_assert(QB % 1024 == 0 && VB % 1024 == 0, "tile arrays must be whole DMA blocks");
@@ -101,7 +116,10 @@ template <int DK, int DV, int T>
 __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamArgs a) {
   using G = FusedGeom<DK, DV, T>;
   constexpr int KS = G::KS;
-  constexpr int NPL = 3;
+  // bf16 planes of S0: three (to about 2^-27 relative), two for d_k = 256
+  // (to about 2^-18: the registers of a 16-row slice of 256 key channels, and
+  // a third less matrix-core work where it is close to the HBM time)
+  constexpr int NPL = DK > 128 ? 2 : 3;
   constexpr int TT = T > 0 ? T : 1;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
   u32x4* s_tab = reinterpret_cast<u32x4*>(smem + G::RINGB);                    // [position]
@@ -115,9 +133,14 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   const int nblk = gridDim.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
   const int chunk_id = bid % a.nchunk;
-  const int rh = bid / a.nchunk;
+  const int vsl = (bid / a.nchunk) % G::NVS;  // value slice
+  const int rh = bid / (a.nchunk * G::NVS);
   const int h = rh % a.H;
   const int r = rh / a.H;
+  const int vs0 = vsl * G::VS;  // first value row of the slice
+  // the first slice writes what is not per value row: ancestry, record keys
+  // and decays
+  const bool slice0 = vsl == 0;
   const int b_begin = chunk_id * a.chunk;
   const int b_end = min(b_begin + a.chunk, a.Wt);
   const int nb = b_end - b_begin;
@@ -135,15 +158,21 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     // ============================================================ DMA waves
     const int dw = w - G::WDMA;  // this wave owns tiles p with p % 2 == dw
     const int cg = lane >> 4;
-    // S0[r, h] into LDS (wave 1), after the schedule's loads have gone out
+    // the slice of S0[r, h] into LDS as [d_k][VS] (wave 1), after the
+    // schedule's loads have gone out; 256 floats per DMA instruction
     auto stage_s0 = [&] {
-      const float* S = a.S + ((size_t)r * a.H + h) * DK * DV;
+      if constexpr (G::S0_LDS) {
+        const float* S = a.S + ((size_t)r * a.H + h) * DK * DV + vs0;
 #pragma unroll
-      for (int m = 0; m < G::S0B / 1024; ++m) dma16(S + m * 256 + lane * 4, smem + G::OS0 + m * 1024);
+        for (int m = 0; m < G::S0B / 1024; ++m) {
+          const int e0 = m * 256 + lane * 4;
+          dma16(S + (size_t)(e0 / G::VS) * DV + e0 % G::VS, smem + G::OS0 + m * 1024);
+        }
+      }
     };
     if (T > 0) {
       if (dw == 0) {
-        build_schedule<T>(a, r, h, b_begin, nb, lane, G::OS0, smem, s_tab, s_slot_hi,
+        build_schedule<T>(a, r, h == 0 && slice0, b_begin, nb, lane, G::OS0, smem, s_tab, s_slot_hi,
                           [] { lds_barrier(); });  // Q inside, once its loads have arrived
       } else {
         lds_barrier();  // Q
@@ -170,7 +199,7 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
       const size_t tok_k = ((size_t)r * a.Wt + b_begin + ib) * a.Hk + h / a.gq;  // its key head
       const uint16_t* qrow = a.q + tok_k * DK;
       const uint16_t* krow = a.k + tok_k * DK;
-      const uint16_t* vrow = a.v + tok * DV;
+      const uint16_t* vrow = a.v + tok * DV + vs0;
 #pragma unroll
       for (int m = 0; m < G::QB / 1024; ++m) dma16(qrow + (m * 4 + cg) * 8, buf + G::OQ + m * 1024);
 #pragma unroll
@@ -283,13 +312,22 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   }
 
   // ============================================================ consumers
-  // This wave's slice of S0[r, h] as bf16 planes in the MFMA A layout: lane
-  // (g, c) holds key channels 32s + 8g .. +7 of value row 16w + c, so C row
-  // 4g + i is value row 16w + 4g + i.
-  // A DMA wave stages S0 in LDS; the planes are formed between barriers S
-  // and A.
+  // This wave's part of S0[r, h] as bf16 planes in the MFMA A layout: lane
+  // (g, c) holds key channels 32s + 8g .. +7 of value row vs0 + 16w + c, so
+  // C row 4g + i is value row vs0 + 16w + 4g + i.
+  // A DMA wave stages the slice in LDS (d_k <= 128), or each lane loads its
+  // entries from HBM here, overlapping the schedule build (d_k = 256); the
+  // planes are formed between barriers S and A.
+  float s0x[G::S0_LDS ? 1 : KS][8];
+  if constexpr (!G::S0_LDS) {
+    const float* Sg = a.S + ((size_t)r * a.H + h) * DK * DV + vs0 + w * 16 + c;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s0x[s][e] = Sg[(size_t)(s * 32 + g * 8 + e) * DV];
+  }
   if (T > 0) lds_barrier();  // Q
-  const int row0 = w * 16 + 4 * g;  // first of this lane's 4 value rows
+  const int row0 = vs0 + w * 16 + 4 * g;  // first of this lane's 4 value rows
 
   // Store windows over the chunk's beams [b_begin, b_end): a lane whose beam
   // is past the chunk (last tile) lands outside its window.
@@ -303,8 +341,9 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   const bool key_writer = h % a.gq == 0;
   const __amdgpu_buffer_rsrc_t w_k = store_window(a.rec_k + rec0k * DK, (nb - 1) * sk + DK * 2);
   const __amdgpu_buffer_rsrc_t w_a = store_window(a.rec_alpha + rec0, (nb - 1) * sa + 4);
-  // this wave's share of the appended key row: 4 channels per lane
-  const int ks = w >> 1, kh = w & 1;
+  // this wave's share of the appended key row: 4 channels per lane (8 when
+  // there are as many consumer waves as 32-channel steps)
+  const int ks = G::NC == 2 * KS ? w >> 1 : w, kh = G::NC == 2 * KS ? w & 1 : 0;
 
   // ancestral update vectors of one tile, this lane's 4 rows of beam c
   auto load_deltas = [&](int p, f32x4* d) {
@@ -327,15 +366,18 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   load_deltas(0, dnext);  // in flight while tile 0 arrives
   lds_barrier();  // S: S0 staged
   u32x4 As[KS][NPL];
-  {
+  if constexpr (G::S0_LDS) {
     const float* S = reinterpret_cast<const float*>(smem + G::OS0);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = S[(s * 32 + g * 8 + e) * DV + w * 16 + c];
+      for (int e = 0; e < 8; ++e) x[e] = S[(s * 32 + g * 8 + e) * G::VS + w * 16 + c];
       split_planes<NPL>(x, As[s]);
     }
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) split_planes<NPL>(s0x[s], As[s]);
   }
   lds_barrier();  // A: tile 0 resident
   lds_barrier();  // 0
@@ -402,12 +444,14 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
 #pragma unroll
     for (int s = 1; s < KS; ++s)
       if (ks == s) kk = kf[s];
-    __builtin_amdgcn_raw_buffer_store_b64(kh ? u32x2{kk[2], kk[3]} : u32x2{kk[0], kk[1]}, w_k,
-                                          live && key_writer ? ib * sk + (ks * 32 + g * 8 + kh * 4) * 2 : kOutside,
-                                          0, 0);
+    const int off_k = live && key_writer && slice0 ? ib * sk + (ks * 32 + g * 8 + kh * 4) * 2 : kOutside;
+    if constexpr (G::NC == 2 * KS)
+      __builtin_amdgcn_raw_buffer_store_b64(kh ? u32x2{kk[2], kk[3]} : u32x2{kk[0], kk[1]}, w_k, off_k, 0, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b128(kk, w_k, off_k, 0, 0);
     const float at = *reinterpret_cast<const float*>(buf + G::OS + c * 4);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(at), w_a,
-                                          (live && w == G::NC - 1 && g == 0) ? ib * sa : kOutside, 0, 0);
+                                          (live && slice0 && w == G::NC - 1 && g == 0) ? ib * sa : kOutside, 0, 0);
     lds_barrier();  // it + 1
   }
 }
@@ -437,13 +481,17 @@ int launch(const gdn_shape& sh, const gdn_store& st, int Wt, const StepIO& io, h
   a.Hk = key_heads(sh);
   a.gq = sh.H / a.Hk;
   // one workgroup per compute unit: the tile ring takes most of its LDS
-  a.chunk = pick_chunk(sh.R * sh.H, Wt, kMaxChunkF, cu_count());
+  a.chunk = pick_chunk(sh.R * sh.H * G::NVS, Wt, kMaxChunkF, cu_count());
   a.nchunk = (Wt + a.chunk - 1) / a.chunk;
-  const long grid = (long)sh.R * sh.H * a.nchunk;
+  const long grid = (long)sh.R * sh.H * G::NVS * a.nchunk;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
   hipLaunchKernelGGL((k_beam_fused<DK, DV, T>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
 }
+
+// longest chain built for a d_k: record keys of every depth share a tile
+// buffer, so d_k = 256 fits three depths in LDS
+constexpr int max_steps(int dk) { return dk > 128 ? 3 : kFusedMaxSteps; }
 
 template <int DK, int DV>
 int launch_dims(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io, hipStream_t stream) {
@@ -452,25 +500,43 @@ int launch_dims(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const S
     case 1: return launch<DK, DV, 1>(sh, st, Wt, io, stream);
     case 2: return launch<DK, DV, 2>(sh, st, Wt, io, stream);
     case 3: return launch<DK, DV, 3>(sh, st, Wt, io, stream);
-    case 4: return launch<DK, DV, 4>(sh, st, Wt, io, stream);
-    case 5: return launch<DK, DV, 5>(sh, st, Wt, io, stream);
-    case 6: return launch<DK, DV, 6>(sh, st, Wt, io, stream);
-    default: return GDN_EUNSUPPORTED;
+    default: break;
   }
+  if constexpr (max_steps(DK) >= 6) {
+    switch (t) {
+      case 4: return launch<DK, DV, 4>(sh, st, Wt, io, stream);
+      case 5: return launch<DK, DV, 5>(sh, st, Wt, io, stream);
+      case 6: return launch<DK, DV, 6>(sh, st, Wt, io, stream);
+      default: break;
+    }
+  }
+  return GDN_EUNSUPPORTED;
+}
+
+bool fused_dims(int dk, int dv) {
+  return (dk == 32 && dv == 32) || (dk == 64 && dv == 64) ||
+         ((dk == 128 || dk == 256) && (dv == 128 || dv == 256 || dv == 512));
 }
 
 }  // namespace
 
 bool beam_fused_supported(const gdn_shape& sh, int t) {
-  return sh.decay_kind == GDN_DECAY_SCALAR && t >= 0 && t <= kFusedMaxSteps &&
-         ((sh.dk == 32 && sh.dv == 32) || (sh.dk == 64 && sh.dv == 64) || (sh.dk == 128 && sh.dv == 128));
+  return sh.decay_kind == GDN_DECAY_SCALAR && fused_dims(sh.dk, sh.dv) && t >= 0 && t <= max_steps(sh.dk);
 }
 
 int launch_beam_fused(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
                       hipStream_t stream) {
-  if (sh.dk == 32 && sh.dv == 32) return launch_dims<32, 32>(sh, st, t, Wt, io, stream);
-  if (sh.dk == 64 && sh.dv == 64) return launch_dims<64, 64>(sh, st, t, Wt, io, stream);
-  if (sh.dk == 128 && sh.dv == 128) return launch_dims<128, 128>(sh, st, t, Wt, io, stream);
+#define GDN_CASE(DK_, DV_) \
+  if (sh.dk == DK_ && sh.dv == DV_) return launch_dims<DK_, DV_>(sh, st, t, Wt, io, stream);
+  GDN_CASE(32, 32)
+  GDN_CASE(64, 64)
+  GDN_CASE(128, 128)
+  GDN_CASE(128, 256)
+  GDN_CASE(128, 512)
+  GDN_CASE(256, 128)
+  GDN_CASE(256, 256)
+  GDN_CASE(256, 512)
+#undef GDN_CASE
   return GDN_EUNSUPPORTED;
 }
 

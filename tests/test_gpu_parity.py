@@ -170,6 +170,15 @@ def test_wider_geometries(dk, dv, channel, Hk):
     assert rel_states(merged, ref) <= TOL
 
 
+def test_wide_state_beams_over_many_workgroups():
+    """d_k = 256, d_v = 512 with one request: four value slices, each cut into
+    16-beam chunks (chunk order, ragged last chunk), two value heads sharing
+    one key head."""
+    inp = synth.make_inputs(R=1, H=2, dk=256, dv=512, W=300, L=4, s0_std=0.05, seed=610,
+                            parents="topk", widths=[300, 283, 300, 271], Hk=1)
+    check_beam(inp, False, label="dk=256 dv=512 W=300 chunked")
+
+
 def test_wide_state_sequences():
     """One beam per request with d_k = 256, d_v = 512: the step runs through
     the beam kernel at W = 1, the log merge through the fold."""
