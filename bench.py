@@ -31,6 +31,7 @@ from linear_attention_beam_gdn_amd import accounting, configs  # noqa: E402
 
 METRIC = "GDN beam-steps/sec (H=32,dk=dv=128,512 beams) + % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
 WORKLOAD = configs.LARGE
 
 _CPU_INPUTS = None
@@ -371,6 +372,7 @@ def main():
         step_bytes.append(accounting.beam_step_bytes(unique_records=uniq, **kw))
         gather_bytes.append(accounting.beam_step_bytes(**kw))
     mean_bytes = float(np.mean(step_bytes))
+    mfma_flops = 3 * 2 * 2 * w.dk * w.dv * w.R * w.W * w.H
     mean_launch_s = float(launch_ms.mean()) * 1e-3
     achieved = mean_bytes / mean_launch_s / 1e9
 
@@ -401,6 +403,10 @@ def main():
             "bytes_per_launch": mean_bytes,
             "bytes_per_launch_per_beam_gather": float(np.mean(gather_bytes)),
             "launch_us": [float(x) * 1e3 for x in launch_ms.mean(0)],
+            # the S0^T [q | k] contraction on the matrix cores: three bf16 planes
+            # x two probes x 2 d_k d_v FLOP per beam-head, over the same launches
+            "mfma_tflops": mfma_flops / mean_launch_s / 1e12,
+            "mfma_frac_of_bf16_peak": mfma_flops / mean_launch_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         },
         "cpu_baseline": cpu,
     }
