@@ -417,6 +417,7 @@ def main():
             "channel_decay_beam_decode": lambda: beam_row(B, torch, dev, stream, configs.KDA, reps),
             "shared_key_heads_beam_decode": lambda: beam_row(B, torch, dev, stream, configs.SHARED_KEYS, reps),
             "wide_state_beam_decode": lambda: beam_row(B, torch, dev, stream, configs.WIDE, reps),
+            "channel_decay_wide_value_beam_decode": lambda: beam_row(B, torch, dev, stream, configs.KDA_WIDE, reps),
             "bounded_log_decode_and_merge": lambda: sequence_row(B, torch, dev, stream, configs.DELTALOG),
             "bounded_log_merge_interval": lambda: merge_interval_row(B, torch, dev, stream, configs.DELTALOG,
                                                                      (4, 8, 16)),

@@ -90,8 +90,12 @@ SHARED_KEYS = BeamWorkload("gdn_large_beam_shared_key_heads", R=8, H=32, dk=128,
 WIDE = BeamWorkload("gdn_wide_state_beam", R=8, H=16, dk=256, dv=512, W=512, L=4,
                     s0_std=0.05, seed=7, parents="topk_hot", hot_frac=0.3)
 
+# channel decay on a wide value state: d_k = 128, d_v = 512
+KDA_WIDE = BeamWorkload("kda_wide_value_beam", R=8, H=16, dk=128, dv=512, W=256, L=4,
+                        s0_std=0.05, seed=8, parents="topk", channel_decay=True)
+
 RWKV6 = SequenceWorkload("rwkv6_bounded_log", R=128, H=32, dk=128, dv=128, T=64, M=4,
                          s0_std=0.05, seed=5, channel_decay=True, plain_update=True)
 
-ALL = (TINY, SINGLE, LARGE, DELTALOG, KDA, RWKV6, SHARED_KEYS, WIDE)
+ALL = (TINY, SINGLE, LARGE, DELTALOG, KDA, RWKV6, SHARED_KEYS, WIDE, KDA_WIDE)
 BY_NAME = {w.name: w for w in ALL}

@@ -11,22 +11,23 @@
 // decay acts on the d_k side, so it lives in the probes: the S0 contraction
 // takes the FP32 probes Q_0 * q and Q_0 * k, split into two bf16 planes.
 //
-// Work split.  A workgroup takes one (request r, head h) and a chunk of its
-// beams, 8 beams per tile.  The 16 columns of the gfx950 16x16x32 bf16 MFMA
+// Work split.  A workgroup takes one (request r, head h), a slice of at most
+// 128 value rows (d_v = 256 and 512 take two and four slices, each preparing
+// the probes and weights itself) and a chunk of its beams, 8 beams per tile.  The 16 columns of the gfx950 16x16x32 bf16 MFMA
 // carry the q-probes (columns 0-7) and the k-probes (columns 8-15) of the
 // same 8 beams, so one MFMA forms both projections.
 // * Two DMA waves (alternate tiles) build the ancestry-ordered schedule and
 //   stream each tile's q|k rows, v, alpha_t, beta_t and, per beam, the keys
 //   and decay vectors of its T ancestral records into a ring of LDS buffers
 //   with LDS-DMA loads and counted waits.
-// * The d_v / 16 consumer waves each hold 16 value rows of S0[r, h] as two
-//   bf16 planes in registers.  Between two barriers a consumer wave
+// * The consumer waves (one per 16 value rows of the slice) each hold 16
+//   value rows of S0[r, h] as two bf16 planes in registers.  Between two barriers a consumer wave
 //   - prepares its share of the next tile (8 / (d_v / 16) beams): each half
 //     wave takes the q or the k row of a beam, walks the chain from the
 //     current step down (y = a_t * x; weight_j = k_j . y; y = a_j * y), and
 //     writes the probe Q_0 * x as hi and lo bf16 planes over the raw row, the
-//     record weights and k_t . q_t; it also appends the beam's key row and
-//     decay vector to the record store;
+//     record weights and k_t . q_t; in the first value slice it also appends
+//     the beam's key row and decay vector to the record store;
 //   - then finishes the current tile: hi*hi + hi*lo + lo*hi plane products
 //     on the matrix cores, the q- and k-halves of the result exchanged with
 //     a DPP row rotation, the replay with the ancestral update vectors
@@ -51,7 +52,10 @@ template <int DK, int DV, int T>
 struct KdaGeom {
   static_assert(DK % 64 == 0 && DV % 64 == 0, "the channel-decay kernel needs d_k, d_v multiples of 64");
   static constexpr int TB = 8;             // beams per tile
-  static constexpr int NC = DV / 16;       // consumer waves, 16 value rows each
+  static constexpr int VS = DV < 128 ? DV : 128;  // value rows per workgroup
+  static_assert(DV % VS == 0, "d_v must split evenly over value slices");
+  static constexpr int NVS = DV / VS;      // value slices
+  static constexpr int NC = VS / 16;       // consumer waves, 16 value rows each
   static_assert(TB % NC == 0, "each consumer wave prepares whole beams");
   static constexpr int BPW = TB / NC;      // beams a consumer wave prepares per tile
   static constexpr int EPL = DK / 32;      // channels per lane in the preparation
@@ -63,7 +67,7 @@ struct KdaGeom {
   // alpha_t of the 8 beams; then the probes' lo plane.  The 8-row slots of
   // beam b are exactly the 16-row slots of rows b and b + 8, so the wave that
   // prepares beam b overwrites only what it has already read.
-  static constexpr int VB = TB * DV * 2;
+  static constexpr int VB = TB * VS * 2;
   static constexpr int AB = TB * DK * 4;
   static constexpr int SMB = 256;          // beta_t
   static constexpr int NWT = (2 + 2 * T + 3) / 4 * 4;  // beta, k.q, T q-weights, T k-weights
@@ -78,9 +82,10 @@ struct KdaGeom {
   static constexpr int NBUF0 = (kLdsBytes - SLOTB) / BUF;
   static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
   static_assert(NBUF >= 3, "tile buffers do not fit in LDS");
-  // S0[r, h] is staged in LDS past the first two tile buffers until the
-  // consumers have split it into planes; the schedule's scratch is the first two.
-  static constexpr int S0B = DK * DV * 4, OS0 = 2 * BUF;
+  // The slice of S0[r, h] ([d_k][VS]) is staged in LDS past the first two
+  // tile buffers until the consumers have split it into planes; the
+  // schedule's scratch is the first two.
+  static constexpr int S0B = DK * VS * 4, OS0 = 2 * BUF;
   static constexpr int RINGB = NBUF * BUF > OS0 + S0B ? NBUF * BUF : OS0 + S0B;
   static constexpr int LDS = RINGB + SLOTB;
   static_assert(LDS <= kLdsBytes, "LDS layout does not fit");
@@ -164,9 +169,12 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   const int nblk = gridDim.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
   const int chunk_id = bid % a.nchunk;
-  const int rh = bid / a.nchunk;
+  const int vsl = (bid / a.nchunk) % G::NVS;  // value slice
+  const int rh = bid / (a.nchunk * G::NVS);
   const int h = rh % a.H;
   const int r = rh / a.H;
+  const int vs0 = vsl * G::VS;  // first value row of the slice
+  const bool slice0 = vsl == 0;  // writes ancestry, record keys and decays
   const int b_begin = chunk_id * a.chunk;
   const int b_end = min(b_begin + a.chunk, a.Wt);
   const int nb = b_end - b_begin;
@@ -180,15 +188,19 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   if (w >= G::WDMA) {
     // ============================================================ DMA waves
     const int dw = w - G::WDMA;
-    // S0[r, h] into LDS (wave 1), after the schedule's loads have gone out
+    // the slice of S0[r, h] into LDS as [d_k][VS] (wave 1), after the
+    // schedule's loads have gone out; 256 floats per DMA instruction
     auto stage_s0 = [&] {
-      const float* S = a.S + ((size_t)r * a.H + h) * DK * DV;
+      const float* S = a.S + ((size_t)r * a.H + h) * DK * DV + vs0;
 #pragma unroll
-      for (int m = 0; m < G::S0B / 1024; ++m) dma16(S + m * 256 + lane * 4, smem + G::OS0 + m * 1024);
+      for (int m = 0; m < G::S0B / 1024; ++m) {
+        const int e0 = m * 256 + lane * 4;
+        dma16(S + (size_t)(e0 / G::VS) * DV + e0 % G::VS, smem + G::OS0 + m * 1024);
+      }
     };
     if (T > 0) {
       if (dw == 0) {
-        build_schedule<T>(a, r, h == 0, b_begin, nb, lane, G::OS0, smem, s_tab, s_slot_hi,
+        build_schedule<T>(a, r, h == 0 && slice0, b_begin, nb, lane, G::OS0, smem, s_tab, s_slot_hi,
                           [] { lds_barrier(); });  // Q inside, once its loads have arrived
       } else {
         lds_barrier();  // Q
@@ -216,7 +228,7 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
 #pragma unroll
       for (int m = 0; m < G::QKB / 1024; ++m) dma16(qkrow + (m * 4 + (lane >> 4)) * 8, buf + G::OQK + m * 1024);
 #pragma unroll
-      for (int m = 0; m < G::VB / 1024; ++m) dma16(a.v + tok * DV + (m * 8 + (lane >> 3)) * 8, buf + G::OV + m * 1024);
+      for (int m = 0; m < G::VB / 1024; ++m) dma16(a.v + tok * DV + vs0 + (m * 8 + (lane >> 3)) * 8, buf + G::OV + m * 1024);
 #pragma unroll
       for (int m = 0; m < G::AB / 1024; ++m)
         dma16(a.alpha + tok * DK + (m * 8 + (lane >> 3)) * 4, buf + G::OA + m * 1024);
@@ -266,7 +278,7 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   const int sk = a.Hk * DK * 2, sa = a.H * DK * 4;  // bytes between beams
   // the record key lives per key head: one of its value heads writes it
   const size_t rec0k = (((size_t)T * a.R + r) * a.Wm + b_begin) * a.Hk + h / a.gq;
-  const bool key_writer = h % a.gq == 0;
+  const bool key_writer = h % a.gq == 0 && slice0;
   const __amdgpu_buffer_rsrc_t w_k = store_window(a.rec_k + rec0k * DK, (nb - 1) * sk + DK * 2);
   const __amdgpu_buffer_rsrc_t w_a = store_window(a.rec_alpha + rec0 * DK, (nb - 1) * sa + DK * 4);
 
@@ -323,12 +335,12 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
                                               live && ps && key_writer ? ib * sk + e0 * 2 : kOutside,
                                               0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{at[0], at[1], at[2], at[3]}), w_a,
-                                               live && !ps ? ib * sa + e0 * 4 : kOutside, 0, 0);
+                                               live && !ps && slice0 ? ib * sa + e0 * 4 : kOutside, 0, 0);
       } else {
         __builtin_amdgcn_raw_buffer_store_b32(kw[0], w_k, live && ps && key_writer ? ib * sk + e0 * 2 : kOutside,
                                               0, 0);
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(at[0]), __float_as_uint(at[1])}, w_a,
-                                              live && !ps ? ib * sa + e0 * 4 : kOutside, 0, 0);
+                                              live && !ps && slice0 ? ib * sa + e0 * 4 : kOutside, 0, 0);
       }
       // probe Q_0 x as hi + lo bf16 planes, over the raw row and this beam's alpha_t
       uint32_t hw[EPL / 2], lw[EPL / 2];
@@ -360,9 +372,9 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     }
   };
 
-  // Slice of S0[r, h] as hi + lo bf16 planes in the MFMA A layout: lane
-  // (g, c) holds key channels 32s + 8g .. +7 of value row 16w + c, so C row
-  // 4g + i is value row 16w + 4g + i.
+  // Part of S0[r, h] as hi + lo bf16 planes in the MFMA A layout: lane
+  // (g, c) holds key channels 32s + 8g .. +7 of value row vs0 + 16w + c, so
+  // C row 4g + i is value row vs0 + 16w + 4g + i.
   const int g = lane >> 4;
   const int c = lane & 15;
   const int bb = c & 7;     // beam of this lane within the tile
@@ -370,7 +382,7 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   // A DMA wave stages S0 in LDS; the planes are formed between barriers S
   // and A.
   if (T > 0) lds_barrier();  // Q
-  const int row0 = w * 16 + 4 * g;
+  const int row0 = vs0 + w * 16 + 4 * g;
   const int so = a.H * DV * 4;
   const size_t tok0 = ((size_t)r * a.Wt + b_begin) * a.H + h;
   const __amdgpu_buffer_rsrc_t w_o = store_window(a.o + tok0 * DV, (nb - 1) * so + DV * 4);
@@ -400,7 +412,7 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     for (int s = 0; s < KS; ++s) {
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = S[(s * 32 + g * 8 + e) * DV + w * 16 + c];
+      for (int e = 0; e < 8; ++e) x[e] = S[(s * 32 + g * 8 + e) * G::VS + w * 16 + c];
       split_planes<2>(x, As[s]);
     }
   }
@@ -502,9 +514,9 @@ int launch(const gdn_shape& sh, const gdn_store& st, int Wt, const StepIO& io, h
   a.Hk = key_heads(sh);
   a.gq = sh.H / a.Hk;
   // one workgroup per compute unit: the tile ring takes most of its LDS
-  a.chunk = pick_chunk(sh.R * sh.H, Wt, kMaxChunkF, cu_count());
+  a.chunk = pick_chunk(sh.R * sh.H * G::NVS, Wt, kMaxChunkF, cu_count());
   a.nchunk = (Wt + a.chunk - 1) / a.chunk;
-  const long grid = (long)sh.R * sh.H * a.nchunk;
+  const long grid = (long)sh.R * sh.H * G::NVS * a.nchunk;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
   hipLaunchKernelGGL((k_beam_fused_kda<DK, DV, T>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
@@ -525,13 +537,15 @@ int launch_dims(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const S
 
 bool beam_fused_kda_supported(const gdn_shape& sh, int t) {
   return sh.decay_kind == GDN_DECAY_CHANNEL && t >= 0 && t <= 3 &&
-         ((sh.dk == 64 && sh.dv == 64) || (sh.dk == 128 && sh.dv == 128));
+         ((sh.dk == 64 && sh.dv == 64) || (sh.dk == 128 && (sh.dv == 128 || sh.dv == 256 || sh.dv == 512)));
 }
 
 int launch_beam_fused_kda(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
                           hipStream_t stream) {
   if (sh.dk == 64 && sh.dv == 64) return launch_dims<64, 64>(sh, st, t, Wt, io, stream);
   if (sh.dk == 128 && sh.dv == 128) return launch_dims<128, 128>(sh, st, t, Wt, io, stream);
+  if (sh.dk == 128 && sh.dv == 256) return launch_dims<128, 256>(sh, st, t, Wt, io, stream);
+  if (sh.dk == 128 && sh.dv == 512) return launch_dims<128, 512>(sh, st, t, Wt, io, stream);
   return GDN_EUNSUPPORTED;
 }
 

@@ -63,6 +63,11 @@ def test_wide_state_workload_sampled():
     check_beam(configs.WIDE.inputs(), False, requests=[3], heads=[0, 15], label="wide state")
 
 
+def test_kda_wide_value_workload_sampled():
+    # full size, channel decay with d_v = 512 (four value slices)
+    check_beam(configs.KDA_WIDE.inputs(), True, requests=[2], heads=[0, 15], label="kda wide value")
+
+
 def test_kda_workload_sampled():
     check_beam(configs.KDA.inputs(), True, requests=[0, 15], heads=[0, 31], label="kda")
 
