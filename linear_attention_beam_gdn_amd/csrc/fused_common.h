@@ -203,6 +203,19 @@ __device__ __forceinline__ void build_schedule(const BeamArgs& a, int r, bool an
   }
 }
 
+// The store windows and per-beam store offsets are 32-bit byte ranges over a
+// chunk of up to kMaxChunkF beams: the widest per-beam stride (o and delta:
+// H d_v FP32; keys: H_k d_k bf16; per-channel decays: H d_k FP32) times the
+// chunk must stay below 2^31.  Shapes past that take the general kernel,
+// which indexes with 64-bit offsets.
+inline bool windows_fit(const gdn_shape& sh) {
+  const long long hk = sh.H_k > 0 ? sh.H_k : sh.H;
+  long long stride = (long long)sh.H * sh.dv * 4;
+  if (hk * sh.dk * 2 > stride) stride = hk * sh.dk * 2;
+  if ((long long)sh.H * sh.dk * 4 > stride) stride = (long long)sh.H * sh.dk * 4;
+  return (long long)kMaxChunkF * stride + stride < (1LL << 31);
+}
+
 inline int cu_count() {
   static int cached[64] = {0};
   int dev = 0;

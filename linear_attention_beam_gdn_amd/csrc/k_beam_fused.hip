@@ -521,7 +521,8 @@ bool fused_dims(int dk, int dv) {
 }  // namespace
 
 bool beam_fused_supported(const gdn_shape& sh, int t) {
-  return sh.decay_kind == GDN_DECAY_SCALAR && fused_dims(sh.dk, sh.dv) && t >= 0 && t <= max_steps(sh.dk);
+  return sh.decay_kind == GDN_DECAY_SCALAR && fused_dims(sh.dk, sh.dv) && t >= 0 && t <= max_steps(sh.dk) &&
+         windows_fit(sh);
 }
 
 int launch_beam_fused(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,

@@ -537,7 +537,8 @@ int launch_dims(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const S
 
 bool beam_fused_kda_supported(const gdn_shape& sh, int t) {
   return sh.decay_kind == GDN_DECAY_CHANNEL && t >= 0 && t <= 3 &&
-         ((sh.dk == 64 && sh.dv == 64) || (sh.dk == 128 && (sh.dv == 128 || sh.dv == 256 || sh.dv == 512)));
+         ((sh.dk == 64 && sh.dv == 64) || (sh.dk == 128 && (sh.dv == 128 || sh.dv == 256 || sh.dv == 512))) &&
+         windows_fit(sh);
 }
 
 int launch_beam_fused_kda(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
