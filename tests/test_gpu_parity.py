@@ -327,6 +327,30 @@ def test_gates_at_extremes(channel):
     check_beam(inp, channel, label="alpha=1")
 
 
+@pytest.mark.parametrize("dk,dv,channel", [(256, 512, False), (256, 128, False), (128, 512, False), (128, 512, True)])
+def test_wide_gates_at_extremes(dk, dv, channel):
+    """The S0 contraction of the wide geometries at full weight (two bf16
+    planes at d_k = 256): beta = 0 gives o = (prod decay) S0^T q, alpha = 1
+    keeps S0 undecayed through the chain."""
+    inp = synth.make_inputs(R=2, H=2, dk=dk, dv=dv, W=20, L=4, s0_std=0.05, seed=700 + dk + dv // 8,
+                            parents="topk", channel_decay=channel, beta_const=0.0)
+    store, _, _ = check_beam(inp, channel, label=f"dk={dk} dv={dv} beta=0")
+    assert torch.count_nonzero(store.rec_delta) == 0
+    inp = synth.make_inputs(R=2, H=2, dk=dk, dv=dv, W=20, L=4, s0_std=0.05, seed=701 + dk + dv // 8,
+                            parents="topk", channel_decay=channel, alpha_const=1.0)
+    check_beam(inp, channel, label=f"dk={dk} dv={dv} alpha=1")
+
+
+@pytest.mark.parametrize("wname,channel,requests,heads", [("LARGE", False, [3], [0, 31]), ("KDA", True, [9], [0, 31]),
+                                                          ("WIDE", False, [5], [15]), ("KDA_WIDE", True, [1], [7]),
+                                                          ("SHARED_KEYS", False, [6], [2, 3])])
+def test_workloads_with_undecayed_context(wname, channel, requests, heads):
+    """Each full-size beam workload with alpha = 1 (scalar or every channel),
+    so that the shared-context term is not damped by the chain's decays."""
+    w = getattr(configs, wname)
+    check_beam(w.inputs(alpha_const=1.0), channel, requests=requests, heads=heads, label=f"{w.name} alpha=1")
+
+
 def test_orthonormal_keys_retrieve_exactly():
     inp = synth.make_inputs(R=2, H=2, dk=32, dv=32, W=9, L=4, s0_std=0.05, seed=13,
                             parents="uniform", alpha_const=1.0, beta_const=1.0)
