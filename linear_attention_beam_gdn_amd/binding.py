@@ -81,14 +81,19 @@ def _ptr(x) -> int | None:
     return None if x is None else x.data_ptr()
 
 
-def _stream(stream) -> int | None:
-    s = torch.cuda.current_stream() if stream is None else stream
+def _stream(stream, device) -> int | None:
+    """The given stream, else the current stream of the store's device."""
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    if s.device != device:
+        raise ValueError(f"stream is on {s.device}, the store on {device}")
     return s.cuda_stream
 
 
-def _check(t: torch.Tensor, name: str, dtypes, shape):
+def _check(t: torch.Tensor, name: str, dtypes, shape, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor (there is no CPU path)")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the store on {device}")
     if t.dtype not in dtypes:
         raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
     if not t.is_contiguous():
@@ -118,12 +123,12 @@ class Store:
         self.channel_decay = bool(channel_decay)
         self.plain_update = bool(plain_update)
         self.A = dk if channel_decay else 1
-        f32 = dict(dtype=torch.float32, device=device)
-        if S is None:
-            self.S = torch.zeros(R, H, dk, dv, **f32)
-        else:
+        if S is not None:
             _check(S, "S", (torch.float32,), (R, H, dk, dv))
-            self.S = S
+            device = S.device  # the records live beside the given state
+        f32 = dict(dtype=torch.float32, device=device)
+        self.S = torch.zeros(R, H, dk, dv, **f32) if S is None else S
+        self.device = self.S.device
         self.rec_delta = torch.zeros(L_max, R, W_max, H, dv, **f32)
         self.rec_k = torch.zeros(L_max, R, W_max, self.Hk, dk, dtype=torch.bfloat16, device=device)
         self.rec_alpha = torch.zeros(L_max, R, W_max, H, self.A, **f32)
@@ -136,21 +141,21 @@ class Store:
 
 def decode_step(store: Store, t, W_t, parent, q, k, v, alpha, beta, o=None, stream=None):
     """One decode step (gdn_beam_decode_step); returns o [R,W_t,H,dv] FP32."""
-    R, H, dk, dv = store.R, store.H, store.dk, store.dv
-    _check(q, "q", _BF16, (R, W_t, store.Hk, dk))
-    _check(k, "k", _BF16, (R, W_t, store.Hk, dk))
-    _check(v, "v", _BF16, (R, W_t, H, dv))
+    R, H, dk, dv, dev = store.R, store.H, store.dk, store.dv, store.device
+    _check(q, "q", _BF16, (R, W_t, store.Hk, dk), dev)
+    _check(k, "k", _BF16, (R, W_t, store.Hk, dk), dev)
+    _check(v, "v", _BF16, (R, W_t, H, dv), dev)
     a_shape = (R, W_t, H, dk) if store.channel_decay else (R, W_t, H)
-    _check(alpha, "alpha", (torch.float32,), a_shape)
-    _check(beta, "beta", (torch.float32,), (R, W_t, H))
+    _check(alpha, "alpha", (torch.float32,), a_shape, dev)
+    _check(beta, "beta", (torch.float32,), (R, W_t, H), dev)
     if t > 0:
-        _check(parent, "parent", (torch.int32,), (R, W_t))
+        _check(parent, "parent", (torch.int32,), (R, W_t), dev)
     if o is None:
-        o = torch.empty(R, W_t, H, dv, dtype=torch.float32, device=q.device)
-    _check(o, "o", (torch.float32,), (R, W_t, H, dv))
+        o = torch.empty(R, W_t, H, dv, dtype=torch.float32, device=dev)
+    _check(o, "o", (torch.float32,), (R, W_t, H, dv), dev)
     rc = lib().gdn_beam_decode_step(ctypes.byref(store.shape), ctypes.byref(store.cstore), t, W_t,
                                     _ptr(parent) if t > 0 else None, _ptr(q), _ptr(k), _ptr(v),
-                                    _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
+                                    _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream, store.device))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_beam_decode_step")
     return o
@@ -159,12 +164,12 @@ def decode_step(store: Store, t, W_t, parent, q, k, v, alpha, beta, o=None, stre
 def materialize(store: Store, t, rb, out=None, stream=None):
     """Dense states after step t of the (request, beam) pairs rb [n,2] int32."""
     n = int(rb.shape[0])
-    _check(rb, "rb", (torch.int32,), (n, 2))
+    _check(rb, "rb", (torch.int32,), (n, 2), store.device)
     if out is None:
-        out = torch.empty(n, store.H, store.dk, store.dv, dtype=torch.float32, device=rb.device)
-    _check(out, "S_out", (torch.float32,), (n, store.H, store.dk, store.dv))
+        out = torch.empty(n, store.H, store.dk, store.dv, dtype=torch.float32, device=store.device)
+    _check(out, "S_out", (torch.float32,), (n, store.H, store.dk, store.dv), store.device)
     rc = lib().gdn_materialize(ctypes.byref(store.shape), ctypes.byref(store.cstore), t, _ptr(rb), n,
-                               _ptr(out), _stream(stream))
+                               _ptr(out), _stream(stream, store.device))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_materialize")
     return out
@@ -173,17 +178,17 @@ def materialize(store: Store, t, rb, out=None, stream=None):
 def decode_merge_step(store: Store, t, q, k, v, alpha, beta, o=None, stream=None):
     """Decode token t of independent sequences and fold the full log into the
     base in the same pass (gdn_decode_merge_step); returns o [R,1,H,dv] FP32."""
-    R, H, dk, dv = store.R, store.H, store.dk, store.dv
-    _check(q, "q", _BF16, (R, 1, store.Hk, dk))
-    _check(k, "k", _BF16, (R, 1, store.Hk, dk))
-    _check(v, "v", _BF16, (R, 1, H, dv))
-    _check(alpha, "alpha", (torch.float32,), (R, 1, H, dk) if store.channel_decay else (R, 1, H))
-    _check(beta, "beta", (torch.float32,), (R, 1, H))
+    R, H, dk, dv, dev = store.R, store.H, store.dk, store.dv, store.device
+    _check(q, "q", _BF16, (R, 1, store.Hk, dk), dev)
+    _check(k, "k", _BF16, (R, 1, store.Hk, dk), dev)
+    _check(v, "v", _BF16, (R, 1, H, dv), dev)
+    _check(alpha, "alpha", (torch.float32,), (R, 1, H, dk) if store.channel_decay else (R, 1, H), dev)
+    _check(beta, "beta", (torch.float32,), (R, 1, H), dev)
     if o is None:
-        o = torch.empty(R, 1, H, dv, dtype=torch.float32, device=q.device)
-    _check(o, "o", (torch.float32,), (R, 1, H, dv))
+        o = torch.empty(R, 1, H, dv, dtype=torch.float32, device=dev)
+    _check(o, "o", (torch.float32,), (R, 1, H, dv), dev)
     rc = lib().gdn_decode_merge_step(ctypes.byref(store.shape), ctypes.byref(store.cstore), t, _ptr(q), _ptr(k),
-                                     _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
+                                     _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream, store.device))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_decode_merge_step")
     return o
@@ -192,7 +197,7 @@ def decode_merge_step(store: Store, t, q, k, v, alpha, beta, o=None, stream=None
 def log_merge(store: Store, n_rec, beam=0, stream=None):
     """Fold the first n_rec records of `beam`'s chain into store.S in place."""
     rc = lib().gdn_log_merge(ctypes.byref(store.shape), ctypes.byref(store.cstore), n_rec, beam,
-                             _stream(stream))
+                             _stream(stream, store.device))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_log_merge")
 

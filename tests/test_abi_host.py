@@ -113,6 +113,7 @@ def test_binding_refuses_host_tensors():
     import torch
     st = B.Store.__new__(B.Store)
     st.R, st.H, st.Hk, st.dk, st.dv, st.channel_decay = 1, 1, 1, 16, 16, False
+    st.device = torch.device("cuda", 0)
     x = torch.zeros(1, 1, 1, 16, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="device tensor"):
         B.decode_step(st, 0, 1, None, x, x, x, torch.zeros(1, 1, 1), torch.zeros(1, 1, 1))
