@@ -75,3 +75,60 @@ def test_random_geometry(case):
     es = rel_states(S, O.beam_states(inp["S0"], inp["steps"], t, [tuple(p) for p in pairs]))
     assert es <= TOL, (label, "materialise", es)
     log(f"[sweep] case {c['id']}: max rel err {max(worst, es):.2e}")
+
+
+def _seq_cases(n=30, seed=4048):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = str(rng.choice(["scalar", "channel", "plain"]))
+        square = [(16, 16), (32, 32), (64, 64), (128, 128)]
+        wide = [(128, 256), (128, 512), (256, 256)] if kind == "scalar" else ([(128, 256)] if kind == "channel" else [])
+        dims = square + wide
+        dk, dv = dims[rng.integers(len(dims))]
+        fused = (dk, dv) in square and bool(rng.random() < 0.6)  # the merge in the decode: square shapes
+        H = int(rng.choice([1, 2, 3, 4, 6]))
+        Hk = int(rng.choice([d for d in range(1, H + 1) if H % d == 0]))
+        out.append(dict(id=i, kind=kind, dk=dk, dv=dv, H=H, Hk=Hk, R=int(rng.integers(1, 6)), T=int(rng.integers(1, 21)),
+                        M=int(rng.integers(1, 9)), fused=fused, seed=1900 + i))
+    return out
+
+
+SEQ_CASES = _seq_cases()
+
+
+@pytest.mark.parametrize("case", SEQ_CASES, ids=[f"s{c['id']}" for c in SEQ_CASES])
+def test_random_sequences(case):
+    """Bounded-log decoding of independent sequences over a seeded sweep: log
+    capacity M, token count, decay kind and update rule, key heads, and the
+    merge either fused into the decode that fills the log or run separately."""
+    c = case
+    channel, plain = c["kind"] != "scalar", c["kind"] == "plain"
+    R, H, dk, dv, T, M = c["R"], c["H"], c["dk"], c["dv"], c["T"], c["M"]
+    label = f"seq case {c['id']}: {c['kind']} dk={dk} dv={dv} R={R} H={H} Hk={c['Hk']} T={T} M={M} fused={c['fused']}"
+    log(f"[sweep] {label}")
+    seq = synth.make_sequence_inputs(R=R, H=H, dk=dk, dv=dv, T=T, s0_std=0.1, seed=c["seed"], channel_decay=channel,
+                                     Hk=c["Hk"])
+    ref = O.sequence_decode(seq["S0"], seq["tokens"], M, rule="plain" if plain else "delta")
+    store = B.Store(R, 1, H, dk, dv, M, channel_decay=channel, plain_update=plain,
+                    S=torch.from_numpy(seq["S0"]).cuda(), Hk=c["Hk"])
+    zero = torch.zeros(R, 1, dtype=torch.int32, device="cuda")
+    worst = 0.0
+    for i in range(T):
+        t = i % M
+        d = B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")})
+        args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        if t == M - 1 and c["fused"]:
+            o = B.decode_merge_step(store, t, *args)
+        else:
+            o = B.decode_step(store, t, 1, zero, *args)
+            if t == M - 1:
+                B.log_merge(store, M, 0)
+        e = rel_slices(o[:, 0].cpu().numpy().reshape(R * H, dv), ref["o"][i])
+        worst = max(worst, e)
+        assert e <= TOL, (label, i, e)
+        if t == M - 1:
+            e = rel_states(store.S.cpu().numpy().reshape(R * H, 1, dk, dv), ref["bases"][i // M][:, None])
+            worst = max(worst, e)
+            assert e <= TOL, (label, "base after merge", i, e)
+    log(f"[sweep] seq case {c['id']}: max rel err {worst:.2e}")
