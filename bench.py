@@ -162,6 +162,47 @@ def beam_row(B, torch, dev, stream, wl, reps):
             "launch_us": us, **{k: v for k, v in _bw(tot_b / wl.L, tot_us / wl.L).items() if k != "us"}}
 
 
+# OneLA's printed operator latencies at its Qwen geometry (unnamed GPU; context only):
+# R = 16 from §4.3 (GDN attention, largest shape), R = 4 from §4.4 (recurrent-state path)
+ONELA_MS = {16: {3: 0.212, 7: 0.990}, 4: {3: 0.0755, 7: 0.308}}
+
+
+def onela_latency_row(B, torch, dev, stream, wl, reps):
+    """Decode latency of O - 1 back-to-back steps (O = 3 and 7 output tokens)
+    at OneLA's Qwen geometry, beside the page's own figure for the shape."""
+    inp = wl.inputs()
+    steps = [B.upload(st, dev) for st in inp["steps"]]
+    store = B.Store(wl.R, wl.W, wl.H, wl.dk, wl.dv, wl.L, S=torch.from_numpy(inp["S0"]).to(dev))
+    outs = [torch.empty(wl.R, wl.W, wl.H, wl.dv, dtype=torch.float32, device=dev) for _ in range(wl.L)]
+
+    def launch(t):
+        d = steps[t]
+        B.decode_step(store, t, wl.W, d.get("parent"), d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                      o=outs[t], stream=stream)
+
+    for _ in range(2):
+        for t in range(wl.L):
+            launch(t)
+    torch.cuda.synchronize()
+    out = {"workload": wl.name}
+    for O in (3, 7):
+        T = O - 1
+        tot = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            _pad(torch, stream)
+            a.record(stream)
+            for t in range(T):
+                launch(t)
+            b.record(stream)
+            torch.cuda.synchronize()
+            tot.append(a.elapsed_time(b))
+        ms = float(np.median(tot))
+        out[f"O={O}"] = {"decode_calls": T, "ms": ms, "beam_steps_per_s": wl.R * wl.W * T / (ms * 1e-3),
+                         "page_ms": ONELA_MS[wl.R][O]}
+    return out
+
+
 def sequence_row(B, torch, dev, stream, wl):
     """Bounded-log decoding of independent sequences: every token's decode
     (log length token mod M) and the merge after every M tokens."""
@@ -447,6 +488,8 @@ def main():
                                                                      (4, 8, 16)),
             "rwkv6_bounded_log": lambda: sequence_row(B, torch, dev, stream, configs.RWKV6),
             "materialize": lambda: materialize_row(B, torch, dev, stream, WORKLOAD, 64, reps),
+            "onela_qwen_geometry_latency_r4": lambda: onela_latency_row(B, torch, dev, stream, configs.QWEN_R4, reps),
+            "onela_qwen_geometry_latency_r16": lambda: onela_latency_row(B, torch, dev, stream, configs.QWEN_R16, reps),
         }
         pick = [r for r in args.rows.split(",") if r] or list(rows)
         unknown = [r for r in pick if r not in rows]

@@ -94,8 +94,15 @@ WIDE = BeamWorkload("gdn_wide_state_beam", R=8, H=16, dk=256, dv=512, W=512, L=4
 KDA_WIDE = BeamWorkload("kda_wide_value_beam", R=8, H=16, dk=128, dv=512, W=256, L=4,
                         s0_std=0.05, seed=8, parents="topk", channel_decay=True)
 
+# OneLA §4.1/§4.3 "Qwen geometry" (H_K = H_V = 16, K = V = 128) at W = 512 with six decode
+# steps (O = 7 output tokens): R = 4 (the recurrent-path breakdown) and R = 16 (the largest shape)
+QWEN_R4 = BeamWorkload("onela_qwen_geometry_r4", R=4, H=16, dk=128, dv=128, W=512, L=6,
+                       s0_std=0.05, seed=9, parents="topk_hot", hot_frac=0.3)
+QWEN_R16 = BeamWorkload("onela_qwen_geometry_r16", R=16, H=16, dk=128, dv=128, W=512, L=6,
+                        s0_std=0.05, seed=10, parents="topk_hot", hot_frac=0.3)
+
 RWKV6 = SequenceWorkload("rwkv6_bounded_log", R=128, H=32, dk=128, dv=128, T=64, M=4,
                          s0_std=0.05, seed=5, channel_decay=True, plain_update=True)
 
-ALL = (TINY, SINGLE, LARGE, DELTALOG, KDA, RWKV6, SHARED_KEYS, WIDE, KDA_WIDE)
+ALL = (TINY, SINGLE, LARGE, DELTALOG, KDA, RWKV6, SHARED_KEYS, WIDE, KDA_WIDE, QWEN_R4, QWEN_R16)
 BY_NAME = {w.name: w for w in ALL}

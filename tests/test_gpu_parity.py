@@ -68,6 +68,13 @@ def test_kda_wide_value_workload_sampled():
     check_beam(configs.KDA_WIDE.inputs(), True, requests=[2], heads=[0, 15], label="kda wide value")
 
 
+@pytest.mark.parametrize("wname,requests,heads", [("QWEN_R4", [1], [0, 15]), ("QWEN_R16", [11], [7])])
+def test_qwen_geometry_workloads_sampled(wname, requests, heads):
+    # full size, six decode steps (chains of up to five records in the fused kernel)
+    w = getattr(configs, wname)
+    check_beam(w.inputs(), False, requests=requests, heads=heads, label=w.name)
+
+
 def test_kda_workload_sampled():
     check_beam(configs.KDA.inputs(), True, requests=[0, 15], heads=[0, 31], label="kda")
 
