@@ -509,6 +509,49 @@ def test_append_only_and_guards():
         assert not torch.isnan(o).any()
 
 
+@pytest.mark.parametrize("dk,dv,channel", [(128, 128, False), (128, 128, True), (16, 16, False), (256, 512, False)])
+def test_beam_decode_graph_replay(dk, dv, channel):
+    """All L steps of a beam decode captured once in a HIP graph (the fused
+    scalar and channel-decay kernels, the general kernel, the value-sliced
+    d_k = 256 kernel): every replay, with eager work and synchronisation in
+    between, equals an eager run bit for bit (outputs, records and ancestry;
+    the schedule-order entry of each ancestry row may differ with tie order)."""
+    R, H, W, L = 2, 2, 40, 4
+    inp = synth.make_inputs(R=R, H=H, dk=dk, dv=dv, W=W, L=L, s0_std=0.05, seed=31 + dk, parents="topk",
+                            channel_decay=channel)
+    S0 = torch.from_numpy(inp["S0"]).cuda()
+    steps = [B.upload(st) for st in inp["steps"]]
+
+    def run(store, outs):
+        for t in range(L):
+            d = steps[t]
+            B.decode_step(store, t, W, d.get("parent"), d["q"], d["k"], d["v"], d["alpha"], d["beta"], o=outs[t])
+
+    mk = lambda: B.Store(R, W, H, dk, dv, L, channel_decay=channel, S=S0.clone())
+    new_outs = lambda: [torch.empty(R, W, H, dv, device="cuda") for _ in range(L)]
+    run(mk(), new_outs())  # warm-up outside the capture
+    torch.cuda.synchronize()
+    eager, graphed = mk(), mk()
+    e_out, g_out = new_outs(), new_outs()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(graphed, g_out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        run(eager, e_out)
+        torch.cuda.synchronize()
+        for t in range(L):
+            assert torch.equal(g_out[t], e_out[t]), (rep, t)
+            assert torch.equal(graphed.anc[t, :, :, :t], eager.anc[t, :, :, :t]), (rep, t)
+        for name in ("rec_delta", "rec_k", "rec_alpha"):
+            assert torch.equal(getattr(graphed, name), getattr(eager, name)), (rep, name)
+    ref = O.beam_decode(inp["S0"], inp["steps"])
+    assert max(rel_slices(g_out[t].cpu().numpy(), ref["o"][t]) for t in range(L)) <= TOL
+    log(f"[parity] beam decode dk={dk} dv={dv} ch={channel}: 3 graph replays equal the eager run")
+
+
 def test_merge_cycle_graph_replay():
     """A bounded-log merge cycle (M - 1 appends, then the decode that merges)
     captured once in a HIP graph: every replay, with eager work and
