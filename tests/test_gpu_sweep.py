@@ -49,6 +49,19 @@ CASES = _cases()
 
 @pytest.mark.parametrize("case", CASES, ids=[f"c{c['id']}" for c in CASES])
 def test_random_geometry(case):
+    _check_geometry(case)
+
+
+@pytest.mark.parametrize("case", CASES[:40], ids=[f"c{c['id']}" for c in CASES[:40]])
+def test_random_geometry_one_chunk(case, monkeypatch):
+    """The same cases with every (request, head) in one beam chunk
+    (GDN_BEAM_CHUNK=512), so that the fused kernels order the beams
+    depth-first with the counting sort instead of taking chunk order."""
+    monkeypatch.setenv("GDN_BEAM_CHUNK", "512")
+    _check_geometry(case)
+
+
+def _check_geometry(case):
     c = case
     label = (f"case {c['id']}: dk={c['dk']} dv={c['dv']} ch={c['channel']} R={c['R']} H={c['H']} Hk={c['Hk']} "
              f"L={c['L']} W_max={c['W_max']} widths={c['widths']} parents={c['parents']}")
