@@ -61,3 +61,21 @@ def test_topk_parents_from_expansion():
         p = st["parent"][0]
         assert np.all((p >= 0) & (p < 32))
         assert len(np.unique(p)) < 32  # reselection merges and prunes branches
+
+
+def test_key_heads():
+    """Hk = H draws exactly what the default draws; Hk < H gives q and k Hk
+    heads (unit-norm) and leaves v, the gates and the parents per value head."""
+    kw = dict(R=2, H=4, dk=16, dv=8, W=10, L=3, s0_std=0.1, seed=12, parents="topk")
+    a, b = synth.make_inputs(**kw), synth.make_inputs(Hk=4, **kw)
+    for sa, sb in zip(a["steps"], b["steps"]):
+        for n in sa:
+            assert np.array_equal(sa[n], sb[n])
+    c = synth.make_inputs(Hk=2, **kw)
+    for st in c["steps"]:
+        assert st["q"].shape == (2, 10, 2, 16) and st["k"].shape == (2, 10, 2, 16)
+        assert st["v"].shape == (2, 10, 4, 8) and st["alpha"].shape == (2, 10, 4)
+        norms = np.linalg.norm(synth.bf16_bits_to_f32(st["k"]).astype(np.float64), axis=-1)
+        assert np.all(np.abs(norms - 1) < 2 ** -7)
+    seq = synth.make_sequence_inputs(R=2, H=6, dk=8, dv=8, T=3, s0_std=0.1, seed=3, Hk=3)
+    assert seq["tokens"]["q"].shape == (3, 2, 3, 8) and seq["tokens"]["v"].shape == (3, 2, 6, 8)
