@@ -31,6 +31,11 @@ update pair is (k_t, v_t): no delta correction, so S_t = D(a_t) S_{t-1} +
 k_t v_t^T, the record's update vector is v_t itself and beta is not used
 (``rule="plain"`` below; the readout stays o_t = S_t^T q_t).
 
+Key heads.  OneLA's operator suite (§4.1) pairs H_K key heads with H_V value
+heads, H_V a multiple of H_K.  When q and k carry fewer heads than v, value
+head h reads the q and k of key head h // (H_V / H_K); everything else stays
+per value head, and each value head's recurrence is the one above.
+
 Every array is converted to float64 exactly (bf16 bit patterns and FP32 values
 widen without rounding) and all arithmetic is FP64.  Batching over beams uses
 numpy broadcasting only; there is no blocking, fusion or reordering.
