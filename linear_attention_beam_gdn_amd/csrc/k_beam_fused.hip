@@ -84,10 +84,13 @@ struct FusedGeom {
   static constexpr int NSM = (2 + T) * 16 > 64 ? 2 : 1;  // dword DMAs: alpha_t, beta_t, alpha_j
   static constexpr int SMB = NSM * 256;
   static constexpr int RKB = 16 * DK * 2;  // keys of one record depth
+  // record-key depths staged in the tile buffer; with d_k = 256 only three
+  // fit, and the dot wave gathers the keys of depths 3 .. T-1 from memory
+  static constexpr int TL = (DK > 128 && T > 3) ? 3 : T;
   static constexpr int NWT = (3 + 2 * T + 3) / 4 * 4;  // weights per beam, padded to 16 B
   static constexpr int WTB = 16 * NWT * 4;
   static constexpr int OQ = 0, OKK = QB, OV = 2 * QB, OS = 2 * QB + VB, OW = OS + SMB, ORK = OW + WTB;
-  static constexpr int BUF = ORK + T * RKB;
+  static constexpr int BUF = ORK + TL * RKB;
   // schedule table: per position {beam, slot_0, slot_1, slot_2}, plus slot_3
   static constexpr int SLOTB = T > 0 ? kMaxChunkF * 16 + (T > 3 ? (T - 3) * kMaxChunkF * 4 : 0) : 0;
   static constexpr int NBUF0 = (kLdsBytes - SLOTB) / BUF;
@@ -106,7 +109,7 @@ struct FusedGeom {
   static_assert(!S0_LDS || S0B % 1024 == 0, "S0 is staged in whole DMA blocks");
   static_assert(NC == 2 * KS || NC == KS, "the key row is appended by the consumer waves in halves or wholes");
   // LDS-DMA instructions the DMA wave issues per tile
-  static constexpr int OPT = 2 * (QB / 1024) + VB / 1024 + NSM + T * (RKB / 1024);
+  static constexpr int OPT = 2 * (QB / 1024) + VB / 1024 + NSM + TL * (RKB / 1024);
   static_assert(QB % 1024 == 0 && VB % 1024 == 0, "tile arrays must be whole DMA blocks");
   static_assert((2 + T) * 16 <= 128, "too many record depths for the small-value block");
   static_assert(T <= 6, "at most six record depths (the small-value block holds 2 + T groups of 16)");
@@ -210,7 +213,7 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
 #pragma unroll
       for (int j = 0; j < T; ++j) rj[j] = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + h;
 #pragma unroll
-      for (int j = 0; j < T; ++j)
+      for (int j = 0; j < G::TL; ++j)
 #pragma unroll
         for (int m = 0; m < G::RKB / 1024; ++m)
           dma16(a.rec_k + ((((size_t)j * a.R + r) * a.Wm + sl[j]) * a.Hk + h / a.gq) * DK + (m * 4 + cg) * 8,
@@ -273,21 +276,61 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
       for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int e = 0; e < 4; ++e) sqq = dot2(kf[s][e], qf[s][e], sqq);
+      // Depths past the staged ones: their keys straight from the record
+      // store, one depth at a time with the next depth's loads in flight
+      // (lane (g, c) takes channels 32s + 8g .. +7 of beam c's key, the
+      // fragment the staged layout would give it).
+      constexpr int TG = T > G::TL ? T - G::TL : 1;
+      float pqg[TG], pkg[TG];
+      if constexpr (T > G::TL) {
+        const int posi = min(p * 16 + c, nb - 1);
+        auto load_key = [&](int j, u32x4* kj) {
+          const int slot = s_slot_hi[(j - 3) * kMaxChunkF + posi];
+          const uint16_t* key = a.rec_k + ((((size_t)j * a.R + r) * a.Wm + slot) * a.Hk + h / a.gq) * DK;
+#pragma unroll
+          for (int s = 0; s < KS; ++s) kj[s] = *reinterpret_cast<const u32x4*>(key + s * 32 + g * 8);
+        };
+        u32x4 cur[KS], nxt[KS];
+        load_key(G::TL, cur);
+#pragma unroll
+        for (int j = G::TL; j < T; ++j) {
+          if (j + 1 < T) load_key(j + 1, nxt);
+          float pq = 0.f, pk = 0.f;
+#pragma unroll
+          for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pq = dot2(cur[s][e], qf[s][e], pq);
+              pk = dot2(cur[s][e], kf[s][e], pk);
+            }
+          pqg[j - G::TL] = sum_lane_groups(pq);
+          pkg[j - G::TL] = sum_lane_groups(pk);
+#pragma unroll
+          for (int s = 0; s < KS; ++s) cur[s] = nxt[s];
+        }
+      }
       float cdec = sm[c];  // alpha_t
 #pragma unroll
       for (int j = T - 1; j >= 0; --j) {
         float pq = 0.f, pk = 0.f;
+        if (j < G::TL) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const u32x4 kj = *reinterpret_cast<const u32x4*>(buf + G::ORK + j * G::RKB + (s * 64 + lane) * 16);
+          for (int s = 0; s < KS; ++s) {
+            const u32x4 kj = *reinterpret_cast<const u32x4*>(buf + G::ORK + j * G::RKB + (s * 64 + lane) * 16);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pq = dot2(kj[e], qf[s][e], pq);
-            pk = dot2(kj[e], kf[s][e], pk);
+            for (int e = 0; e < 4; ++e) {
+              pq = dot2(kj[e], qf[s][e], pq);
+              pk = dot2(kj[e], kf[s][e], pk);
+            }
           }
+          pq = sum_lane_groups(pq);
+          pk = sum_lane_groups(pk);
+        } else {
+          pq = pqg[j >= G::TL ? j - G::TL : 0];
+          pk = pkg[j >= G::TL ? j - G::TL : 0];
         }
-        wt[3 + j] = cdec * sum_lane_groups(pq);
-        wt[3 + T + j] = cdec * sum_lane_groups(pk);
+        wt[3 + j] = cdec * pq;
+        wt[3 + T + j] = cdec * pk;
         cdec *= sm[(2 + j) * 16 + c];
       }
       wt[0] = cdec;
@@ -389,11 +432,16 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     if (it + 1 < ntiles) load_deltas(it + 1, dnext);
 
     const uint8_t* buf = smem + (it % G::NBUF) * G::BUF;
-    u32x4 qf[KS], kf[KS];
+    // the tile's q and k fragments (B operands); with d_k = 256 each is read
+    // at its MFMA step instead, so that 64 registers stay free for the chain
+    constexpr bool kBInLoop = DK > 128;
+    u32x4 qf[kBInLoop ? 1 : KS], kf[kBInLoop ? 1 : KS];
+    if constexpr (!kBInLoop) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      qf[s] = *reinterpret_cast<const u32x4*>(buf + G::OQ + (s * 64 + lane) * 16);
-      kf[s] = *reinterpret_cast<const u32x4*>(buf + G::OKK + (s * 64 + lane) * 16);
+      for (int s = 0; s < KS; ++s) {
+        qf[s] = *reinterpret_cast<const u32x4*>(buf + G::OQ + (s * 64 + lane) * 16);
+        kf[s] = *reinterpret_cast<const u32x4*>(buf + G::OKK + (s * 64 + lane) * 16);
+      }
     }
     const int vch = w * 2 + (g >> 1);  // 16-byte v chunk holding rows row0 .. row0 + 3
     const u32x2 vw = *reinterpret_cast<const u32x2*>(buf + G::OV + ((vch >> 2) * 64 + (vch & 3) * 16 + c) * 16 +
@@ -409,12 +457,21 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     // S0^T [q | k] on the matrix cores, smallest plane first
     f32x4 uq = {0.f, 0.f, 0.f, 0.f}, uk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s) {
+      u32x4 qs, kss;
+      if constexpr (kBInLoop) {
+        qs = *reinterpret_cast<const u32x4*>(buf + G::OQ + (s * 64 + lane) * 16);
+        kss = *reinterpret_cast<const u32x4*>(buf + G::OKK + (s * 64 + lane) * 16);
+      } else {
+        qs = qf[s];
+        kss = kf[s];
+      }
 #pragma unroll
       for (int p = NPL - 1; p >= 0; --p) {
-        uq = mfma16x16x32(As[s][p], qf[s], uq);
-        uk = mfma16x16x32(As[s][p], kf[s], uk);
+        uq = mfma16x16x32(As[s][p], qs, uq);
+        uk = mfma16x16x32(As[s][p], kss, uk);
       }
+    }
 
     // replay (§3.2) with the dot wave's weights, then the current transition
     f32x4 xq = wt[0] * uq, xk = wt[0] * uk;
@@ -440,10 +497,15 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     const int off_o = live ? ib * so + row0 * 4 : kOutside;
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, off_o, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, off_o, 0, 0);
-    u32x4 kk = kf[0];
+    u32x4 kk;
+    if constexpr (kBInLoop) {
+      kk = *reinterpret_cast<const u32x4*>(buf + G::OKK + (ks * 64 + lane) * 16);
+    } else {
+      kk = kf[0];
 #pragma unroll
-    for (int s = 1; s < KS; ++s)
-      if (ks == s) kk = kf[s];
+      for (int s = 1; s < KS; ++s)
+        if (ks == s) kk = kf[s];
+    }
     const int off_k = live && key_writer && slice0 ? ib * sk + (ks * 32 + g * 8 + kh * 4) * 2 : kOutside;
     if constexpr (G::NC == 2 * KS)
       __builtin_amdgcn_raw_buffer_store_b64(kh ? u32x2{kk[2], kk[3]} : u32x2{kk[0], kk[1]}, w_k, off_k, 0, 0);
@@ -489,9 +551,9 @@ int launch(const gdn_shape& sh, const gdn_store& st, int Wt, const StepIO& io, h
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
-// longest chain built for a d_k: record keys of every depth share a tile
-// buffer, so d_k = 256 fits three depths in LDS
-constexpr int max_steps(int dk) { return dk > 128 ? 3 : kFusedMaxSteps; }
+// longest chain built (the same for every d_k: with d_k = 256 the keys of
+// depths past the third come from memory, not the tile buffer)
+constexpr int max_steps(int) { return kFusedMaxSteps; }
 
 template <int DK, int DV>
 int launch_dims(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io, hipStream_t stream) {

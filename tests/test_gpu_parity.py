@@ -182,6 +182,25 @@ def test_wider_geometries(dk, dv, channel, Hk):
     assert rel_states(merged, ref) <= TOL
 
 
+@pytest.mark.parametrize("dv", [128, 512])
+def test_wide_state_long_chains(dv):
+    """d_k = 256 with chains of up to six records: the keys of depths 3 .. 5
+    come from the record store, not the tile buffer (depth-first schedule with
+    one chunk per (request, head), and chunk order)."""
+    inp = synth.make_inputs(R=2, H=2, dk=256, dv=dv, W=48, L=7, s0_std=0.05, seed=620 + dv // 128,
+                            parents="topk", widths=[48, 41, 48, 37, 48, 45, 48], Hk=1)
+    store, _, _ = check_beam(inp, False, label=f"dk=256 dv={dv} L=7")
+    pairs = np.array([[0, 5], [1, 47]], np.int32)
+    S = B.materialize(store, 6, torch.from_numpy(pairs).cuda()).cpu().numpy()
+    assert rel_states(S, O.beam_states(inp["S0"], inp["steps"], 6, [tuple(p) for p in pairs])) <= TOL
+
+
+def test_wide_state_long_chains_one_chunk(monkeypatch):
+    monkeypatch.setenv("GDN_BEAM_CHUNK", "512")
+    inp = synth.make_inputs(R=2, H=2, dk=256, dv=256, W=48, L=7, s0_std=0.05, seed=630, parents="topk_hot")
+    check_beam(inp, False, label="dk=256 dv=256 L=7 one chunk")
+
+
 def test_wide_state_beams_over_many_workgroups():
     """d_k = 256, d_v = 512 with one request: four value slices, each cut into
     16-beam chunks (chunk order, ragged last chunk), two value heads sharing
