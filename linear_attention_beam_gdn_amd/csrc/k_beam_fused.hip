@@ -28,7 +28,9 @@
 //       c_j = alpha_t prod_{i >= j} alpha_i,  c_T = alpha_t,
 //   so the consumers' replay is one FMA per record and value row.  It
 //   publishes c_0, beta_t, k_t . q_t and the 2T record weights in the tile's
-//   LDS buffer.
+//   LDS buffer.  With d_k = 256 a tile buffer holds the keys of three record
+//   depths; the dot wave loads the keys of deeper ones from the record store
+//   itself, one depth at a time.
 // * Consumer waves (one per 16 value rows of the slice, two per SIMD for
 //   128 rows).  Each holds its 16-row part of the shared state S0[r, h] in
 //   registers for the whole chunk as three bf16 planes (hi + mid + lo, each
