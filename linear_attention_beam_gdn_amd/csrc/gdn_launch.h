@@ -37,8 +37,9 @@ bool beam_fused_supported(const gdn_shape& sh, int t);
 int launch_beam_fused(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
                       hipStream_t stream);
 
-// Channel-decay beams with (d_k, d_v) in {64, 128} and chains of at most 3
-// records: the same pipeline with 8-beam tiles.
+// Channel-decay beams with d_k = d_v = 64, or d_k = 128 and d_v in {128,
+// 256, 512}, and chains of at most 6 records: the same pipeline with 8-beam
+// tiles.
 bool beam_fused_kda_supported(const gdn_shape& sh, int t);
 int launch_beam_fused_kda(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,
                           hipStream_t stream);

@@ -26,7 +26,8 @@
 //     wave takes the q or the k row of a beam, walks the chain from the
 //     current step down (y = a_t * x; weight_j = k_j . y; y = a_j * y), and
 //     writes the probe Q_0 * x as hi and lo bf16 planes over the raw row, the
-//     record weights and k_t . q_t; in the first value slice it also appends
+//     record weights and k_t . q_t (chains of up to six records); in the
+//     first value slice it also appends
 //     the beam's key row and decay vector to the record store;
 //   - then finishes the current tile: hi*hi + hi*lo + lo*hi plane products
 //     on the matrix cores, the q- and k-halves of the result exchanged with
@@ -77,19 +78,22 @@ struct KdaGeom {
   static constexpr int OQK = 0, OV = QKB, OA = OV + VB, OLO = OA, OS = OA + AB, OW = OS + SMB, ORK = OW + WTB,
                        ORA = ORK + T * RKB;
   static constexpr int BUF = ORA + T * AB;
-  static_assert(T <= 3, "the channel-decay kernel takes at most three record depths");
-  static constexpr int SLOTB = T > 0 ? kMaxChunkF * 16 : 0;
+  static_assert(T <= 6, "the channel-decay kernel takes at most six record depths");
+  // schedule table: per position {beam, slot_0, slot_1, slot_2}, plus slots 3 .. T-1
+  static constexpr int SLOTB = T > 0 ? kMaxChunkF * 16 + (T > 3 ? (T - 3) * kMaxChunkF * 4 : 0) : 0;
   static constexpr int NBUF0 = (kLdsBytes - SLOTB) / BUF;
   static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
   static_assert(NBUF >= 3, "tile buffers do not fit in LDS");
   // The slice of S0[r, h] ([d_k][VS]) is staged in LDS past the first two
-  // tile buffers until the consumers have split it into planes; the
-  // schedule's scratch is the first two.
+  // tile buffers until the consumers have split it into planes, when it fits
+  // (chains of up to five records); otherwise the consumers load it from HBM
+  // themselves.  The schedule's scratch is the first two buffers.
   static constexpr int S0B = DK * VS * 4, OS0 = 2 * BUF;
-  static constexpr int RINGB = NBUF * BUF > OS0 + S0B ? NBUF * BUF : OS0 + S0B;
+  static constexpr bool S0_LDS = OS0 + S0B + SLOTB <= kLdsBytes;
+  static constexpr int RINGB = (S0_LDS && OS0 + S0B > NBUF * BUF) ? OS0 + S0B : NBUF * BUF;
   static constexpr int LDS = RINGB + SLOTB;
   static_assert(LDS <= kLdsBytes, "LDS layout does not fit");
-  static_assert(S0B % 1024 == 0, "S0 is staged in whole DMA blocks");
+  static_assert(!S0_LDS || S0B % 1024 == 0, "S0 is staged in whole DMA blocks");
   // LDS-DMA instructions per tile (q|k, v, alpha_t, beta_t, then per record k_j, a_j)
   static constexpr int OPT = QKB / 1024 + VB / 1024 + AB / 1024 + 1 + T * (RKB / 1024 + AB / 1024);
   static_assert(QKB % 1024 == 0 && VB % 1024 == 0 && AB % 1024 == 0 && RKB % 1024 == 0,
@@ -161,7 +165,7 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   constexpr int TT = T > 0 ? T : 1;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
   u32x4* s_tab = reinterpret_cast<u32x4*>(smem + G::RINGB);
-  int* s_slot_hi = reinterpret_cast<int*>(smem + G::RINGB + kMaxChunkF * 16);  // unused: T <= 3
+  int* s_slot_hi = reinterpret_cast<int*>(smem + G::RINGB + kMaxChunkF * 16);  // depths 3 .. T-1
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -191,11 +195,13 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     // the slice of S0[r, h] into LDS as [d_k][VS] (wave 1), after the
     // schedule's loads have gone out; 256 floats per DMA instruction
     auto stage_s0 = [&] {
-      const float* S = a.S + ((size_t)r * a.H + h) * DK * DV + vs0;
+      if constexpr (G::S0_LDS) {
+        const float* S = a.S + ((size_t)r * a.H + h) * DK * DV + vs0;
 #pragma unroll
-      for (int m = 0; m < G::S0B / 1024; ++m) {
-        const int e0 = m * 256 + lane * 4;
-        dma16(S + (size_t)(e0 / G::VS) * DV + e0 % G::VS, smem + G::OS0 + m * 1024);
+        for (int m = 0; m < G::S0B / 1024; ++m) {
+          const int e0 = m * 256 + lane * 4;
+          dma16(S + (size_t)(e0 / G::VS) * DV + e0 % G::VS, smem + G::OS0 + m * 1024);
+        }
       }
     };
     if (T > 0) {
@@ -213,13 +219,15 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     auto dma_tile = [&](int p) {
       uint8_t* buf = smem + (p % G::NBUF) * G::BUF;
       const int posi = min(p * G::TB + (lane & 7), nb - 1);  // positions past the chunk repeat its last
-      int ib = posi, sl[3] = {0, 0, 0};
+      int ib = posi, sl[TT > 3 ? TT : 3] = {};
       if constexpr (T > 0) {
         const u32x4 e = lds_read128_opaque(&s_tab[posi]);
         ib = (int)e[0];
         sl[0] = (int)e[1];
         sl[1] = (int)e[2];
         sl[2] = (int)e[3];
+#pragma unroll
+        for (int j = 3; j < T; ++j) sl[j] = lds_read_opaque(&s_slot_hi[(j - 3) * kMaxChunkF + posi]);
       }
       const size_t tok = ((size_t)r * a.Wt + b_begin + ib) * a.H + h;
       // q|k: rows 0-7 the q rows, rows 8-15 the k rows of the tile's beams
@@ -379,8 +387,16 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   const int c = lane & 15;
   const int bb = c & 7;     // beam of this lane within the tile
   const int side = c >> 3;  // 0: q column, 1: k column
-  // A DMA wave stages S0 in LDS; the planes are formed between barriers S
-  // and A.
+  // A DMA wave stages S0 in LDS, or (chains of six records) each lane loads
+  // its entries from HBM here; the planes are formed between barriers S and A.
+  float s0x[G::S0_LDS ? 1 : KS][8];
+  if constexpr (!G::S0_LDS) {
+    const float* Sg = a.S + ((size_t)r * a.H + h) * DK * DV + vs0 + w * 16 + c;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s0x[s][e] = Sg[(size_t)(s * 32 + g * 8 + e) * DV];
+  }
   if (T > 0) lds_barrier();  // Q
   const int row0 = vs0 + w * 16 + 4 * g;
   const int so = a.H * DV * 4;
@@ -392,7 +408,9 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     if constexpr (T > 0) {
       const int posi = min(p * G::TB + bb, nb - 1);
       const u32x4 e = s_tab[posi];
-      const int sl[3] = {(int)e[1], (int)e[2], (int)e[3]};
+      int sl[TT > 3 ? TT : 3] = {(int)e[1], (int)e[2], (int)e[3]};
+#pragma unroll
+      for (int j = 3; j < T; ++j) sl[j] = s_slot_hi[(j - 3) * kMaxChunkF + posi];
 #pragma unroll
       for (int j = 0; j < T; ++j) {
         const size_t rj = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + h;
@@ -406,7 +424,7 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   load_deltas(0, dnext);
   lds_barrier();  // S: S0 staged
   u32x4 As[KS][2];
-  {
+  if constexpr (G::S0_LDS) {
     const float* S = reinterpret_cast<const float*>(smem + G::OS0);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -415,6 +433,9 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       for (int e = 0; e < 8; ++e) x[e] = S[(s * 32 + g * 8 + e) * G::VS + w * 16 + c];
       split_planes<2>(x, As[s]);
     }
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) split_planes<2>(s0x[s], As[s]);
   }
   lds_barrier();  // A: tile 0 resident
   prep(0);
@@ -529,6 +550,9 @@ int launch_dims(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const S
     case 1: return launch<DK, DV, 1>(sh, st, Wt, io, stream);
     case 2: return launch<DK, DV, 2>(sh, st, Wt, io, stream);
     case 3: return launch<DK, DV, 3>(sh, st, Wt, io, stream);
+    case 4: return launch<DK, DV, 4>(sh, st, Wt, io, stream);
+    case 5: return launch<DK, DV, 5>(sh, st, Wt, io, stream);
+    case 6: return launch<DK, DV, 6>(sh, st, Wt, io, stream);
     default: return GDN_EUNSUPPORTED;
   }
 }
@@ -536,7 +560,7 @@ int launch_dims(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const S
 }  // namespace
 
 bool beam_fused_kda_supported(const gdn_shape& sh, int t) {
-  return sh.decay_kind == GDN_DECAY_CHANNEL && t >= 0 && t <= 3 &&
+  return sh.decay_kind == GDN_DECAY_CHANNEL && t >= 0 && t <= 6 &&
          ((sh.dk == 64 && sh.dv == 64) || (sh.dk == 128 && (sh.dv == 128 || sh.dv == 256 || sh.dv == 512))) &&
          windows_fit(sh);
 }

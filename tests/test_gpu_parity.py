@@ -124,14 +124,23 @@ def test_ragged_widths(dims, channel):
     check_beam(inp, channel, label=f"ragged dk={dk} ch={channel}")
 
 
-@pytest.mark.parametrize("dims", [(32, 32), (64, 64), (128, 128)])
-def test_chains_up_to_six_records(dims):
+@pytest.mark.parametrize("dims,channel", [((32, 32), False), ((64, 64), False), ((128, 128), False),
+                                          ((64, 64), True), ((128, 128), True), ((128, 512), True)])
+def test_chains_up_to_six_records(dims, channel):
     """Steps t = 5, 6 (the longest chains of the OneLA operator suite, T = 6)
-    on the fused kernel, with ragged widths."""
+    on the fused kernels (scalar and channel decay; at channel decay the
+    chain of six records takes S0 from HBM, not LDS), with ragged widths."""
     dk, dv = dims
-    inp = synth.make_inputs(R=2, H=2, dk=dk, dv=dv, W=37, L=7, s0_std=0.1, seed=200 + dk,
-                            parents="topk", widths=[37, 29, 37, 20, 33, 37, 17])
-    check_beam(inp, False, label=f"L=7 dk={dk}")
+    inp = synth.make_inputs(R=2, H=2, dk=dk, dv=dv, W=37, L=7, s0_std=0.1, seed=200 + dk + dv // 64,
+                            parents="topk", widths=[37, 29, 37, 20, 33, 37, 17], channel_decay=channel)
+    check_beam(inp, channel, label=f"L=7 dk={dk} dv={dv} ch={channel}")
+
+
+def test_channel_decay_long_chains_one_chunk(monkeypatch):
+    monkeypatch.setenv("GDN_BEAM_CHUNK", "512")
+    inp = synth.make_inputs(R=2, H=2, dk=128, dv=128, W=40, L=7, s0_std=0.1, seed=240, parents="topk_hot",
+                            channel_decay=True)
+    check_beam(inp, True, label="channel decay L=7 one chunk")
 
 
 @pytest.mark.parametrize("channel", [False, True])
