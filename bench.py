@@ -225,6 +225,11 @@ def sequence_row(B, torch, dev, stream, wl):
         if i % wl.M == wl.M - 1:
             calls.append(lambda: B.log_merge(store, wl.M, 0, stream=stream))
             kinds.append(-1)
+    # one untimed pass first (the first launch of a kernel also loads its code
+    # object; a pass over T = a multiple of M tokens leaves the log empty)
+    for fn in calls:
+        fn()
+    torch.cuda.synchronize()
     d = _queued(torch, stream, calls)
     dec_us = [float(np.mean([x for x, k in zip(d, kinds) if k == j])) for j in range(wl.M)]
     merge_us = float(np.mean([x for x, k in zip(d, kinds) if k == -1]))
@@ -241,7 +246,11 @@ def sequence_row(B, torch, dev, stream, wl):
         else:
             B.decode_step(fstore, i % wl.M, 1, zero, *args, o=o, stream=stream)
 
-    df = _queued(torch, stream, [(lambda i=i: fused(i)) for i in range(wl.T)])
+    fcalls = [(lambda i=i: fused(i)) for i in range(wl.T)]
+    for fn in fcalls:
+        fn()
+    torch.cuda.synchronize()
+    df = _queued(torch, stream, fcalls)
     fdec_us = [float(np.mean(df[j::wl.M])) for j in range(wl.M)]
 
     # one merge cycle of the fused path captured in a HIP graph and replayed

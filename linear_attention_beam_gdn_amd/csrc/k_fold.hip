@@ -75,7 +75,10 @@ __global__ __launch_bounds__((FoldGeom<DK, DV>::NT)) void k_fold(FoldArgs a) {
     st[i] = *reinterpret_cast<const f32x4*>(src + (size_t)(row0 + i) * DV + c4 * 4);
 
   const int32_t* arow = a.anc + (((size_t)t * a.R + r) * a.Wm + b) * a.L;
-  for (int j = 0; j <= t; ++j) {
+  // (a do-while: t >= 0, and this loop shape keeps the state in one set of
+  // registers across the loop instead of a copy per entry)
+  int j = 0;
+  do {
     const int slot = j < t ? clampi(arow[j], 0, a.Wm - 1) : b;
     const size_t rj = (((size_t)j * a.R + r) * a.Wm + slot) * a.H + h;
     const size_t rjk = (((size_t)j * a.R + r) * a.Wm + slot) * a.Hk + h / a.gq;
@@ -88,7 +91,7 @@ __global__ __launch_bounds__((FoldGeom<DK, DV>::NT)) void k_fold(FoldArgs a) {
       const float aj = CH ? a.rec_alpha[rj * A + row] : aj0;
       st[i] = apply_record(st[i], aj, kj, dj);
     }
-  }
+  } while (++j <= t);
 #pragma unroll
   for (int i = 0; i < G::RPG; ++i)
     *reinterpret_cast<f32x4*>(dst + (size_t)(row0 + i) * DV + c4 * 4) = st[i];
