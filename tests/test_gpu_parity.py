@@ -14,6 +14,8 @@ from gpu_util import TOL, log, rel_slices, rel_states, run_beam, step_records
 from linear_attention_beam_gdn_amd import binding as B
 from linear_attention_beam_gdn_amd import configs, synth
 
+GDN_MAX = B.GDN_MAX_STEPS  # longest log a store holds
+
 pytestmark = pytest.mark.gpu
 
 
@@ -320,6 +322,47 @@ def test_decode_merge_step(kind):
             S = fused.S.cpu().numpy().reshape(R * H, 1, dk, dv)
             assert rel_states(S, ref["bases"][i // M][:, None]) <= TOL
     log(f"[parity] decode+merge fused {kind}: equal to decode-then-merge")
+
+
+
+@pytest.mark.parametrize("dk", [16, 128])
+@pytest.mark.parametrize("kind", ["scalar", "channel", "plain"])
+def test_sequences_full_log_capacity(dk, kind):
+    """Logs of the largest capacity (16 records): every log length 0 .. 15,
+    so the sequence kernel stages up to 17 key rows, 15 update vectors and 16
+    decay rows (at d = 128 the second round of staged loads; at d = 16 the
+    64 threads are exactly filled).  Decode-then-merge and the fused merge
+    path agree bit for bit, and both match the oracle, over two full cycles."""
+    channel, plain = kind != "scalar", kind == "plain"
+    R, H, M = 2, 3, GDN_MAX
+    T = 2 * M
+    seq = synth.make_sequence_inputs(R=R, H=H, dk=dk, dv=dk, T=T, s0_std=0.1, seed=23,
+                                     channel_decay=channel)
+    ref = O.sequence_decode(seq["S0"], seq["tokens"], M, rule="plain" if plain else "delta")
+    S0 = torch.from_numpy(seq["S0"]).cuda()
+    fused = B.Store(R, 1, H, dk, dk, M, channel_decay=channel, plain_update=plain, S=S0.clone())
+    split = B.Store(R, 1, H, dk, dk, M, channel_decay=channel, plain_update=plain, S=S0.clone())
+    zero = torch.zeros(R, 1, dtype=torch.int32, device="cuda")
+    worst = 0.0
+    for i in range(T):
+        t = i % M
+        d = B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")})
+        args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        o_f = B.decode_merge_step(fused, t, *args) if t == M - 1 else B.decode_step(fused, t, 1, zero, *args)
+        o_s = B.decode_step(split, t, 1, zero, *args)
+        if t == M - 1:
+            B.log_merge(split, M, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(o_f, o_s), i
+        e = rel_slices(o_f[:, 0].cpu().numpy().reshape(R * H, dk), ref["o"][i])
+        worst = max(worst, e)
+        assert e <= TOL, (i, e)
+        if t == M - 1:
+            assert torch.equal(fused.S, split.S), i
+            e = rel_states(fused.S.cpu().numpy().reshape(R * H, 1, dk, dk), ref["bases"][i // M][:, None])
+            worst = max(worst, e)
+            assert e <= TOL, (i, e)
+    log(f"[parity] full log capacity d={dk} {kind}: max rel err {worst:.2e}")
 
 
 # ---------------------------------------------------------------- edge cases
