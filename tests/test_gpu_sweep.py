@@ -90,7 +90,7 @@ def _check_geometry(case):
     log(f"[sweep] case {c['id']}: max rel err {max(worst, es):.2e}")
 
 
-def _seq_cases(n=30, seed=4048):
+def _seq_cases(n=30, seed=4048, m_range=(1, 9), long_logs=False):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -102,12 +102,20 @@ def _seq_cases(n=30, seed=4048):
         fused = (dk, dv) in square and bool(rng.random() < 0.6)  # the merge in the decode: square shapes
         H = int(rng.choice([1, 2, 3, 4, 6]))
         Hk = int(rng.choice([d for d in range(1, H + 1) if H % d == 0]))
-        out.append(dict(id=i, kind=kind, dk=dk, dv=dv, H=H, Hk=Hk, R=int(rng.integers(1, 6)), T=int(rng.integers(1, 21)),
-                        M=int(rng.integers(1, 9)), fused=fused, seed=1900 + i))
+        if not long_logs:
+            out.append(dict(id=i, kind=kind, dk=dk, dv=dv, H=H, Hk=Hk, R=int(rng.integers(1, 6)),
+                            T=int(rng.integers(1, 21)), M=int(rng.integers(*m_range)), fused=fused, seed=1900 + i))
+        else:
+            M = int(rng.integers(*m_range))
+            out.append(dict(id=i, kind=kind, dk=dk, dv=dv, H=H, Hk=Hk, R=int(rng.integers(1, 4)),
+                            T=int(rng.integers(M, 2 * M + 4)), M=M, fused=fused, seed=2900 + i))
     return out
 
 
 SEQ_CASES = _seq_cases()
+# long logs (capacity 9 .. 16, the largest a store holds): one or two merges
+# per case, every log length up to M - 1
+SEQ_LONG_CASES = _seq_cases(n=16, seed=5150, m_range=(9, 17), long_logs=True)
 
 
 @pytest.mark.parametrize("case", SEQ_CASES, ids=[f"s{c['id']}" for c in SEQ_CASES])
@@ -115,7 +123,16 @@ def test_random_sequences(case):
     """Bounded-log decoding of independent sequences over a seeded sweep: log
     capacity M, token count, decay kind and update rule, key heads, and the
     merge either fused into the decode that fills the log or run separately."""
-    c = case
+    _check_sequences(case)
+
+
+@pytest.mark.parametrize("case", SEQ_LONG_CASES, ids=[f"l{c['id']}" for c in SEQ_LONG_CASES])
+def test_random_sequences_long_logs(case):
+    """The same sweep with long logs (capacity 9 .. 16)."""
+    _check_sequences(case)
+
+
+def _check_sequences(c):
     channel, plain = c["kind"] != "scalar", c["kind"] == "plain"
     R, H, dk, dv, T, M = c["R"], c["H"], c["dk"], c["dv"], c["T"], c["M"]
     label = f"seq case {c['id']}: {c['kind']} dk={dk} dv={dv} R={R} H={H} Hk={c['Hk']} T={T} M={M} fused={c['fused']}"
