@@ -86,15 +86,29 @@ struct FusedGeom {
   static constexpr int NSM = (2 + T) * 16 > 64 ? 2 : 1;  // dword DMAs: alpha_t, beta_t, alpha_j
   static constexpr int SMB = NSM * 256;
   static constexpr int RKB = 16 * DK * 2;  // keys of one record depth
-  // record-key depths staged in the tile buffer; with d_k = 256 only three
-  // fit, and the dot wave gathers the keys of depths 3 .. T-1 from memory
-  static constexpr int TL = (DK > 128 && T > 3) ? 3 : T;
   static constexpr int NWT = (3 + 2 * T + 3) / 4 * 4;  // weights per beam, padded to 16 B
   static constexpr int WTB = 16 * NWT * 4;
   static constexpr int OQ = 0, OKK = QB, OV = 2 * QB, OS = 2 * QB + VB, OW = OS + SMB, ORK = OW + WTB;
-  static constexpr int BUF = ORK + TL * RKB;
   // schedule table: per position {beam, slot_0, slot_1, slot_2}, plus slot_3
   static constexpr int SLOTB = T > 0 ? kMaxChunkF * 16 + (T > 3 ? (T - 3) * kMaxChunkF * 4 : 0) : 0;
+  // Record-key depths staged in the tile buffer (the dot wave gathers the
+  // keys of the others, depths TL .. T-1, from memory).  Up to d_k = 128
+  // every depth is staged.  A d_k = 256 depth takes 8 KiB of every buffer,
+  // so there the most depths (at most three) are staged that leave room for
+  // four ring buffers (a DMA wave's next tile in flight while the consumers
+  // and the dot wave hold two) with the dot wave gathering at most two
+  // depths (more and its gathers pace the pipeline); else three.  Measured
+  // at 8 x 512 beams, H = 16, d_v = 512: t = 3 and 4 take 204 and 222 us
+  // with two staged depths, against 231 and 240 us with three.
+  static constexpr int staged_depths() {
+    if (DK <= 128) return T;
+    const int most = T < 3 ? T : 3;
+    for (int tl = most; tl >= 1 && T - tl <= 2; --tl)
+      if ((kLdsBytes - SLOTB) / (ORK + tl * RKB) >= 4) return tl;
+    return most;
+  }
+  static constexpr int TL = staged_depths();
+  static constexpr int BUF = ORK + TL * RKB;
   static constexpr int NBUF0 = (kLdsBytes - SLOTB) / BUF;
   static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
   static_assert(NBUF >= 3, "tile buffers do not fit in LDS");
@@ -287,7 +301,7 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
       if constexpr (T > G::TL) {
         const int posi = min(p * 16 + c, nb - 1);
         auto load_key = [&](int j, u32x4* kj) {
-          const int slot = s_slot_hi[(j - 3) * kMaxChunkF + posi];
+          const int slot = j < 3 ? (int)s_tab[posi][1 + j] : s_slot_hi[(j - 3) * kMaxChunkF + posi];
           const uint16_t* key = a.rec_k + ((((size_t)j * a.R + r) * a.Wm + slot) * a.Hk + h / a.gq) * DK;
 #pragma unroll
           for (int s = 0; s < KS; ++s) kj[s] = *reinterpret_cast<const u32x4*>(key + s * 32 + g * 8);
