@@ -158,7 +158,7 @@ def beam_row(B, torch, dev, stream, wl, reps):
                                             channel_decay=wl.channel_decay, unique_records=uniq, Hk=wl.Hk)
         per.append(_bw(nbytes, us[t]))
     tot_b, tot_us = sum(p["bytes"] for p in per), sum(us)
-    return {"workload": wl.name, "beam_steps_per_s": wl.R * wl.W * wl.L / (tot_us * 1e-6),
+    return {"workload": wl.name, "decode_steps": wl.L, "beam_steps_per_s": wl.R * wl.W * wl.L / (tot_us * 1e-6),
             "launch_us": us, **{k: v for k, v in _bw(tot_b / wl.L, tot_us / wl.L).items() if k != "us"}}
 
 
@@ -492,6 +492,13 @@ def main():
             "shared_key_heads_beam_decode": lambda: beam_row(B, torch, dev, stream, configs.SHARED_KEYS, reps),
             "wide_state_beam_decode": lambda: beam_row(B, torch, dev, stream, configs.WIDE, reps),
             "channel_decay_wide_value_beam_decode": lambda: beam_row(B, torch, dev, stream, configs.KDA_WIDE, reps),
+            # chains to the OneLA operator suite's longest (T = 6): the same
+            # workloads decoded for seven steps, t = 0 .. 6
+            "long_chain_beam_decode": lambda: beam_row(B, torch, dev, stream, dataclasses.replace(WORKLOAD, L=7), reps),
+            "wide_state_long_chain_beam_decode": lambda: beam_row(B, torch, dev, stream,
+                                                                  dataclasses.replace(configs.WIDE, L=7), reps),
+            "channel_decay_long_chain_beam_decode": lambda: beam_row(B, torch, dev, stream,
+                                                                     dataclasses.replace(configs.KDA, L=7), reps),
             "bounded_log_decode_and_merge": lambda: sequence_row(B, torch, dev, stream, configs.DELTALOG),
             "bounded_log_merge_interval": lambda: merge_interval_row(B, torch, dev, stream, configs.DELTALOG,
                                                                      (4, 8, 16)),

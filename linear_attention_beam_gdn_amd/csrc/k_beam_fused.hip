@@ -92,17 +92,17 @@ struct FusedGeom {
   // schedule table: per position {beam, slot_0, slot_1, slot_2}, plus slot_3
   static constexpr int SLOTB = T > 0 ? kMaxChunkF * 16 + (T > 3 ? (T - 3) * kMaxChunkF * 4 : 0) : 0;
   // Record-key depths staged in the tile buffer (the dot wave gathers the
-  // keys of the others, depths TL .. T-1, from memory).  Up to d_k = 128
-  // every depth is staged.  A d_k = 256 depth takes 8 KiB of every buffer,
-  // so there the most depths (at most three) are staged that leave room for
-  // four ring buffers (a DMA wave's next tile in flight while the consumers
-  // and the dot wave hold two) with the dot wave gathering at most two
-  // depths (more and its gathers pace the pipeline); else three.  Measured
-  // at 8 x 512 beams, H = 16, d_v = 512: t = 3 and 4 take 204 and 222 us
-  // with two staged depths, against 231 and 240 us with three.
+  // keys of the others, depths TL .. T-1, from memory).  Staged are the most
+  // depths (every one up to d_k = 128, at most three at d_k = 256, where a
+  // depth takes 8 KiB of every buffer) that leave room for four ring
+  // buffers (a DMA wave's next tile in flight while the consumers and the
+  // dot wave hold two) with the dot wave gathering at most two depths (more
+  // and its gathers pace the pipeline); if none does, all that fit.
+  // Measured at 8 x 512 beams, H = 16, d_k = 256, d_v = 512: t = 3 and 4 take
+  // 204 and 222 us with two staged depths, against 231 and 240 us with
+  // three; at d_k = d_v = 128, H = 32, t = 6 stages five.
   static constexpr int staged_depths() {
-    if (DK <= 128) return T;
-    const int most = T < 3 ? T : 3;
+    const int most = DK > 128 ? (T < 3 ? T : 3) : T;
     for (int tl = most; tl >= 1 && T - tl <= 2; --tl)
       if ((kLdsBytes - SLOTB) / (ORK + tl * RKB) >= 4) return tl;
     return most;
