@@ -419,6 +419,30 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 2 * src.numel() * 4 / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
 
+    # The same buffers at other read:write mixes (HBM turns the bus around
+    # between reads and writes, so the rate depends on the mix): writes only
+    # (a fill), one read to two writes (each element read once, written
+    # twice), and two reads to one write (an add).
+    def _rate(fn, nbytes):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(10):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return nbytes / (a.elapsed_time(b) / 10 * 1e-3) / 1e9
+
+    half = src.numel() // 2
+    stream_rates = {
+        "writes_only": _rate(lambda: dst.fill_(1.0), 4 * src.numel()),
+        "reads1_writes2": _rate(lambda: dst.view(half, 2).copy_(src[:half].unsqueeze(1).expand(half, 2)),
+                                3 * half * 4),
+        "reads1_writes1": copy_gbps,
+        "reads2_writes1": _rate(lambda: torch.add(src[:half], src[half:], out=dst[:half]), 3 * half * 4),
+    }
+
     # Per-launch durations of the decode kernel, from HIP events recorded on
     # the launch stream around every launch (a second live loop of K passes;
     # the events themselves add a few microseconds between launches).  The
@@ -442,6 +466,17 @@ def main():
         step_bytes.append(accounting.beam_step_bytes(unique_records=uniq, **kw))
         gather_bytes.append(accounting.beam_step_bytes(**kw))
     mean_bytes = float(np.mean(step_bytes))
+    # each launch's read fraction, and the streaming rate of that mix on this
+    # GPU (piecewise linear between the measured mixes); frac_of_mix_matched
+    # is the time those rates would take for the launches' bytes over the
+    # launches' measured time
+    write_bytes = [accounting.beam_step_write_bytes(R=w.R, H=w.H, dk=w.dk, dv=w.dv, W_t=w.W, t=t)
+                   for t in range(w.L)]
+    read_frac = [1.0 - wb / sb for wb, sb in zip(write_bytes, step_bytes)]
+    mix_pts = ([0.0, 1 / 3, 1 / 2, 2 / 3],
+               [stream_rates[k] for k in ("writes_only", "reads1_writes2", "reads1_writes1", "reads2_writes1")])
+    mix_rate = [float(np.interp(f, *mix_pts)) for f in read_frac]
+    mix_s = sum(b_ / (r * 1e9) for b_, r in zip(step_bytes, mix_rate))
     mfma_flops = 3 * 2 * 2 * w.dk * w.dv * w.R * w.W * w.H
     mean_launch_s = float(launch_ms.mean()) * 1e-3
     achieved = mean_bytes / mean_launch_s / 1e9
@@ -472,6 +507,10 @@ def main():
             # the achievable streaming rate beside the nominal peak
             "copy_GBps": copy_gbps,
             "frac_of_copy": achieved / copy_gbps,
+            "stream_GBps": stream_rates,
+            "read_fraction": read_frac,
+            "mix_matched_GBps": mix_rate,
+            "frac_of_mix_matched": mix_s / (float(launch_ms.mean(0).sum()) * 1e-3),
             "cache": "Infinity Cache flushed (1 GiB device copy) before every event-timed launch",
             "traffic": measured_traffic(),
             "bytes_per_launch": mean_bytes,

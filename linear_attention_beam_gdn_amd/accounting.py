@@ -70,6 +70,14 @@ def beam_step_bytes(*, R, H, dk, dv, W_t, t, channel_decay=False, unique_records
     return R * H * 4 * dk * dv + R * W_t * per_beam + chain * (H * rec_v + Hk * rec_k) + ancestry
 
 
+def beam_step_write_bytes(*, R, H, dk, dv, W_t, t, channel_decay=False, Hk=None):
+    """The written part of ``beam_step_bytes``: outputs, appended records and
+    the step's ancestry rows (the rest of a step's bytes are reads)."""
+    Hk = H if Hk is None else Hk
+    A = dk if channel_decay else 1
+    return R * W_t * (H * (output_bytes(dv) + 4 * A + 4 * dv) + Hk * 2 * dk) + 4 * R * W_t * t
+
+
 def beam_step_flops(*, R, H, dk, dv, W_t, t):
     """FLOPs of one step: 2 x (2 d_k d_v) for S0^T [q|k], 4 (d_k + d_v) per
     ancestor (two dot products, two axpys), and the current transition."""

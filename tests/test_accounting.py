@@ -75,3 +75,20 @@ def test_bounded_log_run_bytes():
     assert separate == 22_925_541_376
     assert fused == 20_778_057_728
     assert separate - fused == 8 * 128 * 32 * 4 * 128 * 128  # one base read per cycle
+
+
+def test_step_write_bytes_are_the_written_part():
+    """Outputs (4 d_v), appended records (4A + 4 d_v per value head, 2 d_k per
+    key head) and the step's ancestry rows are written; taking them from the
+    total leaves the reads: S0, the inputs, the ancestral records and the
+    ancestry read."""
+    for ch, Hk in ((False, None), (True, None), (False, 8)):
+        R, H, dk, dv, W, t, uniq = 3, 16, 128, 256, 40, 2, 57
+        hk = H if Hk is None else Hk
+        Ach = dk if ch else 1
+        total = A.beam_step_bytes(R=R, H=H, dk=dk, dv=dv, W_t=W, t=t, channel_decay=ch, unique_records=uniq, Hk=Hk)
+        writes = A.beam_step_write_bytes(R=R, H=H, dk=dk, dv=dv, W_t=W, t=t, channel_decay=ch, Hk=Hk)
+        reads = (R * H * 4 * dk * dv + R * W * (H * (2 * dv + 4 * Ach + 4) + hk * 4 * dk)
+                 + uniq * (H * (4 * Ach + 4 * dv) + hk * 2 * dk) + 4 * R * W * t)
+        assert writes == R * W * (H * (4 * dv + 4 * Ach + 4 * dv) + hk * 2 * dk) + 4 * R * W * t
+        assert total - writes == reads
