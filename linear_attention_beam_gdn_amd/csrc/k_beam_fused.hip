@@ -14,7 +14,9 @@
 //   d_k = 256 the slice does not fit beside the tile ring, and the consumers
 //   load their part of it from HBM at the start instead).  Both
 //   then stream every tile's q, k, v, alpha, beta and, for each beam, the
-//   keys and decays of its T ancestral records straight from HBM into a ring
+//   decays of its T ancestral records and the keys of the first TL of them
+//   (all T unless that would leave fewer than four buffers) straight from
+//   HBM into a ring
 //   of NBUF LDS buffers with LDS-DMA loads (global_load_lds, no register
 //   round trip): tiles 0 and 1 first, the rest of the prologue after A.  They
 //   keep tiles in flight (a wave holds at most 63 memory operations, so two
@@ -28,9 +30,8 @@
 //       c_j = alpha_t prod_{i >= j} alpha_i,  c_T = alpha_t,
 //   so the consumers' replay is one FMA per record and value row.  It
 //   publishes c_0, beta_t, k_t . q_t and the 2T record weights in the tile's
-//   LDS buffer.  With d_k = 256 a tile buffer holds the keys of three record
-//   depths; the dot wave loads the keys of deeper ones from the record store
-//   itself, one depth at a time.
+//   LDS buffer.  The keys of depths TL .. T-1, which the tile buffers do
+//   not stage, it loads from the record store itself, one depth at a time.
 // * Consumer waves (one per 16 value rows of the slice, two per SIMD for
 //   128 rows).  Each holds its 16-row part of the shared state S0[r, h] in
 //   registers for the whole chunk as three bf16 planes (hi + mid + lo, each
