@@ -5,6 +5,8 @@ and merged states within 1e-4 max relative error per slice (infinity norm of
 the difference over the infinity norm of the oracle's slice).
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -79,6 +81,19 @@ def test_qwen_geometry_workloads_sampled(wname, requests, heads):
 
 def test_kda_workload_sampled():
     check_beam(configs.KDA.inputs(), True, requests=[0, 15], heads=[0, 31], label="kda")
+
+
+@pytest.mark.parametrize("wname,channel,requests,heads", [("LARGE", False, [6], [0, 29]),
+                                                           ("WIDE", False, [2], [11]),
+                                                           ("KDA", True, [9], [4])])
+def test_long_chain_workloads_sampled(wname, channel, requests, heads):
+    # full size, seven decode steps (t = 0 .. 6), as the long-chain bench rows
+    # time them: at t = 6 the d = 128 kernel stages five of the six record
+    # depths' keys and its dot wave gathers the sixth; d_k = 256 stages two
+    # at t = 3, 4 and three from t = 5; channel decay runs its ring at three
+    # buffers from t = 5
+    w = dataclasses.replace(getattr(configs, wname), L=7)
+    check_beam(w.inputs(), channel, requests=requests, heads=heads, label=f"{w.name} L = 7")
 
 
 @pytest.mark.parametrize("wname,fused", [("DELTALOG", False), ("DELTALOG", True), ("RWKV6", True)])
