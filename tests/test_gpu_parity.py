@@ -83,6 +83,18 @@ def test_kda_workload_sampled():
     check_beam(configs.KDA.inputs(), True, requests=[0, 15], heads=[0, 31], label="kda")
 
 
+@pytest.mark.parametrize("H,Hk,dv,R,W,channel", [(64, 4, 128, 4, 256, False), (64, 16, 256, 2, 128, False),
+                                                 (64, 8, 128, 2, 256, True)])
+def test_many_value_heads_sampled(H, Hk, dv, R, W, channel):
+    # the OneLA operator suite's largest head counts: 64 value heads on 4 to 16
+    # key heads (16 down to 4 value heads per key head), hot-parent lineage
+    inp = synth.make_inputs(R=R, H=H, dk=128, dv=dv, W=W, L=4, s0_std=0.05, seed=31 + Hk, parents="topk_hot",
+                            channel_decay=channel, Hk=Hk)
+    g = H // Hk
+    heads = [0, g - 1, g, H - 1]  # two value heads of key head 0, the first of key head 1, the last
+    check_beam(inp, channel, requests=[R - 1], heads=heads, label=f"H = {H} on H_k = {Hk}, d_v = {dv}")
+
+
 @pytest.mark.parametrize("wname,channel,requests,heads", [("LARGE", False, [6], [0, 29]),
                                                            ("WIDE", False, [2], [11]),
                                                            ("KDA", True, [9], [4])])
