@@ -44,10 +44,26 @@ struct FoldGeom {
   static constexpr int NSL = DK / (NRG * RPG);       // row slices
   static_assert(NSL * NRG * RPG == DK, "d_k must split evenly over row slices");
   static constexpr int NT = C4 * NRG;
+  // 16-byte pieces of a record row staged in LDS (bf16 key, FP32 update
+  // vector, FP32 per-channel decays) and the pieces a thread loads at most
+  static_assert(DK % 8 == 0 && DV % 4 == 0, "record rows must be whole 16-byte pieces");
+  static constexpr int KCH = DK / 8, DCH = DV / 4, ACH = DK / 4;
+  static constexpr int NKL = (GDN_MAX_STEPS * KCH + NT - 1) / NT;
+  static constexpr int NDL = (GDN_MAX_STEPS * DCH + NT - 1) / NT;
+  static constexpr int NAL = (GDN_MAX_STEPS * ACH + NT - 1) / NT;
 };
 
+// Dynamic LDS of a chain of n records (floats): keys [n][d_k], update vectors
+// [n][d_v], decays [n][A] padded to a multiple of four.
+__host__ __device__ constexpr int fold_lds_floats(int dk, int dv, int a, int n) {
+  return n * dk + n * dv + ((n * a + 3) & ~3);
+}
+
+// Built for four waves per SIMD (at most 128 registers) where that needs no
+// spills: d_v up to 256, and d_v = 128 with per-channel decay.
 template <int DK, int DV, bool CH>
-__global__ __launch_bounds__((FoldGeom<DK, DV>::NT)) void k_fold(FoldArgs a) {
+__global__ __launch_bounds__((FoldGeom<DK, DV>::NT), ((DV <= 256 && !(CH && DV > 128)) ? 4 : 1))
+void k_fold(FoldArgs a) {
   using G = FoldGeom<DK, DV>;
   constexpr int A = CH ? DK : 1;
   const int tid = threadIdx.x;
@@ -65,30 +81,91 @@ __global__ __launch_bounds__((FoldGeom<DK, DV>::NT)) void k_fold(FoldArgs a) {
   r = clampi(r, 0, a.R - 1);
   b = clampi(b, 0, a.Wm - 1);
   const int t = a.t;
+  const int n = t + 1;  // records in the chain: the ancestors' and the beam's own
 
   const float* src = a.src + ((size_t)r * a.H + h) * DK * DV;
   float* dst = a.dst_per_item ? a.dst + ((size_t)item * a.H + h) * DK * DV
                               : a.dst + ((size_t)r * a.H + h) * DK * DV;
+
+  // The chain's records in one batch of 16-byte loads (each piece looks up
+  // its record's slot in the beam's ancestry row), issued before the state's
+  // rows and put in LDS while those are in flight, so the fold below reads
+  // LDS only.
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
+  float* lk = dyn;              // [n][DK] keys
+  float* ld = lk + n * DK;      // [n][DV] update vectors
+  float* la = ld + n * DV;      // [n][A] decays
+  const int32_t* arow = a.anc + (((size_t)t * a.R + r) * a.Wm + b) * a.L;
+  auto rec_at = [&](int j) -> size_t {
+    const int slot = j < t ? clampi(arow[j], 0, a.Wm - 1) : b;
+    return (((size_t)j * a.R + r) * a.Wm + slot) * a.H + h;
+  };
+  auto rec_at_k = [&](int j) -> size_t {
+    const int slot = j < t ? clampi(arow[j], 0, a.Wm - 1) : b;
+    return (((size_t)j * a.R + r) * a.Wm + slot) * a.Hk + h / a.gq;
+  };
+  const int nk = n * G::KCH, nd = n * G::DCH;
+  u32x4 kb[G::NKL];
+  f32x4 db[G::NDL], ab[CH ? G::NAL : 1];
+  float as = 0.f;
+#pragma unroll
+  for (int m = 0; m < G::NKL; ++m) {
+    const int c = min(tid + m * G::NT, nk - 1);
+    kb[m] = *reinterpret_cast<const u32x4*>(a.rec_k + rec_at_k(c / G::KCH) * DK + (c % G::KCH) * 8);
+  }
+#pragma unroll
+  for (int m = 0; m < G::NDL; ++m) {
+    const int c = min(tid + m * G::NT, nd - 1);
+    db[m] = *reinterpret_cast<const f32x4*>(a.rec_delta + rec_at(c / G::DCH) * DV + (c % G::DCH) * 4);
+  }
+  if constexpr (CH) {
+#pragma unroll
+    for (int m = 0; m < G::NAL; ++m) {
+      const int c = min(tid + m * G::NT, n * G::ACH - 1);
+      ab[m] = *reinterpret_cast<const f32x4*>(a.rec_alpha + rec_at(c / G::ACH) * A + (c % G::ACH) * 4);
+    }
+  } else {
+    if (tid < n) as = a.rec_alpha[rec_at(tid)];
+  }
+
   f32x4 st[G::RPG];
 #pragma unroll
   for (int i = 0; i < G::RPG; ++i)
     st[i] = *reinterpret_cast<const f32x4*>(src + (size_t)(row0 + i) * DV + c4 * 4);
 
-  const int32_t* arow = a.anc + (((size_t)t * a.R + r) * a.Wm + b) * a.L;
-  // (a do-while: t >= 0, and this loop shape keeps the state in one set of
+#pragma unroll
+  for (int m = 0; m < G::NKL; ++m) {
+    const int c = tid + m * G::NT;
+    if (c < nk) {
+      const u32x4 w = kb[m];
+      *reinterpret_cast<f32x4*>(lk + c * 8) = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+      *reinterpret_cast<f32x4*>(lk + c * 8 + 4) = f32x4{bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3])};
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < G::NDL; ++m)
+    if (tid + m * G::NT < nd) *reinterpret_cast<f32x4*>(ld + (tid + m * G::NT) * 4) = db[m];
+  if constexpr (CH) {
+#pragma unroll
+    for (int m = 0; m < G::NAL; ++m)
+      if (tid + m * G::NT < n * G::ACH) *reinterpret_cast<f32x4*>(la + (tid + m * G::NT) * 4) = ab[m];
+  } else {
+    if (tid < n) la[tid] = as;
+  }
+  __syncthreads();
+
+  // the records in chain order (a do-while: every chain has at least the
+  // beam's own record, and this loop shape keeps the state in one set of
   // registers across the loop instead of a copy per entry)
   int j = 0;
   do {
-    const int slot = j < t ? clampi(arow[j], 0, a.Wm - 1) : b;
-    const size_t rj = (((size_t)j * a.R + r) * a.Wm + slot) * a.H + h;
-    const size_t rjk = (((size_t)j * a.R + r) * a.Wm + slot) * a.Hk + h / a.gq;
-    const f32x4 dj = *reinterpret_cast<const f32x4*>(a.rec_delta + rj * DV + c4 * 4);
-    const float aj0 = CH ? 0.f : a.rec_alpha[rj];
+    const f32x4 dj = *reinterpret_cast<const f32x4*>(ld + j * DV + c4 * 4);
+    const float aj0 = CH ? 0.f : la[j];
 #pragma unroll
     for (int i = 0; i < G::RPG; ++i) {
       const int row = row0 + i;
-      const float kj = bf16_at(a.rec_k[rjk * DK + row]);
-      const float aj = CH ? a.rec_alpha[rj * A + row] : aj0;
+      const float kj = lk[j * DK + row];
+      const float aj = CH ? la[j * A + row] : aj0;
       st[i] = apply_record(st[i], aj, kj, dj);
     }
   } while (++j <= t);
@@ -119,7 +196,8 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, const int32_t* rb, i
   a.dst_per_item = dst_per_item ? 1 : 0;
   const long grid = (long)n * sh.H * FoldGeom<DK, DV>::NSL;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
-  hipLaunchKernelGGL((k_fold<DK, DV, CH>), dim3((unsigned)grid), dim3(FoldGeom<DK, DV>::NT), 0,
+  const size_t lds = (size_t)fold_lds_floats(DK, DV, CH ? DK : 1, t + 1) * sizeof(float);
+  hipLaunchKernelGGL((k_fold<DK, DV, CH>), dim3((unsigned)grid), dim3(FoldGeom<DK, DV>::NT), lds,
                      stream, a);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
 }
