@@ -357,7 +357,7 @@ def test_decode_merge_step(kind):
 def test_sequences_full_log_capacity(dk, kind):
     """Logs of the largest capacity (16 records): every log length 0 .. 15,
     so the sequence kernel stages up to 17 key rows, 15 update vectors and 16
-    decay rows (at d = 128 the second round of staged loads; at d = 16 the
+    decay rows (at d = 128 a second staged load per thread; at d = 16 the
     64 threads are exactly filled).  Decode-then-merge and the fused merge
     path agree bit for bit, and both match the oracle, over two full cycles."""
     channel, plain = kind != "scalar", kind == "plain"
