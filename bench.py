@@ -129,6 +129,19 @@ def _bw(nbytes, us):
     return {"bytes": float(nbytes), "us": us, "achieved_GBps": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
 
 
+# streaming rates of this GPU at several read:write mixes (set by main())
+_STREAM_RATES = {}
+
+
+def mix_rate(read_frac):
+    """Streaming rate (GB/s) of a read fraction, piecewise linear between the
+    measured mixes (writes only, 1:2, 1:1, 2:1), or None before they exist."""
+    if not _STREAM_RATES:
+        return None
+    keys = ("writes_only", "reads1_writes2", "reads1_writes1", "reads2_writes1")
+    return float(np.interp(read_frac, [0.0, 1 / 3, 1 / 2, 2 / 3], [_STREAM_RATES[k] for k in keys]))
+
+
 def beam_row(B, torch, dev, stream, wl, reps):
     """The L decode steps of a beam workload: per-launch durations and
     bandwidth under the unique-record byte model."""
@@ -157,9 +170,17 @@ def beam_row(B, torch, dev, stream, wl, reps):
         nbytes = accounting.beam_step_bytes(R=wl.R, H=wl.H, dk=wl.dk, dv=wl.dv, W_t=wl.W, t=t,
                                             channel_decay=wl.channel_decay, unique_records=uniq, Hk=wl.Hk)
         per.append(_bw(nbytes, us[t]))
+        wb = accounting.beam_step_write_bytes(R=wl.R, H=wl.H, dk=wl.dk, dv=wl.dv, W_t=wl.W, t=t,
+                                              channel_decay=wl.channel_decay, Hk=wl.Hk)
+        per[-1]["read_fraction"] = 1.0 - wb / nbytes
     tot_b, tot_us = sum(p["bytes"] for p in per), sum(us)
-    return {"workload": wl.name, "decode_steps": wl.L, "beam_steps_per_s": wl.R * wl.W * wl.L / (tot_us * 1e-6),
-            "launch_us": us, **{k: v for k, v in _bw(tot_b / wl.L, tot_us / wl.L).items() if k != "us"}}
+    out = {"workload": wl.name, "decode_steps": wl.L, "beam_steps_per_s": wl.R * wl.W * wl.L / (tot_us * 1e-6),
+           "launch_us": us, **{k: v for k, v in _bw(tot_b / wl.L, tot_us / wl.L).items() if k != "us"}}
+    if _STREAM_RATES:
+        out["read_fraction"] = [p["read_fraction"] for p in per]
+        out["frac_of_mix_matched"] = (sum(p["bytes"] / (mix_rate(p["read_fraction"]) * 1e9) for p in per)
+                                      / (tot_us * 1e-6))
+    return out
 
 
 # OneLA's printed operator latencies at its Qwen geometry (unnamed GPU; context only):
@@ -473,10 +494,9 @@ def main():
     write_bytes = [accounting.beam_step_write_bytes(R=w.R, H=w.H, dk=w.dk, dv=w.dv, W_t=w.W, t=t)
                    for t in range(w.L)]
     read_frac = [1.0 - wb / sb for wb, sb in zip(write_bytes, step_bytes)]
-    mix_pts = ([0.0, 1 / 3, 1 / 2, 2 / 3],
-               [stream_rates[k] for k in ("writes_only", "reads1_writes2", "reads1_writes1", "reads2_writes1")])
-    mix_rate = [float(np.interp(f, *mix_pts)) for f in read_frac]
-    mix_s = sum(b_ / (r * 1e9) for b_, r in zip(step_bytes, mix_rate))
+    _STREAM_RATES.update(stream_rates)
+    mix_rates = [mix_rate(f) for f in read_frac]
+    mix_s = sum(b_ / (r * 1e9) for b_, r in zip(step_bytes, mix_rates))
     mfma_flops = 3 * 2 * 2 * w.dk * w.dv * w.R * w.W * w.H
     mean_launch_s = float(launch_ms.mean()) * 1e-3
     achieved = mean_bytes / mean_launch_s / 1e9
@@ -509,7 +529,7 @@ def main():
             "frac_of_copy": achieved / copy_gbps,
             "stream_GBps": stream_rates,
             "read_fraction": read_frac,
-            "mix_matched_GBps": mix_rate,
+            "mix_matched_GBps": mix_rates,
             "frac_of_mix_matched": mix_s / (float(launch_ms.mean(0).sum()) * 1e-3),
             "cache": "Infinity Cache flushed (1 GiB device copy) before every event-timed launch",
             "traffic": measured_traffic(),
