@@ -13,15 +13,18 @@
 //
 // Work split.  A workgroup takes one (request r, head h), a slice of at most
 // 128 value rows (d_v = 256 and 512 take two and four slices, each preparing
-// the probes and weights itself) and a chunk of its beams, 8 beams per tile.  The 16 columns of the gfx950 16x16x32 bf16 MFMA
+// the probes and weights itself; with chains of at most three records the
+// slices hold 256 rows, two 16-row blocks per consumer wave) and a chunk of its
+// beams, 8 beams per tile.  The 16 columns of the gfx950 16x16x32 bf16 MFMA
 // carry the q-probes (columns 0-7) and the k-probes (columns 8-15) of the
 // same 8 beams, so one MFMA forms both projections.
 // * Two DMA waves (alternate tiles) build the ancestry-ordered schedule and
 //   stream each tile's q|k rows, v, alpha_t, beta_t and, per beam, the keys
 //   and decay vectors of its T ancestral records into a ring of LDS buffers
 //   with LDS-DMA loads and counted waits.
-// * The consumer waves (one per 16 value rows of the slice) each hold 16
-//   value rows of S0[r, h] as two bf16 planes in registers.  Between two barriers a consumer wave
+// * The consumer waves (one per 16 value rows of the slice, or per 32 in
+//   the 256-row slices) each hold their value rows of S0[r, h] as two
+//   bf16 planes in registers.  Between two barriers a consumer wave
 //   - prepares its share of the next tile (8 / (d_v / 16) beams): each half
 //     wave takes the q or the k row of a beam, walks the chain from the
 //     current step down (y = a_t * x; weight_j = k_j . y; y = a_j * y), and
@@ -53,10 +56,20 @@ template <int DK, int DV, int T>
 struct KdaGeom {
   static_assert(DK % 64 == 0 && DV % 64 == 0, "the channel-decay kernel needs d_k, d_v multiples of 64");
   static constexpr int TB = 8;             // beams per tile
-  static constexpr int VS = DV < 128 ? DV : 128;  // value rows per workgroup
+  // 16-row blocks of S0 a consumer wave holds: two for d_v of 256 and more
+  // with chains of at most three records, so that a slice has 256 value rows
+  // (half the slices, each preparing the probes and weights itself) with
+  // eight consumer waves; one for longer chains, whose update vectors would
+  // not fit the registers beside two blocks of S0 planes
+  static constexpr int NRB = (DV >= 256 && T <= 3) ? 2 : 1;
+  // the next tile's update vectors loaded in one batch at the top of a tile
+  // (two sets held) where the registers allow it, else block by block right
+  // after use (one set)
+  static constexpr bool DBUF = NRB == 1 || T <= 1;
+  static constexpr int VS = DV < 128 ? DV : 128 * NRB;  // value rows per workgroup
   static_assert(DV % VS == 0, "d_v must split evenly over value slices");
   static constexpr int NVS = DV / VS;      // value slices
-  static constexpr int NC = VS / 16;       // consumer waves, 16 value rows each
+  static constexpr int NC = VS / (16 * NRB);  // consumer waves, 16 NRB value rows each
   static_assert(TB % NC == 0, "each consumer wave prepares whole beams");
   static constexpr int BPW = TB / NC;      // beams a consumer wave prepares per tile
   static constexpr int EPL = DK / 32;      // channels per lane in the preparation
@@ -381,30 +394,38 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   };
 
   // Part of S0[r, h] as hi + lo bf16 planes in the MFMA A layout: lane
-  // (g, c) holds key channels 32s + 8g .. +7 of value row vs0 + 16w + c, so
-  // C row 4g + i is value row vs0 + 16w + 4g + i.
+  // (g, c) holds, in row block rb, key channels 32s + 8g .. +7 of value row
+  // vs0 + 16 (NRB w + rb) + c, so C row 4g + i of that block is value row
+  // vs0 + 16 (NRB w + rb) + 4g + i.
   const int g = lane >> 4;
   const int c = lane & 15;
   const int bb = c & 7;     // beam of this lane within the tile
   const int side = c >> 3;  // 0: q column, 1: k column
   // A DMA wave stages S0 in LDS, or (chains of six records) each lane loads
   // its entries from HBM here; the planes are formed between barriers S and A.
-  float s0x[G::S0_LDS ? 1 : KS][8];
+  constexpr int NRB = G::NRB;
+  float s0x[G::S0_LDS ? 1 : NRB][G::S0_LDS ? 1 : KS][8];
   if constexpr (!G::S0_LDS) {
-    const float* Sg = a.S + ((size_t)r * a.H + h) * DK * DV + vs0 + w * 16 + c;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float* Sg = a.S + ((size_t)r * a.H + h) * DK * DV + vs0 + (w * NRB + rb) * 16 + c;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s0x[s][e] = Sg[(size_t)(s * 32 + g * 8 + e) * DV];
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s0x[rb][s][e] = Sg[(size_t)(s * 32 + g * 8 + e) * DV];
+    }
   }
   if (T > 0) lds_barrier();  // Q
-  const int row0 = vs0 + w * 16 + 4 * g;
+  // this lane's first value row in row block rb: row0 + 16 rb
+  const int row0 = vs0 + w * NRB * 16 + 4 * g;
   const int so = a.H * DV * 4;
   const size_t tok0 = ((size_t)r * a.Wt + b_begin) * a.H + h;
   const __amdgpu_buffer_rsrc_t w_o = store_window(a.o + tok0 * DV, (nb - 1) * so + DV * 4);
   const __amdgpu_buffer_rsrc_t w_d = store_window(a.rec_delta + rec0 * DV, (nb - 1) * so + DV * 4);
 
-  auto load_deltas = [&](int p, f32x4* d) {
+  // ancestral update vectors of tile p, this lane's 4 rows of beam bb in row
+  // blocks rb0 .. rb1 - 1
+  auto load_deltas = [&](int p, f32x4 (*d)[NRB], int rb0 = 0, int rb1 = G::NRB) {
     if constexpr (T > 0) {
       const int posi = min(p * G::TB + bb, nb - 1);
       const u32x4 e = s_tab[posi];
@@ -414,42 +435,58 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
 #pragma unroll
       for (int j = 0; j < T; ++j) {
         const size_t rj = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + h;
-        d[j] = *reinterpret_cast<const f32x4*>(a.rec_delta + rj * DV + row0);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          if (rb >= rb0 && rb < rb1)
+            d[j][rb] = *reinterpret_cast<const f32x4*>(a.rec_delta + rj * DV + row0 + 16 * rb);
       }
     }
   };
 
   lds_barrier();  // P
-  f32x4 dnext[TT];
+  f32x4 dnext[TT][NRB];
   load_deltas(0, dnext);
   lds_barrier();  // S: S0 staged
-  u32x4 As[KS][2];
+  u32x4 As[NRB][KS][2];
   if constexpr (G::S0_LDS) {
     const float* S = reinterpret_cast<const float*>(smem + G::OS0);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      float x[8];
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = S[(s * 32 + g * 8 + e) * G::VS + w * 16 + c];
-      split_planes<2>(x, As[s]);
-    }
+      for (int s = 0; s < KS; ++s) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = S[(s * 32 + g * 8 + e) * G::VS + (w * NRB + rb) * 16 + c];
+        split_planes<2>(x, As[rb][s]);
+      }
   } else {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) split_planes<2>(s0x[s], As[s]);
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) split_planes<2>(s0x[rb][s], As[rb][s]);
   }
   lds_barrier();  // A: tile 0 resident
   prep(0);
   lds_barrier();  // 0
 
   for (int it = 0; it < ntiles; ++it) {
-    f32x4 dcur[TT];
+    // Double-buffered: this tile's update vectors move to dcur and the next
+    // tile's are loaded at once.  Otherwise each row block's next update
+    // vectors are loaded into dnext right after the block has used them
+    // (below), which holds one set instead of two.
+    constexpr bool DBUF = G::DBUF;
+    f32x4 dcur[DBUF ? TT : 1][DBUF ? NRB : 1];
+    if constexpr (DBUF) {
 #pragma unroll
-    for (int j = 0; j < T; ++j) dcur[j] = dnext[j];
+      for (int j = 0; j < T; ++j)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) dcur[j][rb] = dnext[j][rb];
+      load_deltas(it + 1, dnext);
+    }
     // Next tile, unconditionally so that it shares a basic block with this
     // tile's work.  Past the last tile it reads a free buffer (no load of
     // this launch targets it any more), writes only there, and its appends
     // fall outside the store windows.
-    load_deltas(it + 1, dnext);
     prep(it + 1);
 
     const uint8_t* buf = smem + (it % G::NBUF) * G::BUF;
@@ -459,8 +496,6 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       bh[s] = *reinterpret_cast<const u32x4*>(buf + G::OQK + slot16(c, s * 4 + g) * 16);
       bl[s] = *reinterpret_cast<const u32x4*>(buf + G::OLO + slot16(c, s * 4 + g) * 16);
     }
-    const int vch = w * 2 + (g >> 1);  // 16-byte v chunk holding rows row0 .. row0 + 3
-    const u32x2 vw = *reinterpret_cast<const u32x2*>(buf + G::OV + slot8(bb, vch) * 16 + (g & 1) * 8);
     float wt[G::NWT];
 #pragma unroll
     for (int v = 0; v < G::NWT; v += 4) {
@@ -468,44 +503,53 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
 #pragma unroll
       for (int e = 0; e < 4; ++e) wt[v + e] = q4[e];
     }
-
-    // S0^T [Q_0 q | Q_0 k] for the tile's 8 beams: hi*hi + hi*lo + lo*hi
-    f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u = mfma16x16x32(As[s][1], bh[s], u);
-      u = mfma16x16x32(As[s][0], bl[s], u);
-      u = mfma16x16x32(As[s][0], bh[s], u);
-    }
-    f32x4 uq, uk;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float other = swap8(u[i]);
-      uq[i] = side ? other : u[i];
-      uk[i] = side ? u[i] : other;
-    }
-    f32x4 xq = uq, xk = uk;
-#pragma unroll
-    for (int j = 0; j < T; ++j) {
-      xq += wt[2 + j] * dcur[j];
-      xk += wt[2 + T + j] * dcur[j];
-    }
-    f32x4 dt, ot;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t word = vw[i >> 1];
-      const float vv = (i & 1) ? bf16_hi(word) : bf16_lo(word);
-      dt[i] = wt[0] * (vv - xk[i]);
-      ot[i] = xq[i] + dt[i] * wt[1];
-    }
-
-    // output (q-column lanes) and the appended update vector (k-column lanes)
     const int posi = it * G::TB + bb;
     const bool live = posi < nb;
     const int ib = T > 0 ? (int)s_tab[min(posi, nb - 1)][0] : posi;
-    const int off = live ? ib * so + row0 * 4 : kOutside;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, side ? kOutside : off, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, side ? off : kOutside, 0, 0);
+
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      // 16-byte v chunk holding this lane's rows row0 + 16 rb .. + 3
+      const int vch = (w * NRB + rb) * 2 + (g >> 1);
+      const u32x2 vw = *reinterpret_cast<const u32x2*>(buf + G::OV + slot8(bb, vch) * 16 + (g & 1) * 8);
+
+      // S0^T [Q_0 q | Q_0 k] for the tile's 8 beams: hi*hi + hi*lo + lo*hi
+      f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        u = mfma16x16x32(As[rb][s][1], bh[s], u);
+        u = mfma16x16x32(As[rb][s][0], bl[s], u);
+        u = mfma16x16x32(As[rb][s][0], bh[s], u);
+      }
+      f32x4 uq, uk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float other = swap8(u[i]);
+        uq[i] = side ? other : u[i];
+        uk[i] = side ? u[i] : other;
+      }
+      f32x4 xq = uq, xk = uk;
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const f32x4 dj = DBUF ? dcur[DBUF ? j : 0][DBUF ? rb : 0] : dnext[j][rb];
+        xq += wt[2 + j] * dj;
+        xk += wt[2 + T + j] * dj;
+      }
+      f32x4 dt, ot;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t word = vw[i >> 1];
+        const float vv = (i & 1) ? bf16_hi(word) : bf16_lo(word);
+        dt[i] = wt[0] * (vv - xk[i]);
+        ot[i] = xq[i] + dt[i] * wt[1];
+      }
+
+      // output (q-column lanes) and the appended update vector (k-column lanes)
+      const int off = live ? ib * so + (row0 + 16 * rb) * 4 : kOutside;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, side ? kOutside : off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, side ? off : kOutside, 0, 0);
+      if constexpr (!DBUF) load_deltas(it + 1, dnext, rb, rb + 1);
+    }
     lds_barrier();  // it + 1
   }
 }
