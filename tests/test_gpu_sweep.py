@@ -61,6 +61,43 @@ def test_random_geometry_one_chunk(case, monkeypatch):
     _check_geometry(case)
 
 
+def _wide_chain_cases(n=48, seed=77):
+    """Cases weighted to the fused kernels' shape-dependent paths: channel
+    decay at d_v 256 / 512 (256-row value slices up to three records, 128-row
+    beyond), d_k 256 and d = 128 scalar chains up to six records (how many
+    record depths' keys the tile buffers stage), ragged widths, and one or
+    several beam chunks per (request, head)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = rng.integers(3)
+        if kind == 0:
+            channel, (dk, dv) = True, [(128, 256), (128, 512)][rng.integers(2)]
+        elif kind == 1:
+            channel, (dk, dv) = False, [(256, 128), (256, 256), (256, 512)][rng.integers(3)]
+        else:
+            channel, (dk, dv) = False, [(128, 128), (64, 64), (128, 512)][rng.integers(3)]
+        H = int(rng.choice([1, 2, 3]))
+        Hk = int(rng.choice([d for d in range(1, H + 1) if H % d == 0]))
+        L = int(rng.integers(2, 8))
+        W_max = int(rng.choice([5, 17, 40, 70, 130, 300]))
+        widths = [int(rng.integers(max(1, W_max // 2), W_max + 1)) for _ in range(L)]
+        out.append(dict(id=1000 + i, channel=channel, dk=dk, dv=dv, H=H, Hk=Hk, R=int(rng.integers(1, 3)), L=L,
+                        W_max=W_max, widths=widths, parents=str(rng.choice(["topk", "uniform"])), seed=5000 + i,
+                        one_chunk=bool(rng.random() < 0.5)))
+    return out
+
+
+WIDE_CHAIN_CASES = _wide_chain_cases()
+
+
+@pytest.mark.parametrize("case", WIDE_CHAIN_CASES, ids=[f"w{c['id']}" for c in WIDE_CHAIN_CASES])
+def test_random_wide_and_long_chains(case, monkeypatch):
+    if case["one_chunk"]:
+        monkeypatch.setenv("GDN_BEAM_CHUNK", "512")
+    _check_geometry(case)
+
+
 def _check_geometry(case):
     c = case
     label = (f"case {c['id']}: dk={c['dk']} dv={c['dv']} ch={c['channel']} R={c['R']} H={c['H']} Hk={c['Hk']} "
