@@ -36,6 +36,12 @@
  *     error nothing is enqueued and a negative status is returned.
  *   - No global mutable state: calls on different stores or streams are
  *     independent.  Calls that write the same store must be stream-ordered.
+ *   - Two environment variables, read at every beam-decode call, exist for
+ *     tests and comparisons only: GDN_BEAM_CHUNK=n (a multiple of 16, at
+ *     least 16) fixes the number of beams per workgroup, which only changes
+ *     which lanes compute a beam, never a result; GDN_BEAM_GENERIC=1 makes
+ *     gdn_beam_decode_step use its general kernel for every shape, whose
+ *     results differ from the fused kernels' by FP32 rounding only.
  */
 #ifndef GDN_BEAM_H
 #define GDN_BEAM_H
