@@ -216,16 +216,14 @@ inline bool windows_fit(const gdn_shape& sh) {
   return (long long)kMaxChunkF * stride + stride < (1LL << 31);
 }
 
-inline int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
+// Compute units of the device a stream runs on, asked of the runtime at every
+// launch (no cache, so concurrent first calls share no state).
+inline int cu_count(hipStream_t stream) {
+  hipDevice_t dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) return 256;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
 }
 
 }  // namespace fused

@@ -30,8 +30,9 @@ inline int key_heads(const gdn_shape& sh) { return sh.H_k > 0 ? sh.H_k : sh.H; }
 int launch_beam_decode(const gdn_shape& sh, const gdn_store& st, int t, int Wt,
                        const StepIO& io, hipStream_t stream);
 
-// Scalar-decay beams with (d_k, d_v) in {32, 64, 128} and chains of at most
-// kFusedMaxSteps records: loader/consumer pipeline through LDS.
+// Scalar-decay beams with (d_k, d_v) = (32, 32) or (64, 64), or d_k in
+// {128, 256} x d_v in {128, 256, 512}, and chains of at most kFusedMaxSteps
+// records: loader/consumer pipeline through LDS.
 constexpr int kFusedMaxSteps = 6;
 bool beam_fused_supported(const gdn_shape& sh, int t);
 int launch_beam_fused(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,

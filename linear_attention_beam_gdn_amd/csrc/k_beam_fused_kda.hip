@@ -579,7 +579,7 @@ int launch(const gdn_shape& sh, const gdn_store& st, int Wt, const StepIO& io, h
   a.Hk = key_heads(sh);
   a.gq = sh.H / a.Hk;
   // one workgroup per compute unit: the tile ring takes most of its LDS
-  a.chunk = pick_chunk(sh.R * sh.H * G::NVS, Wt, kMaxChunkF, cu_count());
+  a.chunk = pick_chunk(sh.R * sh.H * G::NVS, Wt, kMaxChunkF, cu_count(stream));
   a.nchunk = (Wt + a.chunk - 1) / a.chunk;
   const long grid = (long)sh.R * sh.H * G::NVS * a.nchunk;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
