@@ -1,8 +1,11 @@
 """Compile libgdnbeam.so for gfx950 in-tree with hipcc.
 
 Every kernel source is compiled to an object in ``_build/`` (in parallel),
-then linked into ``linear_attention_beam_gdn_amd/libgdnbeam.so``.  All HIP code
-is built with packed-FP32 instructions disabled.
+then linked into ``linear_attention_beam_gdn_amd/libgdnbeam.so``.  Two
+measurement libraries are built beside it: ``libgdnbeam_stamps.so``, the same
+library with the headline kernel's clock stamps compiled in (GDN_STAMPS), and
+``measure/libgdnmeasure.so``, the streaming-rate reference kernels.  All HIP
+code is built with packed-FP32 instructions disabled.
 """
 
 from __future__ import annotations
@@ -20,6 +23,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdnbeam.so")
+STAMPS_LIB = os.path.join(PKG, "libgdnbeam_stamps.so")
+MEASURE_SRC = os.path.join(PKG, "measure", "k_stream.hip")
+MEASURE_LIB = os.path.join(PKG, "measure", "libgdnmeasure.so")
+STAMPED = "k_beam_fused.hip"  # the source built a second time with GDN_STAMPS
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -37,8 +44,8 @@ def hipcc() -> str:
     return exe
 
 
-def _compile(src: str, extra=()) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
+def _compile(src: str, extra=(), suffix="") -> str:
+    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", suffix + ".o"))
     cmd = [hipcc(), *HIP_FLAGS, *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -46,19 +53,30 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    stamped = os.path.join(CSRC, STAMPED)
+    jobs = [(s, tuple(extra), "") for s in srcs]
+    jobs.append((stamped, tuple(extra) + ("-DGDN_STAMPS",), "_stamps"))
+    jobs.append((MEASURE_SRC, tuple(extra), ""))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    prod = objs[:len(srcs)]
+    _link(prod, LIB)
+    _link([o for o, s in zip(prod, srcs) if s != stamped] + [objs[len(srcs)]], STAMPS_LIB)
+    _link([objs[-1]], MEASURE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} (and {os.path.basename(STAMPS_LIB)}, measure/{os.path.basename(MEASURE_LIB)})")
     return LIB
 
 

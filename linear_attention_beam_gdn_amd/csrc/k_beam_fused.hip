@@ -62,6 +62,40 @@
 // 1 KiB access, free of bank conflicts.
 #include "fused_common.h"
 
+// Clock stamps (measurement builds only, compiled with GDN_STAMPS): lane 0 of
+// consumer wave 0 of every workgroup records the real-time clock at kernel
+// entry, after each prologue barrier and after its last tile, and the XCD
+// and compute unit it ran on, into a per-workgroup row of a device array
+// that gdn_stamps_read copies out.  The product build records nothing.
+#ifdef GDN_STAMPS
+namespace gdn {
+namespace {
+constexpr int kStampWgs = 4096, kStamps = 8;
+__device__ unsigned long long g_stamps[kStampWgs * kStamps];
+}  // namespace
+}  // namespace gdn
+#define GDN_STAMP(i)                                                                  \
+  do {                                                                                \
+    if (w == 0 && lane == 0 && blockIdx.x < kStampWgs)                                \
+      g_stamps[blockIdx.x * kStamps + (i)] = __builtin_amdgcn_s_memrealtime();        \
+  } while (0)
+#define GDN_STAMP_WHERE()                                                             \
+  do {                                                                                \
+    if (w == 0 && lane == 0 && blockIdx.x < kStampWgs) {                              \
+      const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xF;           \
+      const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);                  \
+      g_stamps[blockIdx.x * kStamps + 7] = ((unsigned long long)xcc << 32) | hw;      \
+    }                                                                                 \
+  } while (0)
+#else
+#define GDN_STAMP(i) \
+  do {               \
+  } while (0)
+#define GDN_STAMP_WHERE() \
+  do {                    \
+  } while (0)
+#endif
+
 namespace gdn {
 namespace {
 
@@ -378,6 +412,8 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   // A DMA wave stages the slice in LDS (d_k <= 128), or each lane loads its
   // entries from HBM here, overlapping the schedule build (d_k = 256); the
   // planes are formed between barriers S and A.
+  GDN_STAMP(0);
+  GDN_STAMP_WHERE();
   float s0x[G::S0_LDS ? 1 : KS][8];
   if constexpr (!G::S0_LDS) {
     const float* Sg = a.S + ((size_t)r * a.H + h) * DK * DV + vs0 + w * 16 + c;
@@ -387,6 +423,7 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
       for (int e = 0; e < 8; ++e) s0x[s][e] = Sg[(size_t)(s * 32 + g * 8 + e) * DV];
   }
   if (T > 0) lds_barrier();  // Q
+  GDN_STAMP(1);
   const int row0 = vs0 + w * 16 + 4 * g;  // first of this lane's 4 value rows
 
   // Store windows over the chunk's beams [b_begin, b_end): a lane whose beam
@@ -422,9 +459,11 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   };
 
   lds_barrier();  // P: schedule table written
+  GDN_STAMP(2);
   f32x4 dnext[TT];
   load_deltas(0, dnext);  // in flight while tile 0 arrives
   lds_barrier();  // S: S0 staged
+  GDN_STAMP(3);
   u32x4 As[KS][NPL];
   if constexpr (G::S0_LDS) {
     const float* S = reinterpret_cast<const float*>(smem + G::OS0);
@@ -440,7 +479,9 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     for (int s = 0; s < KS; ++s) split_planes<NPL>(s0x[s], As[s]);
   }
   lds_barrier();  // A: tile 0 resident
+  GDN_STAMP(4);
   lds_barrier();  // 0
+  GDN_STAMP(5);
 
   for (int it = 0; it < ntiles; ++it) {
     f32x4 dcur[TT];
@@ -533,6 +574,7 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
                                           (live && slice0 && w == G::NC - 1 && g == 0) ? ib * sa : kOutside, 0, 0);
     lds_barrier();  // it + 1
   }
+  GDN_STAMP(6);
 }
 
 template <int DK, int DV, int T>
@@ -621,3 +663,23 @@ int launch_beam_fused(const gdn_shape& sh, const gdn_store& st, int t, int Wt, c
 }
 
 }  // namespace gdn
+
+#ifdef GDN_STAMPS
+// Measurement builds only: copy the first n_wg rows of clock stamps (8 per
+// workgroup: entry, barriers Q, P, S, A, 0, after the last tile, and
+// (XCD << 32 | hardware id)) to host memory, and report the real-time
+// clock's rate.
+extern "C" int gdn_stamps_read(unsigned long long* host, int n_wg) {
+  if (host == nullptr || n_wg < 0 || n_wg > gdn::kStampWgs) return GDN_EINVAL;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(gdn::g_stamps), (size_t)n_wg * gdn::kStamps * 8, 0,
+                             hipMemcpyDeviceToHost) == hipSuccess
+             ? GDN_OK
+             : GDN_EHIP;
+}
+extern "C" int gdn_stamps_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return -1;
+  return khz;
+}
+#endif

@@ -1,0 +1,130 @@
+"""Where a headline decode launch spends its time: per-workgroup clock stamps.
+
+Runs the large-beam workload (8 requests x 512 beams, H = 32, d_k = d_v =
+128, four decode steps) on libgdnbeam_stamps.so, the library built with the
+fused kernel's clock stamps compiled in (lane 0 of one consumer wave per
+workgroup reads the 100 MHz real-time clock at entry, after each prologue
+barrier and after its last tile).  Each launch runs after a 1 GiB
+cache-flushing copy, between HIP events on the launch stream, as the
+benchmark times it.  Prints a markdown summary: per step, the median time of
+each phase boundary after the first workgroup's entry, the tile loop's
+length, the spread of the exits, and the time between the HIP events that no
+workgroup covers.
+
+    python -m linear_attention_beam_gdn_amd.measure.stamps [--reps N] [--out FILE]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import os
+import sys
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(PKG)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+NAMES = ["entry", "Q (schedule inputs in)", "P (schedule built)", "S (S0 staged)", "A (tile 0 in)",
+         "loop start (dots of tile 0)", "last tile done"]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--out", default="")
+    args = ap.parse_args()
+
+    import torch
+
+    from linear_attention_beam_gdn_amd import binding as B
+    from linear_attention_beam_gdn_amd import build, configs
+
+    B.LIB_PATH = build.STAMPS_LIB
+    L = B.lib()
+    L.gdn_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    L.gdn_stamps_read.restype = ctypes.c_int
+    L.gdn_stamps_clock_khz.argtypes = []
+    L.gdn_stamps_clock_khz.restype = ctypes.c_int
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = configs.LARGE
+    inp = w.inputs()
+    steps = [B.upload(st, dev) for st in inp["steps"]]
+    store = B.Store(w.R, w.W, w.H, w.dk, w.dv, w.L, S=torch.from_numpy(inp["S0"]).to(dev))
+    outs = [torch.empty(w.R, w.W, w.H, w.dv, dtype=torch.float32, device=dev) for _ in range(w.L)]
+    stream = torch.cuda.current_stream()
+    n_wg = w.R * w.H  # one workgroup per (request, head) at this shape
+
+    def launch(t):
+        d = steps[t]
+        B.decode_step(store, t, w.W, d.get("parent"), d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                      o=outs[t], stream=stream)
+
+    for _ in range(2):
+        for t in range(w.L):
+            launch(t)
+    torch.cuda.synchronize()
+    khz = L.gdn_stamps_clock_khz()
+    tick_us = 1e3 / khz
+    src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    buf = np.zeros((n_wg, 8), np.uint64)
+    rows = {t: [] for t in range(w.L)}
+    for _ in range(args.reps):
+        for t in range(w.L):
+            dst.copy_(src)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch(t)
+            b.record(stream)
+            torch.cuda.synchronize()
+            rc = L.gdn_stamps_read(buf.ctypes.data, n_wg)
+            if rc != 0:
+                raise RuntimeError(f"gdn_stamps_read returned {rc}")
+            rows[t].append((a.elapsed_time(b) * 1e3, buf.copy()))
+
+    lines = [f"Clock stamps of `k_beam_fused<128,128,t>` at `{w.name}` (8 x 512 beams, H = 32, d = 128), "
+             f"{args.reps} launches per step, each after a 1 GiB cache-flushing copy; real-time clock "
+             f"{khz / 1e3:.0f} MHz; times in us after the first workgroup's entry, medians over "
+             f"workgroups and launches.", ""]
+    hdr = "| step | HIP events | " + " | ".join(NAMES[1:]) + " | loop (median) | loop p10-p90 | " \
+          "exit spread (last - median) | first entry to last exit | events - that |"
+    lines += [hdr, "|" + "---|" * (hdr.count("|") - 1)]
+    xcd_rows = []
+    for t in range(w.L):
+        ev = np.array([r[0] for r in rows[t]])
+        st = np.stack([r[1] for r in rows[t]]).astype(np.int64)  # [reps, wg, 8]
+        t0 = st[:, :, 0].min(axis=1, keepdims=True)
+        rel = (st[:, :, :7] - t0[..., None]) * tick_us
+        if t == 0:
+            rel[:, :, 1] = np.nan  # no barrier Q without a chain
+        med = [np.nanmedian(rel[:, :, i]) for i in range(1, 7)]
+        loop = (st[:, :, 6] - st[:, :, 5]) * tick_us
+        last = rel[:, :, 6].max(axis=1)
+        spread = last - np.median(rel[:, :, 6], axis=1)
+        gap = ev - last
+        lines.append(f"| {t} | {np.median(ev):.1f} | " + " | ".join(f"{m:.1f}" for m in med) +
+                     f" | {np.median(loop):.1f} | {np.percentile(loop, 10):.1f}-{np.percentile(loop, 90):.1f} | "
+                     f"{np.median(spread):.1f} | {np.median(last):.1f} | {np.median(gap):.1f} |")
+        xcd = (st[:, :, 7] >> 32) & 0xF
+        per = {int(x): float(np.median(rel[:, :, 6][xcd == x])) for x in np.unique(xcd)}
+        xcd_rows.append((t, per))
+    lines += ["", "Median exit (last tile done) per XCD, us after the first entry:", "",
+              "| step | " + " | ".join(f"XCD {x}" for x in sorted(xcd_rows[0][1])) + " |",
+              "|---|" + "---|" * len(xcd_rows[0][1])]
+    for t, per in xcd_rows:
+        lines.append(f"| {t} | " + " | ".join(f"{per[x]:.1f}" for x in sorted(per)) + " |")
+    text = "\n".join(lines)
+    print(text, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,91 @@
+"""Streaming rates of this GPU at fixed read:write mixes, from the hand-written
+reference kernel in k_stream.hip (measurement only; not part of the decode
+path).
+
+A mix (rd, wr) moves rd bytes read for every wr bytes written, with fully
+coalesced 16-byte accesses over buffers far larger than the 256 MB Infinity
+Cache.  For each mix the launch shape (workgroups) and store kind (plain or
+non-temporal) are swept, and the best rate is kept: the fastest this kernel
+streams that mix on this GPU.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdnmeasure.so")
+
+# (reads, writes) built into the reference kernel, by read fraction
+MIXES = [(0, 1), (1, 2), (2, 3), (4, 5), (1, 1), (5, 4), (3, 2), (2, 1), (1, 0)]
+UNIT = 4096  # bytes per block
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the package first")
+        L = ctypes.CDLL(LIB_PATH)
+        L.gdn_stream_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.gdn_stream_run.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def mix_rate(torch, stream, rd, wr, total_bytes=2 << 30, wgs=(1024, 2048, 4096, 8192), reps=10):
+    """Best rate (GB/s, read + written bytes over time) of the mix (rd, wr),
+    with the launch shape and store kind that gave it."""
+    units = total_bytes // ((rd + wr) * UNIT) // 4 * 4
+    src = torch.empty(max(1, units * rd * UNIT // 4), dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty(max(1024, units * wr * UNIT // 4), dtype=torch.float32, device="cuda")
+    nbytes = units * (rd + wr) * UNIT
+    best = (0.0, None)
+    h = ctypes.c_void_p(stream.cuda_stream)
+    for n_wg in wgs:
+        for nts in (0, 1):
+            if wr == 0 and nts:
+                continue
+
+            def go():
+                rc = lib().gdn_stream_run(rd, wr, src.data_ptr(), dst.data_ptr(), units, n_wg, nts, h)
+                if rc != 0:
+                    raise RuntimeError(f"gdn_stream_run({rd}, {wr}) returned {rc}")
+
+            go()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(reps):
+                go()
+            b.record(stream)
+            torch.cuda.synchronize()
+            gbs = nbytes / (a.elapsed_time(b) / reps * 1e-3) / 1e9
+            if gbs > best[0]:
+                best = (gbs, {"workgroups": n_wg, "nontemporal_stores": bool(nts)})
+    del src, dst
+    return {"GBps": best[0], **best[1], "read_fraction": rd / (rd + wr), "bytes": nbytes}
+
+
+def all_rates(torch, stream, **kw):
+    """Best rate of every built mix, keyed 'r<rd>w<wr>'."""
+    return {f"r{rd}w{wr}": mix_rate(torch, stream, rd, wr, **kw) for rd, wr in MIXES}
+
+
+def rate_at(rates, read_fraction):
+    """The measured rate (GB/s) at a read fraction, piecewise linear between
+    the measured mixes."""
+    pts = sorted((v["read_fraction"], v["GBps"]) for v in rates.values())
+    xs = [p[0] for p in pts]
+    ys = [p[1] for p in pts]
+    if read_fraction <= xs[0]:
+        return ys[0]
+    for i in range(1, len(xs)):
+        if read_fraction <= xs[i]:
+            f = (read_fraction - xs[i - 1]) / (xs[i] - xs[i - 1])
+            return ys[i - 1] + f * (ys[i] - ys[i - 1])
+    return ys[-1]

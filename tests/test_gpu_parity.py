@@ -50,8 +50,44 @@ def test_single_request_workload():
     check_beam(configs.SINGLE.inputs(), False, label="single-request")
 
 
+def _full_beam(w, channel, tmp_path, **over):
+    """Workload ``w`` at full size: ancestry, record keys and decays bit-exact
+    for every beam here, then o_t and delta_t of every (request, head) pair
+    against the FP64 eager oracle in a child process (full_parity)."""
+    import full_parity
+
+    if over:
+        w = dataclasses.replace(w, **over)
+    inp = w.inputs()
+    log(f"[parity] full size {w.name}: R={w.R} W={w.W} H={w.H} dk={w.dk} dv={w.dv} L={w.L}, every pair")
+    store, outs = run_beam(inp, channel)
+    steps = inp["steps"]
+    anc = O.ancestry([st.get("parent") for st in steps], w.R, steps[0]["q"].shape[1])
+    for t, st in enumerate(steps):
+        d, kbits, a, anc_t = step_records(store, t, w.W)
+        assert np.array_equal(anc_t, anc[t]), f"{w.name}: ancestry differs at t={t}"
+        assert np.array_equal(kbits, st["k"]), f"{w.name}: record keys differ at t={t}"
+        assert np.array_equal(a.reshape(st["alpha"].shape), st["alpha"]), f"{w.name}: decays differ at t={t}"
+        np.save(tmp_path / f"o_{t}.npy", outs[t])
+        np.save(tmp_path / f"d_{t}.npy", d)
+    del store, outs
+    res = full_parity.run("beam", w.name, str(tmp_path), over=over or None)
+    log(f"[parity] full size {w.name}: {res['pairs']} pairs, worst {res['worst']}, {res['seconds']:.0f} s "
+        f"on {res['workers']} host workers")
+    for k, v in res["worst"].items():
+        assert v["rel_err"] <= TOL, (w.name, k, v)
+
+
+@pytest.mark.parametrize("wname,channel", [("LARGE", False), ("KDA", True), ("SHARED_KEYS", False)])
+def test_full_size_workload_every_pair(wname, channel, tmp_path):
+    """The large-beam (8 x 512 beams, 30 % hot parent) and channel-decay
+    (16 x 256 beams) workloads, and the shared-key-head variant, compared in
+    full: every beam, head and step."""
+    _full_beam(getattr(configs, wname), channel, tmp_path)
+
+
 def test_large_beam_workload_sampled():
-    # full size (8 x 512 beams, H = 32); the oracle recomputes 2 requests x 3 heads
+    # full size, eager oracle on a sample (kept beside the full comparison)
     check_beam(configs.LARGE.inputs(), False, requests=[0, 5], heads=[0, 13, 31],
                label="large-beam")
 
@@ -77,10 +113,6 @@ def test_qwen_geometry_workloads_sampled(wname, requests, heads):
     # full size, six decode steps (chains of up to five records in the fused kernel)
     w = getattr(configs, wname)
     check_beam(w.inputs(), False, requests=requests, heads=heads, label=w.name)
-
-
-def test_kda_workload_sampled():
-    check_beam(configs.KDA.inputs(), True, requests=[0, 15], heads=[0, 31], label="kda")
 
 
 @pytest.mark.parametrize("H,Hk,dv,R,W,channel", [(64, 4, 128, 4, 256, False), (64, 16, 256, 2, 128, False),
@@ -109,20 +141,21 @@ def test_long_chain_workloads_sampled(wname, channel, requests, heads):
 
 
 @pytest.mark.parametrize("wname,fused", [("DELTALOG", False), ("DELTALOG", True), ("RWKV6", True)])
-def test_deltalog_workload(wname, fused):
+def test_deltalog_workload_every_pair(wname, fused, tmp_path):
+    """Bounded-log decoding at full size (128 sequences x 32 heads, 64
+    tokens): o_t and the appended update vector of every token, and every
+    merged base, for every (sequence, head) pair against the FP64 eager
+    oracle in a child process (full_parity)."""
+    import full_parity
+
     w = getattr(configs, wname)
     seq = w.inputs()
-    pairs = [(0, 0), (0, 31), (17, 5), (64, 16), (101, 30), (127, 0), (127, 31), (90, 9)]
-    rs = np.array([p[0] for p in pairs])
-    hs = np.array([p[1] for p in pairs])
-    log(f"[parity] {w.name} R={w.R} H={w.H} T={w.T} M={w.M} fused merge={fused}")
-    ref = O.sequence_decode(seq["S0"], seq["tokens"], w.M, pairs=pairs, rule=w.rule)
+    log(f"[parity] {w.name} R={w.R} H={w.H} T={w.T} M={w.M} fused merge={fused}, every pair")
     store = B.Store(w.R, 1, w.H, w.dk, w.dv, w.M, channel_decay=w.channel_decay, plain_update=w.plain_update,
                     S=torch.from_numpy(seq["S0"]).cuda())
     zero = torch.zeros(w.R, 1, dtype=torch.int32, device="cuda")
-    rs_d = torch.from_numpy(rs).cuda()
-    hs_d = torch.from_numpy(hs).cuda()
-    worst = 0.0
+    o_all = np.empty((w.T, w.R, w.H, w.dv), np.float32)
+    d_all = np.empty_like(o_all)
     for i in range(w.T):
         t = i % w.M
         d = B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")})
@@ -130,16 +163,20 @@ def test_deltalog_workload(wname, fused):
             o = B.decode_merge_step(store, t, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
         else:
             o = B.decode_step(store, t, 1, zero, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
-        o_s = o[rs_d, 0, hs_d].cpu().numpy()
-        d_s = store.rec_delta[t, rs_d, 0, hs_d].cpu().numpy()
-        worst = max(worst, rel_slices(o_s, ref["o"][i]), rel_slices(d_s, ref["delta"][i]))
+        o_all[i] = o[:, 0].cpu().numpy()
+        d_all[i] = store.rec_delta[t, :, 0].cpu().numpy()
         if t == w.M - 1:
             if not fused:
                 B.log_merge(store, w.M, 0)
-            S_s = store.S[rs_d, hs_d].cpu().numpy()
-            worst = max(worst, rel_states(S_s[:, None], ref["bases"][i // w.M][:, None]))
-        assert worst <= TOL, (i, worst)
-    log(f"[parity] deltalog: max rel err {worst:.2e}")
+            np.save(tmp_path / f"S_{i // w.M}.npy", store.S.cpu().numpy())
+    np.save(tmp_path / "o.npy", o_all)
+    np.save(tmp_path / "d.npy", d_all)
+    del store, o_all, d_all
+    res = full_parity.run("seq", w.name, str(tmp_path))
+    log(f"[parity] {w.name} fused={fused}: {res['pairs']} pairs, worst {res['worst']}, {res['seconds']:.0f} s "
+        f"on {res['workers']} host workers")
+    for k, v in res["worst"].items():
+        assert v["rel_err"] <= TOL, (w.name, k, v)
 
 
 # ------------------------------------------------- shapes: tiles, ragged tails
