@@ -46,13 +46,14 @@
 #ifndef GDN_BEAM_H
 #define GDN_BEAM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define GDN_BEAM_ABI_VERSION 4
+#define GDN_BEAM_ABI_VERSION 5
 
 /* status codes */
 #define GDN_OK 0
@@ -66,9 +67,11 @@ extern "C" {
 /* RWKV6 row of DeltaLog Table 1: one alpha per key channel (A = d_k) and the
  * update pair (k_t, v_t), no delta correction: S_t = diag(a_t) S_{t-1} +
  * k_t v_t^T, so the record's update vector is delta_t = v_t and beta is
- * ignored.  Bounded-log (independent sequence, W_max == 1) decoding, merge
- * and materialisation only; gdn_beam_decode_step with W_max > 1 returns
- * GDN_EUNSUPPORTED. */
+ * ignored (its pointer is still checked).  The store keeps these update
+ * vectors as bf16 (the BF16/BF16 log of DeltaLog Table 3): an exact copy of
+ * the bf16 input v_t.  Bounded-log (independent sequence, W_max == 1)
+ * decoding, merge and materialisation only; gdn_beam_decode_step with
+ * W_max > 1 returns GDN_EUNSUPPORTED. */
 #define GDN_DECAY_CHANNEL_PLAIN 2
 
 /* largest L_max (records per chain / log capacity) */
@@ -99,7 +102,10 @@ typedef struct gdn_shape {
 /* The record / ancestry store (caller-allocated device memory). */
 typedef struct gdn_store {
   float* S;          /* [R][H][dk][dv]  FP32 shared state (dense base)       */
-  float* rec_delta;  /* [L_max][R][W_max][H][dv]  FP32 update vectors delta  */
+  float* rec_delta;  /* [L_max][R][W_max][H][dv]  FP32 update vectors delta;
+                        with GDN_DECAY_CHANNEL_PLAIN the same index layout
+                        holds bf16 bit patterns (uint16_t, 2 dv bytes per
+                        record and head), the bits of v_t                    */
   uint16_t* rec_k;   /* [L_max][R][W_max][H_k][dk]  bf16 keys (bit copies)   */
   float* rec_alpha;  /* [L_max][R][W_max][H][A]   FP32 decays                */
   int32_t* anc;      /* [L_max][R][W_max][L_max]  ancestry: anc[t][r][b][j] =
@@ -163,6 +169,42 @@ int gdn_beam_decode_step(const gdn_shape* shape, const gdn_store* store, int32_t
 int gdn_decode_merge_step(const gdn_shape* shape, const gdn_store* store, int32_t t,
                           const uint16_t* q, const uint16_t* k, const uint16_t* v,
                           const float* alpha, const float* beta, float* o, void* stream);
+
+/*
+ * Split-replay bounded-log decoding (DeltaLog Figure 5 caption: an append
+ * decode in three stages, shared replay preparation, parallel append decode
+ * across value tiles, single-writer metadata commit, and a merge path of the
+ * same structure that writes back base tiles; Figure 9: the split-replay
+ * ablation).  For independent sequences (W_max == 1) with d_k = d_v = 128:
+ * decode token t exactly as gdn_beam_decode_step (merge == 0) or
+ * gdn_decode_merge_step (merge == 1) define it, with the d_v columns of each
+ * (sequence, head) cut into n_split value tiles (1, 2 or 4) that run as
+ * separate workgroups.  Every tile needs the same replay preparation: the
+ * probes c * q_t and c * k_t (c the product of the chain's per-channel
+ * decays, 1 for scalar decay) and the dot products k_j . (probe) of the
+ * log's records.
+ *   shared_prep == 1: a first kernel forms that preparation once per
+ *     (sequence, head) into `workspace` and commits the record's key, decay
+ *     and ancestry row; the tiles read it there.  workspace: device memory of
+ *     at least gdn_split_workspace_bytes(shape) bytes, 16-byte aligned, owned
+ *     by the caller, overwritten by the call (its contents are only scratch).
+ *   shared_prep == 0: every tile forms the preparation itself; tile 0
+ *     commits.  workspace is ignored (may be NULL).
+ * Results (o, the appended record, the merged base) agree with the unsplit
+ * entry points to FP32 rounding (the projections are summed over a
+ * different number of row groups); the two arms give identical bits.
+ *   n_split  1, 2 or 4;  shared_prep, merge  0 or 1
+ *   t, q, k, v, alpha, beta, o  as for gdn_decode_merge_step
+ * Returns GDN_EUNSUPPORTED unless W_max == 1 and d_k = d_v = 128 (any decay
+ * kind), GDN_EINVAL for a workspace that is missing, misaligned or too
+ * small (shared_prep == 1) and for the errors of the other entry points.
+ * Calls that share a workspace must be stream-ordered.
+ */
+size_t gdn_split_workspace_bytes(const gdn_shape* shape); /* 0 for an invalid shape */
+int gdn_decode_step_split(const gdn_shape* shape, const gdn_store* store, int32_t t, int32_t n_split,
+                          int32_t shared_prep, int32_t merge, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* v, const float* alpha, const float* beta, float* o,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Dense states after step t of n beams (the conceptual S_{t,b} of OneLA §3.1,

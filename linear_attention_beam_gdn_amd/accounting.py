@@ -9,6 +9,8 @@ A = d_k for channel decay:
 * output  o (FP32):                         out = 4 d_v
 * record  (alpha FP32 x A, delta FP32 d_v, k bf16 d_k), appended once and
           read back by every descendant:   rec = 4 A + 4 d_v + 2 d_k
+          (the plain rule, RWKV6, keeps its update vector v_t in bf16 and
+          reads no beta: rec = 4 A + 2 d_v + 2 d_k, in = ... without the 4)
 * shared state, read once per (request, head) per step: 4 d_k d_v.
 
 Ancestor records read at step t are counted two ways:
@@ -28,14 +30,14 @@ import numpy as np
 MiB = float(1 << 20)
 
 
-def record_bytes(dk, dv, channel_decay=False):
-    A = dk if channel_decay else 1
-    return 4 * A + 4 * dv + 2 * dk
+def record_bytes(dk, dv, channel_decay=False, plain=False):
+    A = dk if (channel_decay or plain) else 1
+    return 4 * A + (2 if plain else 4) * dv + 2 * dk
 
 
-def input_bytes(dk, dv, channel_decay=False):
-    A = dk if channel_decay else 1
-    return 4 * dk + 2 * dv + 4 * A + 4
+def input_bytes(dk, dv, channel_decay=False, plain=False):
+    A = dk if (channel_decay or plain) else 1
+    return 4 * dk + 2 * dv + 4 * A + (0 if plain else 4)
 
 
 def output_bytes(dv):
@@ -85,24 +87,24 @@ def beam_step_flops(*, R, H, dk, dv, W_t, t):
     return R * W_t * H * per
 
 
-def sequence_token_bytes(*, R, H, dk, dv, log_len, channel_decay=False):
+def sequence_token_bytes(*, R, H, dk, dv, log_len, channel_decay=False, plain=False):
     """One W = 1 decode token with ``log_len`` records in the log."""
-    rec = record_bytes(dk, dv, channel_decay)
-    per = input_bytes(dk, dv, channel_decay) + output_bytes(dv) + rec + log_len * rec
+    rec = record_bytes(dk, dv, channel_decay, plain)
+    per = input_bytes(dk, dv, channel_decay, plain) + output_bytes(dv) + rec + log_len * rec
     return R * H * (4 * dk * dv + per)
 
 
-def merge_bytes(*, R, H, dk, dv, n_rec, channel_decay=False):
+def merge_bytes(*, R, H, dk, dv, n_rec, channel_decay=False, plain=False):
     """Fold n_rec records into the dense base: base read + written + records."""
-    return R * H * (2 * 4 * dk * dv + n_rec * record_bytes(dk, dv, channel_decay))
+    return R * H * (2 * 4 * dk * dv + n_rec * record_bytes(dk, dv, channel_decay, plain))
 
 
-def decode_merge_bytes(*, R, H, dk, dv, log_len, channel_decay=False):
+def decode_merge_bytes(*, R, H, dk, dv, log_len, channel_decay=False, plain=False):
     """The decode that fills the log with the merge in the same pass: the
     token's bytes (base read once), the base written back, and the log's
     log_len + 1 records read by the fold."""
-    rec = record_bytes(dk, dv, channel_decay)
-    return (sequence_token_bytes(R=R, H=H, dk=dk, dv=dv, log_len=log_len, channel_decay=channel_decay)
+    rec = record_bytes(dk, dv, channel_decay, plain)
+    return (sequence_token_bytes(R=R, H=H, dk=dk, dv=dv, log_len=log_len, channel_decay=channel_decay, plain=plain)
             + R * H * (4 * dk * dv + (log_len + 1) * rec))
 
 

@@ -58,6 +58,11 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_merge_step.argtypes = [ctypes.POINTER(GdnShape), ctypes.POINTER(GdnStore), I32,
                                             P, P, P, P, P, P, P]
         L.gdn_decode_merge_step.restype = ctypes.c_int
+        L.gdn_split_workspace_bytes.argtypes = [ctypes.POINTER(GdnShape)]
+        L.gdn_split_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_decode_step_split.argtypes = [ctypes.POINTER(GdnShape), ctypes.POINTER(GdnStore), I32, I32, I32,
+                                            I32, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.gdn_decode_step_split.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -108,7 +113,8 @@ _BF16 = (torch.bfloat16, torch.int16)
 class Store:
     """Caller-owned record / ancestry store (device memory from PyTorch).
 
-    S [R,H,dk,dv] FP32, rec_delta [L,R,W,H,dv] FP32, rec_k [L,R,W,Hk,dk] bf16,
+    S [R,H,dk,dv] FP32, rec_delta [L,R,W,H,dv] FP32 (bf16 with the plain
+    update rule, whose update vectors are v itself), rec_k [L,R,W,Hk,dk] bf16,
     rec_alpha [L,R,W,H,A] FP32, anc [L,R,W,L] int32.
     """
 
@@ -129,7 +135,8 @@ class Store:
         f32 = dict(dtype=torch.float32, device=device)
         self.S = torch.zeros(R, H, dk, dv, **f32) if S is None else S
         self.device = self.S.device
-        self.rec_delta = torch.zeros(L_max, R, W_max, H, dv, **f32)
+        self.rec_delta = torch.zeros(L_max, R, W_max, H, dv, dtype=torch.bfloat16 if plain_update else torch.float32,
+                                     device=device)
         self.rec_k = torch.zeros(L_max, R, W_max, self.Hk, dk, dtype=torch.bfloat16, device=device)
         self.rec_alpha = torch.zeros(L_max, R, W_max, H, self.A, **f32)
         self.anc = torch.zeros(L_max, R, W_max, L_max, dtype=torch.int32, device=device)
@@ -191,6 +198,41 @@ def decode_merge_step(store: Store, t, q, k, v, alpha, beta, o=None, stream=None
                                      _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream, store.device))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_decode_merge_step")
+    return o
+
+
+def split_workspace_bytes(store: Store) -> int:
+    """Bytes of the workspace the shared-preparation arm of
+    decode_step_split needs for this store (gdn_split_workspace_bytes)."""
+    return int(lib().gdn_split_workspace_bytes(ctypes.byref(store.shape)))
+
+
+def decode_step_split(store: Store, t, n_split, shared_prep, merge, q, k, v, alpha, beta, o=None,
+                      workspace=None, stream=None):
+    """Token t of independent sequences with d_v cut into n_split value tiles
+    (gdn_decode_step_split); shared_prep forms the replay preparation once in
+    ``workspace`` (a device tensor of at least split_workspace_bytes bytes),
+    else every tile forms it; merge folds the full log as decode_merge_step
+    does.  Returns o [R,1,H,dv] FP32."""
+    R, H, dk, dv, dev = store.R, store.H, store.dk, store.dv, store.device
+    _check(q, "q", _BF16, (R, 1, store.Hk, dk), dev)
+    _check(k, "k", _BF16, (R, 1, store.Hk, dk), dev)
+    _check(v, "v", _BF16, (R, 1, H, dv), dev)
+    _check(alpha, "alpha", (torch.float32,), (R, 1, H, dk) if store.channel_decay else (R, 1, H), dev)
+    _check(beta, "beta", (torch.float32,), (R, 1, H), dev)
+    if o is None:
+        o = torch.empty(R, 1, H, dv, dtype=torch.float32, device=dev)
+    _check(o, "o", (torch.float32,), (R, 1, H, dv), dev)
+    ws, ws_bytes = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor on the store's device")
+        ws, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rc = lib().gdn_decode_step_split(ctypes.byref(store.shape), ctypes.byref(store.cstore), t, n_split,
+                                     int(bool(shared_prep)), int(bool(merge)), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(alpha), _ptr(beta), _ptr(o), ws, ws_bytes, _stream(stream, store.device))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_decode_step_split")
     return o
 
 

@@ -2,8 +2,8 @@
 
 Shapes follow the OneLA operator suite (§4.1: R requests, W beams, T decode
 steps, H heads, K = d_k, V = d_v) and the DeltaLog recurrent-kernel table
-(Table 3: H/d_k/d_v = 32/128/128, FP32 state; GDN log with M = 8, RWKV6 log
-with M = 4).  Seeds: the tiny workload uses seed 0; the others use their index.
+(Table 3: H/d_k/d_v = 32/128/128, FP32 state; GDN log with M = 8, KDA and
+RWKV6 logs with M = 4).  Seeds: the tiny workload uses seed 0; the others use their index.
 """
 
 from __future__ import annotations
@@ -104,5 +104,9 @@ QWEN_R16 = BeamWorkload("onela_qwen_geometry_r16", R=16, H=16, dk=128, dv=128, W
 RWKV6 = SequenceWorkload("rwkv6_bounded_log", R=128, H=32, dk=128, dv=128, T=64, M=4,
                          s0_std=0.05, seed=5, channel_decay=True, plain_update=True)
 
-ALL = (TINY, SINGLE, LARGE, DELTALOG, KDA, RWKV6, SHARED_KEYS, WIDE, KDA_WIDE, QWEN_R4, QWEN_R16)
+# the KDA row of DeltaLog Table 3: 32/128/128, FP32 state, BF16 K / FP32 U log, M = 4
+KDA_LOG = SequenceWorkload("kda_bounded_log", R=128, H=32, dk=128, dv=128, T=64, M=4,
+                           s0_std=0.05, seed=11, channel_decay=True)
+
+ALL = (TINY, SINGLE, LARGE, DELTALOG, KDA, RWKV6, SHARED_KEYS, WIDE, KDA_WIDE, QWEN_R4, QWEN_R16, KDA_LOG)
 BY_NAME = {w.name: w for w in ALL}

@@ -1,6 +1,7 @@
 // C ABI of libgdnbeam (declared in include/gdn_beam.h): host-side argument
 // validation, then dispatch to the gfx950 kernels on the caller's stream.
 // Validation touches no HIP API, so every error path runs without a GPU.
+#include <stddef.h>
 #include <stdint.h>
 
 #include "gdn_beam.h"
@@ -105,6 +106,32 @@ int gdn_decode_merge_step(const gdn_shape* shape, const gdn_store* store, int32_
     return GDN_EINVAL;
   const gdn::StepIO io{nullptr, q, k, v, alpha, beta, o};
   return gdn::launch_seq_decode(*shape, *store, t, true, io, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t gdn_split_workspace_bytes(const gdn_shape* shape) {
+  if (check_shape(shape) != GDN_OK) return 0;
+  return gdn::seq_split_workspace_bytes(*shape);
+}
+
+int gdn_decode_step_split(const gdn_shape* shape, const gdn_store* store, int32_t t, int32_t n_split,
+                          int32_t shared_prep, int32_t merge, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* v, const float* alpha, const float* beta, float* o, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if ((rc = check_store(store)) != GDN_OK) return rc;
+  if (shape->W_max != 1 || !gdn::seq_split_supported(*shape, n_split)) return GDN_EUNSUPPORTED;
+  if (t < 0 || t >= shape->L_max || (merge != 0 && merge != 1) || (shared_prep != 0 && shared_prep != 1))
+    return GDN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 16) ||
+      !aligned(beta, 16) || !aligned(o, 16))
+    return GDN_EINVAL;
+  if (shared_prep && (!aligned(workspace, 16) || workspace_bytes < gdn::seq_split_workspace_bytes(*shape)))
+    return GDN_EINVAL;
+  const gdn::StepIO io{nullptr, q, k, v, alpha, beta, o};
+  return gdn::launch_seq_split(*shape, *store, t, merge != 0, n_split, shared_prep != 0,
+                               shared_prep ? static_cast<float*>(workspace) : nullptr, io,
+                               reinterpret_cast<hipStream_t>(stream));
 }
 
 int gdn_materialize(const gdn_shape* shape, const gdn_store* store, int32_t t, const int32_t* rb,

@@ -50,6 +50,14 @@ int launch_beam_fused_kda(const gdn_shape& sh, const gdn_store& st, int t, int W
 int launch_seq_decode(const gdn_shape& sh, const gdn_store& st, int t, bool merge, const StepIO& io,
                       hipStream_t stream);
 
+// The same step with d_v cut into n_split value tiles per (sequence, head),
+// the replay preparation formed once into `prep` (shared_prep, a workspace
+// of seq_split_workspace_bytes) or by every tile.
+bool seq_split_supported(const gdn_shape& sh, int n_split);
+size_t seq_split_workspace_bytes(const gdn_shape& sh);
+int launch_seq_split(const gdn_shape& sh, const gdn_store& st, int t, bool merge, int n_split, bool shared_prep,
+                     float* prep, const StepIO& io, hipStream_t stream);
+
 // Fold chains of records onto dense states.  Item i is the (request, beam)
 // pair rb[2i], rb[2i+1] (or (i, beam) when rb is NULL); its chain is the
 // ancestors in anc row t and its own record at step t.  Reads the state of

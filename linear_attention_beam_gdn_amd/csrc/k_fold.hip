@@ -13,6 +13,9 @@
 // decays of a record are the same for a whole row, the update vector for a
 // column.  States up to 128 x 128 take one slice; wider ones (d_v = 512 or
 // d_k = 256) are cut into NSL slices of d_k rows.
+//
+// Update vectors are FP32, or bf16 for the plain rule (the RWKV6 row of
+// DeltaLog Table 1, whose log keeps U in BF16 per Table 3).
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -22,7 +25,7 @@ namespace {
 struct FoldArgs {
   const float* src;
   float* dst;
-  const float* rec_delta;
+  const float* rec_delta;  // FP32 update vectors (bf16 bit patterns when UB16)
   const uint16_t* rec_k;
   const float* rec_alpha;
   const int32_t* anc;
@@ -50,6 +53,8 @@ struct FoldGeom {
   static constexpr int KCH = DK / 8, DCH = DV / 4, ACH = DK / 4;
   static constexpr int NKL = (GDN_MAX_STEPS * KCH + NT - 1) / NT;
   static constexpr int NDL = (GDN_MAX_STEPS * DCH + NT - 1) / NT;
+  static constexpr int VCH = DV / 8;  // 16-byte pieces of a bf16 update vector
+  static constexpr int NDL16 = (GDN_MAX_STEPS * VCH + NT - 1) / NT;
   static constexpr int NAL = (GDN_MAX_STEPS * ACH + NT - 1) / NT;
 };
 
@@ -61,7 +66,7 @@ __host__ __device__ constexpr int fold_lds_floats(int dk, int dv, int a, int n) 
 
 // Built for four waves per SIMD (at most 128 registers) where that needs no
 // spills: d_v up to 256, and d_v = 128 with per-channel decay.
-template <int DK, int DV, bool CH>
+template <int DK, int DV, bool CH, bool UB16>
 __global__ __launch_bounds__((FoldGeom<DK, DV>::NT), ((DV <= 256 && !(CH && DV > 128)) ? 4 : 1))
 void k_fold(FoldArgs a) {
   using G = FoldGeom<DK, DV>;
@@ -104,9 +109,12 @@ void k_fold(FoldArgs a) {
     const int slot = j < t ? clampi(arow[j], 0, a.Wm - 1) : b;
     return (((size_t)j * a.R + r) * a.Wm + slot) * a.Hk + h / a.gq;
   };
-  const int nk = n * G::KCH, nd = n * G::DCH;
+  const int nk = n * G::KCH, nd = UB16 ? n * G::VCH : n * G::DCH;
+  constexpr int NDLX = UB16 ? G::NDL16 : G::NDL;
   u32x4 kb[G::NKL];
-  f32x4 db[G::NDL], ab[CH ? G::NAL : 1];
+  f32x4 db[UB16 ? 1 : G::NDL], ab[CH ? G::NAL : 1];
+  u32x4 db16[UB16 ? G::NDL16 : 1];
+  const uint16_t* rec_u16 = reinterpret_cast<const uint16_t*>(a.rec_delta);
   float as = 0.f;
 #pragma unroll
   for (int m = 0; m < G::NKL; ++m) {
@@ -114,9 +122,12 @@ void k_fold(FoldArgs a) {
     kb[m] = *reinterpret_cast<const u32x4*>(a.rec_k + rec_at_k(c / G::KCH) * DK + (c % G::KCH) * 8);
   }
 #pragma unroll
-  for (int m = 0; m < G::NDL; ++m) {
+  for (int m = 0; m < NDLX; ++m) {
     const int c = min(tid + m * G::NT, nd - 1);
-    db[m] = *reinterpret_cast<const f32x4*>(a.rec_delta + rec_at(c / G::DCH) * DV + (c % G::DCH) * 4);
+    if constexpr (UB16)
+      db16[m] = *reinterpret_cast<const u32x4*>(rec_u16 + rec_at(c / G::VCH) * DV + (c % G::VCH) * 8);
+    else
+      db[m] = *reinterpret_cast<const f32x4*>(a.rec_delta + rec_at(c / G::DCH) * DV + (c % G::DCH) * 4);
   }
   if constexpr (CH) {
 #pragma unroll
@@ -143,8 +154,18 @@ void k_fold(FoldArgs a) {
     }
   }
 #pragma unroll
-  for (int m = 0; m < G::NDL; ++m)
-    if (tid + m * G::NT < nd) *reinterpret_cast<f32x4*>(ld + (tid + m * G::NT) * 4) = db[m];
+  for (int m = 0; m < NDLX; ++m) {
+    const int c = tid + m * G::NT;
+    if constexpr (UB16) {
+      if (c < nd) {
+        const u32x4 w = db16[m];
+        *reinterpret_cast<f32x4*>(ld + c * 8) = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+        *reinterpret_cast<f32x4*>(ld + c * 8 + 4) = f32x4{bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3])};
+      }
+    } else {
+      if (c < nd) *reinterpret_cast<f32x4*>(ld + c * 4) = db[m];
+    }
+  }
   if constexpr (CH) {
 #pragma unroll
     for (int m = 0; m < G::NAL; ++m)
@@ -174,7 +195,7 @@ void k_fold(FoldArgs a) {
     *reinterpret_cast<f32x4*>(dst + (size_t)(row0 + i) * DV + c4 * 4) = st[i];
 }
 
-template <int DK, int DV, bool CH>
+template <int DK, int DV, bool CH, bool UB16 = false>
 int launch(const gdn_shape& sh, const gdn_store& st, int t, const int32_t* rb, int beam, int n,
            const float* src, float* dst, bool dst_per_item, hipStream_t stream) {
   FoldArgs a;
@@ -197,7 +218,7 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, const int32_t* rb, i
   const long grid = (long)n * sh.H * FoldGeom<DK, DV>::NSL;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
   const size_t lds = (size_t)fold_lds_floats(DK, DV, CH ? DK : 1, t + 1) * sizeof(float);
-  hipLaunchKernelGGL((k_fold<DK, DV, CH>), dim3((unsigned)grid), dim3(FoldGeom<DK, DV>::NT), lds,
+  hipLaunchKernelGGL((k_fold<DK, DV, CH, UB16>), dim3((unsigned)grid), dim3(FoldGeom<DK, DV>::NT), lds,
                      stream, a);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
 }
@@ -206,15 +227,25 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, const int32_t* rb, i
 
 int launch_fold(const gdn_shape& sh, const gdn_store& st, int t, const int32_t* rb, int beam, int n,
                 const float* src, float* dst, bool dst_per_item, hipStream_t stream) {
-  const bool ch = sh.decay_kind != GDN_DECAY_SCALAR;  // the fold is the same for both channel rules
-#define GDN_CASE(DK_, DV_)                                                           \
-  if (sh.dk == DK_ && sh.dv == DV_)                                                  \
-    return ch ? launch<DK_, DV_, true>(sh, st, t, rb, beam, n, src, dst, dst_per_item, stream) \
-              : launch<DK_, DV_, false>(sh, st, t, rb, beam, n, src, dst, dst_per_item, stream);
+  // the fold is the same for both channel rules; the plain rule keeps its
+  // update vectors (v_t itself) in bf16
+  const bool ch = sh.decay_kind != GDN_DECAY_SCALAR;
+  const bool plain = sh.decay_kind == GDN_DECAY_CHANNEL_PLAIN;
+#define GDN_CASE(DK_, DV_)                                                                          \
+  if (sh.dk == DK_ && sh.dv == DV_) {                                                               \
+    if (plain) return launch<DK_, DV_, true, true>(sh, st, t, rb, beam, n, src, dst, dst_per_item, stream); \
+    return ch ? launch<DK_, DV_, true>(sh, st, t, rb, beam, n, src, dst, dst_per_item, stream)      \
+              : launch<DK_, DV_, false>(sh, st, t, rb, beam, n, src, dst, dst_per_item, stream);    \
+  }
   GDN_CASE(16, 16)
   GDN_CASE(32, 32)
   GDN_CASE(64, 64)
   GDN_CASE(128, 128)
+#undef GDN_CASE
+#define GDN_CASE(DK_, DV_)                                                           \
+  if (sh.dk == DK_ && sh.dv == DV_ && !plain)                                        \
+    return ch ? launch<DK_, DV_, true>(sh, st, t, rb, beam, n, src, dst, dst_per_item, stream) \
+              : launch<DK_, DV_, false>(sh, st, t, rb, beam, n, src, dst, dst_per_item, stream);
   GDN_CASE(128, 256)
   GDN_CASE(128, 512)
 #undef GDN_CASE

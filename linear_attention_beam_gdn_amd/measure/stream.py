@@ -89,3 +89,23 @@ def rate_at(rates, read_fraction):
             f = (read_fraction - xs[i - 1]) / (xs[i] - xs[i - 1])
             return ys[i - 1] + f * (ys[i] - ys[i - 1])
     return ys[-1]
+
+
+class ReadFlush:
+    """Evicts the 256 MB Infinity Cache by reading a 1 GiB buffer with the
+    reads-only mix: the cache then holds clean lines of that buffer and none
+    of the next kernel's data, and no dirty line of the flush is left to be
+    written back while the next kernel runs (a copy would leave up to the
+    cache's size of them)."""
+
+    def __init__(self, torch, nbytes=1 << 30):
+        self.units = nbytes // UNIT // 4 * 4
+        self.src = torch.zeros(self.units * UNIT // 4, dtype=torch.float32, device="cuda")
+        self.dst = torch.empty(1024, dtype=torch.float32, device="cuda")
+
+    def __call__(self, stream):
+        rc = lib().gdn_stream_run(1, 0, self.src.data_ptr(), self.dst.data_ptr(), self.units, 1024, 0,
+                                  ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"gdn_stream_run(1, 0) returned {rc}")
+

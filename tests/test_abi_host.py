@@ -39,7 +39,8 @@ def decode(L, sh=None, st=None, t=1, W_t=4, parent=FAKE, q=FAKE, k=FAKE, v=FAKE,
 def test_exports_every_header_function(L):
     names = B.header_functions()
     assert set(names) == {"gdn_beam_decode_step", "gdn_decode_merge_step", "gdn_materialize",
-                          "gdn_log_merge", "gdn_status_string", "gdn_abi_version"}
+                          "gdn_log_merge", "gdn_status_string", "gdn_abi_version",
+                          "gdn_split_workspace_bytes", "gdn_decode_step_split"}
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
@@ -49,7 +50,7 @@ def test_exports_every_header_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gdn_abi_version() == 4
+    assert L.gdn_abi_version() == 5
     for s in (B.GDN_OK, B.GDN_EINVAL, B.GDN_EUNSUPPORTED, B.GDN_EHIP, 12345):
         assert isinstance(B.status_string(s), str) and B.status_string(s)
 
@@ -137,3 +138,33 @@ def test_decode_merge_validation(L):
         assert dm(**{name: FAKE + 8}) == E, name
     for name in ("S", "rec_delta", "rec_k", "rec_alpha", "anc"):
         assert dm(st=store(**{name: None})) == E, name
+
+
+def split(L, sh=None, st=None, t=1, n_split=2, shared=1, merge=0, ws=FAKE, ws_bytes=1 << 30):
+    sh = shape(W_max=1) if sh is None else sh
+    st = store() if st is None else st
+    return L.gdn_decode_step_split(ctypes.byref(sh), ctypes.byref(st), t, n_split, shared, merge, FAKE, FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_split_workspace_size(L):
+    # one replay preparation per (sequence, head): 2 d_k probes, 2 x 16 dot products, k_t . q_t, padding
+    sh = shape(R=128, W_max=1, H=32)
+    assert L.gdn_split_workspace_bytes(ctypes.byref(sh)) == 128 * 32 * (2 * 128 + 2 * 16 + 4) * 4
+    assert L.gdn_split_workspace_bytes(ctypes.byref(shape(R=0))) == 0
+
+
+def test_split_validation(L):
+    E, U = B.GDN_EINVAL, B.GDN_EUNSUPPORTED
+    need = L.gdn_split_workspace_bytes(ctypes.byref(shape(W_max=1)))
+    assert split(L, sh=shape(W_max=4)) == U                    # beams: sequences only
+    assert split(L, sh=shape(W_max=1, dk=64, dv=64)) == U      # d = 128 only
+    assert split(L, n_split=3) == U and split(L, n_split=8) == U
+    assert split(L, t=4) == E and split(L, t=-1) == E
+    assert split(L, merge=2) == E and split(L, shared=2) == E
+    assert split(L, ws=None) == E                             # the shared arm needs a workspace
+    assert split(L, ws=FAKE + 4) == E                         # misaligned
+    assert split(L, ws_bytes=need - 1) == E                   # too small
+    assert split(L, st=store(rec_k=FAKE + 2)) == E
+    assert split(L, sh=shape(W_max=1, decay_kind=7)) == U
+

@@ -140,43 +140,71 @@ def test_long_chain_workloads_sampled(wname, channel, requests, heads):
     check_beam(w.inputs(), channel, requests=requests, heads=heads, label=f"{w.name} L = 7")
 
 
-@pytest.mark.parametrize("wname,fused", [("DELTALOG", False), ("DELTALOG", True), ("RWKV6", True)])
-def test_deltalog_workload_every_pair(wname, fused, tmp_path):
-    """Bounded-log decoding at full size (128 sequences x 32 heads, 64
-    tokens): o_t and the appended update vector of every token, and every
-    merged base, for every (sequence, head) pair against the FP64 eager
-    oracle in a child process (full_parity)."""
+def _full_sequences(w, fused, tmp_path, split=None):
+    """Bounded-log decoding of workload ``w`` at full size, every token's o_t
+    and appended update vector and every merged base, for every (sequence,
+    head) pair against the FP64 eager oracle in a child process
+    (full_parity).  ``split`` = (n_split, shared_prep) runs every token
+    through gdn_decode_step_split instead (merge fused into the token that
+    fills the log)."""
     import full_parity
 
-    w = getattr(configs, wname)
     seq = w.inputs()
-    log(f"[parity] {w.name} R={w.R} H={w.H} T={w.T} M={w.M} fused merge={fused}, every pair")
+    log(f"[parity] {w.name} R={w.R} H={w.H} T={w.T} M={w.M} fused merge={fused} split={split}, every pair")
     store = B.Store(w.R, 1, w.H, w.dk, w.dv, w.M, channel_decay=w.channel_decay, plain_update=w.plain_update,
                     S=torch.from_numpy(seq["S0"]).cuda())
+    ws = None
+    if split is not None and split[1]:
+        ws = torch.empty(B.split_workspace_bytes(store) // 4, dtype=torch.float32, device="cuda")
     zero = torch.zeros(w.R, 1, dtype=torch.int32, device="cuda")
     o_all = np.empty((w.T, w.R, w.H, w.dv), np.float32)
     d_all = np.empty_like(o_all)
     for i in range(w.T):
         t = i % w.M
         d = B.upload({n: seq["tokens"][n][i][:, None] for n in ("q", "k", "v", "alpha", "beta")})
-        if fused and t == w.M - 1:
-            o = B.decode_merge_step(store, t, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        if split is not None:
+            o = B.decode_step_split(store, t, split[0], split[1], t == w.M - 1, *args, workspace=ws)
+        elif fused and t == w.M - 1:
+            o = B.decode_merge_step(store, t, *args)
         else:
-            o = B.decode_step(store, t, 1, zero, d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+            o = B.decode_step(store, t, 1, zero, *args)
         o_all[i] = o[:, 0].cpu().numpy()
-        d_all[i] = store.rec_delta[t, :, 0].cpu().numpy()
+        d_all[i] = store.rec_delta[t, :, 0].float().cpu().numpy()
+        if w.plain_update:  # the bf16 log holds v_t's own bits (DeltaLog Table 3, RWKV6 row)
+            bits = store.rec_delta[t, :, 0].view(torch.int16).cpu().numpy().view(np.uint16)
+            assert np.array_equal(bits, seq["tokens"]["v"][i]), i
         if t == w.M - 1:
-            if not fused:
+            if not fused and split is None:
                 B.log_merge(store, w.M, 0)
             np.save(tmp_path / f"S_{i // w.M}.npy", store.S.cpu().numpy())
     np.save(tmp_path / "o.npy", o_all)
     np.save(tmp_path / "d.npy", d_all)
     del store, o_all, d_all
-    res = full_parity.run("seq", w.name, str(tmp_path))
-    log(f"[parity] {w.name} fused={fused}: {res['pairs']} pairs, worst {res['worst']}, {res['seconds']:.0f} s "
-        f"on {res['workers']} host workers")
+    res = full_parity.run("seq", w.name, str(tmp_path), over={"M": w.M})
+    log(f"[parity] {w.name} fused={fused} split={split}: {res['pairs']} pairs, worst {res['worst']}, "
+        f"{res['seconds']:.0f} s on {res['workers']} host workers")
     for k, v in res["worst"].items():
         assert v["rel_err"] <= TOL, (w.name, k, v)
+
+
+@pytest.mark.parametrize("wname,fused", [("DELTALOG", False), ("DELTALOG", True), ("RWKV6", True),
+                                         ("KDA_LOG", True)])
+def test_deltalog_workload_every_pair(wname, fused, tmp_path):
+    """Bounded-log decoding at full size (128 sequences x 32 heads, 64
+    tokens), every pair: the GDN log (M = 8) with separate and fused merges,
+    and the RWKV6 and KDA logs (M = 4, DeltaLog Table 3)."""
+    _full_sequences(getattr(configs, wname), fused, tmp_path)
+
+
+@pytest.mark.parametrize("wname,M,split", [("DELTALOG", 8, (4, True)), ("DELTALOG", 4, (2, False)),
+                                           ("KDA_LOG", 4, (2, True)), ("KDA_LOG", 8, (4, False)),
+                                           ("RWKV6", 4, (4, True)), ("RWKV6", 8, (2, False))])
+def test_split_replay_workload_every_pair(wname, M, split, tmp_path):
+    """The split-replay path (value tiles; preparation shared through the
+    workspace or repeated per tile) at full size, every pair, for the three
+    rules at log capacities 4 and 8 (DeltaLog Figure 9)."""
+    _full_sequences(dataclasses.replace(getattr(configs, wname), M=M), True, tmp_path, split=split)
 
 
 # ------------------------------------------------- shapes: tiles, ragged tails

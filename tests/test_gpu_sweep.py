@@ -194,6 +194,13 @@ def _check_sequences(c):
         e = rel_slices(o[:, 0].cpu().numpy().reshape(R * H, dv), ref["o"][i])
         worst = max(worst, e)
         assert e <= TOL, (label, i, e)
+        if plain:  # the bf16 log keeps v_t's own bits
+            bits = store.rec_delta[t, :, 0].view(torch.int16).cpu().numpy().view(np.uint16)
+            assert np.array_equal(bits, seq["tokens"]["v"][i]), (label, "log bits", i)
+        else:
+            e = rel_slices(store.rec_delta[t, :, 0].cpu().numpy().reshape(R * H, dv), ref["delta"][i])
+            worst = max(worst, e)
+            assert e <= TOL, (label, "delta", i, e)
         if t == M - 1:
             e = rel_states(store.S.cpu().numpy().reshape(R * H, 1, dk, dv), ref["bases"][i // M][:, None])
             worst = max(worst, e)
