@@ -4,9 +4,9 @@ Runs the large-beam workload (8 requests x 512 beams, H = 32, d_k = d_v =
 128, four decode steps) on libgdnbeam_stamps.so, the library built with the
 fused kernel's clock stamps compiled in (lane 0 of one consumer wave per
 workgroup reads the 100 MHz real-time clock at entry, after each prologue
-barrier and after its last tile).  Each launch runs after a 1 GiB
-cache-flushing copy, between HIP events on the launch stream, as the
-benchmark times it.  Prints a markdown summary: per step, the median time of
+barrier and after its last tile).  Each launch runs after a 1 GiB read-only
+sweep that evicts the Infinity Cache, between HIP events on the launch
+stream, as the benchmark times it.  Prints a markdown summary: per step, the median time of
 each phase boundary after the first workgroup's entry, the tile loop's
 length, the spread of the exits, and the time between the HIP events that no
 workgroup covers.
@@ -71,13 +71,14 @@ def main():
     torch.cuda.synchronize()
     khz = L.gdn_stamps_clock_khz()
     tick_us = 1e3 / khz
-    src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
+    from linear_attention_beam_gdn_amd.measure import stream as S
+
+    flush = S.ReadFlush(torch)
     buf = np.zeros((n_wg, 8), np.uint64)
     rows = {t: [] for t in range(w.L)}
     for _ in range(args.reps):
         for t in range(w.L):
-            dst.copy_(src)
+            flush(stream)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             launch(t)
@@ -89,7 +90,7 @@ def main():
             rows[t].append((a.elapsed_time(b) * 1e3, buf.copy()))
 
     lines = [f"Clock stamps of `k_beam_fused<128,128,t>` at `{w.name}` (8 x 512 beams, H = 32, d = 128), "
-             f"{args.reps} launches per step, each after a 1 GiB cache-flushing copy; real-time clock "
+             f"{args.reps} launches per step, each after a 1 GiB read-only cache-flushing sweep; real-time clock "
              f"{khz / 1e3:.0f} MHz; times in us after the first workgroup's entry, medians over "
              f"workgroups and launches.", ""]
     hdr = "| step | HIP events | " + " | ".join(NAMES[1:]) + " | loop (median) | loop p10-p90 | " \
