@@ -36,6 +36,8 @@
  *     error nothing is enqueued and a negative status is returned.
  *   - No global mutable state: calls on different stores or streams are
  *     independent.  Calls that write the same store must be stream-ordered.
+ *     The one exception is gdn_decode_step_split_noalloc, whose built-in
+ *     scratch buffer (one per GPU) all its calls on that GPU share.
  *   - Two environment variables, read at every beam-decode call, exist for
  *     tests and comparisons only: GDN_BEAM_CHUNK=n (a multiple of 16, at
  *     least 16) fixes the number of beams per workgroup, which only changes
@@ -60,6 +62,7 @@ extern "C" {
 #define GDN_EINVAL (-1)       /* null/misaligned pointer, index or size out of range */
 #define GDN_EUNSUPPORTED (-2) /* (d_k, d_v) pair or decay kind not built in */
 #define GDN_EHIP (-3)         /* the HIP runtime rejected a kernel launch */
+#define GDN_ESCRATCH (-4)     /* larger than the built-in scratch buffer (no-alloc entry point) */
 
 /* decay kinds (and update rules) */
 #define GDN_DECAY_SCALAR 0  /* GDN: one alpha per (beam, head, step)      */
@@ -205,6 +208,30 @@ int gdn_decode_step_split(const gdn_shape* shape, const gdn_store* store, int32_
                           int32_t shared_prep, int32_t merge, const uint16_t* q, const uint16_t* k,
                           const uint16_t* v, const float* alpha, const float* beta, float* o,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_decode_step_split without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving
+ * loops that must not allocate, harnesses that forbid it.  The
+ * shared-preparation arm keeps its workspace in a buffer built into the
+ * library, one per GPU, GDN_SPLIT_SCRATCH_BYTES long and held until the
+ * process ends; its device address is looked up (not allocated) once per
+ * device, at the first call on that device.  Nothing is allocated or freed.
+ *   Arguments, results and errors as gdn_decode_step_split; in addition
+ *   GDN_ESCRATCH when shared_prep == 1 and gdn_split_workspace_bytes(shape)
+ *   exceeds GDN_SPLIT_SCRATCH_BYTES (8 MiB: 7,182 (sequence, head) pairs at
+ *   d_k = 128), GDN_EHIP when the buffer's address cannot be found.
+ * Every call on one GPU shares that buffer and the buffer keeps the last
+ * call's contents (each call writes every entry it reads before reading
+ * it, so nothing needs to start at zero): calls that overlap on one GPU
+ * (other streams, or host threads without ordering) race and must not be
+ * issued; stream-order them.
+ */
+#define GDN_SPLIT_SCRATCH_BYTES (8u << 20)
+int gdn_decode_step_split_noalloc(const gdn_shape* shape, const gdn_store* store, int32_t t, int32_t n_split,
+                                  int32_t shared_prep, int32_t merge, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, const float* alpha, const float* beta, float* o,
+                                  void* stream);
 
 /*
  * Dense states after step t of n beams (the conceptual S_{t,b} of OneLA §3.1,

@@ -17,7 +17,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgdnbeam.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "gdn_beam.h")
 
-GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP = 0, -1, -2, -3
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP, GDN_ESCRATCH = 0, -1, -2, -3, -4
+GDN_SPLIT_SCRATCH_BYTES = 8 << 20
 GDN_DECAY_SCALAR, GDN_DECAY_CHANNEL, GDN_DECAY_CHANNEL_PLAIN = 0, 1, 2
 GDN_MAX_STEPS = 16
 
@@ -63,6 +64,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_step_split.argtypes = [ctypes.POINTER(GdnShape), ctypes.POINTER(GdnStore), I32, I32, I32,
                                             I32, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.gdn_decode_step_split.restype = ctypes.c_int
+        L.gdn_decode_step_split_noalloc.argtypes = [ctypes.POINTER(GdnShape), ctypes.POINTER(GdnStore), I32, I32,
+                                                    I32, I32, P, P, P, P, P, P, P]
+        L.gdn_decode_step_split_noalloc.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -233,6 +237,26 @@ def decode_step_split(store: Store, t, n_split, shared_prep, merge, q, k, v, alp
                                      _ptr(alpha), _ptr(beta), _ptr(o), ws, ws_bytes, _stream(stream, store.device))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_decode_step_split")
+    return o
+
+
+def decode_step_split_noalloc(store: Store, t, n_split, shared_prep, merge, q, k, v, alpha, beta, o,
+                              stream=None):
+    """decode_step_split with the library's built-in scratch buffer instead of
+    a workspace (gdn_decode_step_split_noalloc): nothing is allocated, so the
+    output ``o`` [R,1,H,dv] FP32 must be given."""
+    R, H, dk, dv, dev = store.R, store.H, store.dk, store.dv, store.device
+    _check(q, "q", _BF16, (R, 1, store.Hk, dk), dev)
+    _check(k, "k", _BF16, (R, 1, store.Hk, dk), dev)
+    _check(v, "v", _BF16, (R, 1, H, dv), dev)
+    _check(alpha, "alpha", (torch.float32,), (R, 1, H, dk) if store.channel_decay else (R, 1, H), dev)
+    _check(beta, "beta", (torch.float32,), (R, 1, H), dev)
+    _check(o, "o", (torch.float32,), (R, 1, H, dv), dev)
+    rc = lib().gdn_decode_step_split_noalloc(ctypes.byref(store.shape), ctypes.byref(store.cstore), t, n_split,
+                                             int(bool(shared_prep)), int(bool(merge)), _ptr(q), _ptr(k), _ptr(v),
+                                             _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream, store.device))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_decode_step_split_noalloc")
     return o
 
 

@@ -66,6 +66,7 @@ const char* gdn_status_string(int status) {
     case GDN_EINVAL: return "invalid argument (null or misaligned pointer, index or size out of range)";
     case GDN_EUNSUPPORTED: return "unsupported head dims or decay kind";
     case GDN_EHIP: return "HIP kernel launch failed";
+    case GDN_ESCRATCH: return "larger than the built-in scratch buffer of the no-alloc entry point";
     default: return "unknown status";
   }
 }

@@ -40,7 +40,8 @@ def test_exports_every_header_function(L):
     names = B.header_functions()
     assert set(names) == {"gdn_beam_decode_step", "gdn_decode_merge_step", "gdn_materialize",
                           "gdn_log_merge", "gdn_status_string", "gdn_abi_version",
-                          "gdn_split_workspace_bytes", "gdn_decode_step_split"}
+                          "gdn_split_workspace_bytes", "gdn_decode_step_split",
+                          "gdn_decode_step_split_noalloc"}
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
@@ -51,7 +52,7 @@ def test_exports_every_header_function(L):
 
 def test_version_and_status_strings(L):
     assert L.gdn_abi_version() == 5
-    for s in (B.GDN_OK, B.GDN_EINVAL, B.GDN_EUNSUPPORTED, B.GDN_EHIP, 12345):
+    for s in (B.GDN_OK, B.GDN_EINVAL, B.GDN_EUNSUPPORTED, B.GDN_EHIP, B.GDN_ESCRATCH, 12345):
         assert isinstance(B.status_string(s), str) and B.status_string(s)
 
 
@@ -167,4 +168,21 @@ def test_split_validation(L):
     assert split(L, ws_bytes=need - 1) == E                   # too small
     assert split(L, st=store(rec_k=FAKE + 2)) == E
     assert split(L, sh=shape(W_max=1, decay_kind=7)) == U
+
+
+def test_noalloc_split_rejects_before_touching_the_gpu(L):
+    """The no-alloc entry point refuses a shape whose preparation would not fit
+    its built-in scratch buffer (and the split path's own errors) before any
+    HIP call."""
+    def call(sh, shared=1, n_split=2, st=None):
+        st = store() if st is None else st
+        return L.gdn_decode_step_split_noalloc(ctypes.byref(sh), ctypes.byref(st), 0, n_split, shared, 0, FAKE,
+                                               FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    per = (2 * 128 + 2 * 16 + 4) * 4
+    too_many = B.GDN_SPLIT_SCRATCH_BYTES // per + 1
+    assert call(shape(R=too_many, W_max=1, H=1)) == B.GDN_ESCRATCH
+    assert call(shape(R=too_many, W_max=1, H=1), shared=0, n_split=3) == B.GDN_EUNSUPPORTED
+    assert call(shape(W_max=4), shared=0) == B.GDN_EUNSUPPORTED
+    assert call(shape(R=0, W_max=1)) == B.GDN_EINVAL
+    assert call(shape(W_max=1), shared=0, st=store(S=FAKE + 8)) == B.GDN_EINVAL
 
