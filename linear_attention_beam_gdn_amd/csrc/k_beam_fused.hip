@@ -65,20 +65,25 @@
 // Clock stamps (measurement builds only, compiled with GDN_STAMPS): lane 0 of
 // consumer wave 0 of every workgroup records the real-time clock at kernel
 // entry, after each prologue barrier and after its last tile, and the XCD
-// and compute unit it ran on, into a per-workgroup row of a device array
-// that gdn_stamps_read copies out.  The product build records nothing.
+// and compute unit it ran on; the dot wave, consumer wave 0 and the DMA
+// waves add up the time they spend working and waiting in the tile loop.
+// All go into a per-workgroup row of a device array that gdn_stamps_read
+// copies out.  The product build records nothing.
 #ifdef GDN_STAMPS
 namespace gdn {
 namespace {
-constexpr int kStampWgs = 4096, kStamps = 8;
+constexpr int kStampWgs = 4096, kStamps = 16;
 __device__ unsigned long long g_stamps[kStampWgs * kStamps];
+__device__ __forceinline__ unsigned long long stamp_now() { return __builtin_amdgcn_s_memrealtime(); }
 }  // namespace
 }  // namespace gdn
-#define GDN_STAMP(i)                                                                  \
+// lane 0 of wave `wave` writes `val` into slot i of its workgroup's row
+#define GDN_STAMP_AT(i, wave, val)                                                    \
   do {                                                                                \
-    if (w == 0 && lane == 0 && blockIdx.x < kStampWgs)                                \
-      g_stamps[blockIdx.x * kStamps + (i)] = __builtin_amdgcn_s_memrealtime();        \
+    if (w == (wave) && lane == 0 && blockIdx.x < kStampWgs)                           \
+      g_stamps[blockIdx.x * kStamps + (i)] = (val);                                   \
   } while (0)
+#define GDN_STAMP(i) GDN_STAMP_AT(i, 0, stamp_now())
 #define GDN_STAMP_WHERE()                                                             \
   do {                                                                                \
     if (w == 0 && lane == 0 && blockIdx.x < kStampWgs) {                              \
@@ -88,6 +93,14 @@ __device__ unsigned long long g_stamps[kStampWgs * kStamps];
     }                                                                                 \
   } while (0)
 #else
+namespace gdn {
+namespace {
+__device__ __forceinline__ unsigned long long stamp_now() { return 0; }
+}  // namespace
+}  // namespace gdn
+#define GDN_STAMP_AT(i, wave, val) \
+  do {                             \
+  } while (0)
 #define GDN_STAMP(i) \
   do {               \
   } while (0)
@@ -299,19 +312,31 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     for (int p = 2 + dw; p < npro; p += 2) dma_tile(p);
     if (dw == 1) wait_tiles<G::OPT, 2>(later(1, npro - 1));  // tile 1 resident
     lds_barrier();                                          // 0
+    unsigned long long waited = 0;
     for (int i = 0; i < ntiles; ++i) {
       // buffer (i - 1) % NBUF was released at the last barrier
       const int p = i + G::NBUF - 1;
       if (p < ntiles && (p & 1) == dw) dma_tile(p);
       const int last = min(p, ntiles - 1);
+      const unsigned long long w0 = stamp_now();
       if (i + 2 < ntiles && ((i + 2) & 1) == dw) wait_tiles<G::OPT, 2>(later(i + 2, last));  // tile i + 2 resident
+      waited += stamp_now() - w0;
       lds_barrier();                                                                     // i + 1
     }
+    GDN_STAMP_AT(11 + dw, G::WDMA + dw, waited);
     return;
   }
 
   if (w == G::WDOT) {
     // ============================================================ dot wave
+    // keys of record depth j of tile p's beams from the record store
+    auto load_key = [&](int p, int j, u32x4* kj) {
+      const int posi = min(p * 16 + c, nb - 1);
+      const int slot = j < 3 ? (int)s_tab[posi][1 + j] : s_slot_hi[(j - 3) * kMaxChunkF + posi];
+      const uint16_t* key = a.rec_k + ((((size_t)j * a.R + r) * a.Wm + slot) * a.Hk + h / a.gq) * DK;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kj[s] = *reinterpret_cast<const u32x4*>(key + s * 32 + g * 8);
+    };
     auto dots = [&](int p) {
       uint8_t* buf = smem + (p % G::NBUF) * G::BUF;
       const float* sm = reinterpret_cast<const float*>(buf + G::OS);
@@ -334,18 +359,11 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
       constexpr int TG = T > G::TL ? T - G::TL : 1;
       float pqg[TG], pkg[TG];
       if constexpr (T > G::TL) {
-        const int posi = min(p * 16 + c, nb - 1);
-        auto load_key = [&](int j, u32x4* kj) {
-          const int slot = j < 3 ? (int)s_tab[posi][1 + j] : s_slot_hi[(j - 3) * kMaxChunkF + posi];
-          const uint16_t* key = a.rec_k + ((((size_t)j * a.R + r) * a.Wm + slot) * a.Hk + h / a.gq) * DK;
-#pragma unroll
-          for (int s = 0; s < KS; ++s) kj[s] = *reinterpret_cast<const u32x4*>(key + s * 32 + g * 8);
-        };
         u32x4 cur[KS], nxt[KS];
-        load_key(G::TL, cur);
+        load_key(p, G::TL, cur);
 #pragma unroll
         for (int j = G::TL; j < T; ++j) {
-          if (j + 1 < T) load_key(j + 1, nxt);
+          if (j + 1 < T) load_key(p, j + 1, nxt);
           float pq = 0.f, pk = 0.f;
 #pragma unroll
           for (int s = 0; s < KS; ++s)
@@ -396,12 +414,21 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     lds_barrier();  // P
     lds_barrier();  // S
     lds_barrier();  // A
+    const unsigned long long d0 = stamp_now();
     dots(0);
+    GDN_STAMP_AT(9, G::WDOT, stamp_now() - d0);
     lds_barrier();  // 0
+    unsigned long long busy = 0, at_barrier = 0;
     for (int i = 0; i < ntiles; ++i) {
+      const unsigned long long b0 = stamp_now();
       if (i + 1 < ntiles) dots(i + 1);
+      const unsigned long long b1 = stamp_now();
       lds_barrier();  // i + 1
+      busy += b1 - b0;
+      at_barrier += stamp_now() - b1;
     }
+    GDN_STAMP_AT(8, G::WDOT, busy);
+    GDN_STAMP_AT(13, G::WDOT, at_barrier);
     return;
   }
 
@@ -483,7 +510,9 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   lds_barrier();  // 0
   GDN_STAMP(5);
 
+  unsigned long long c_busy = 0, c_barrier = 0;
   for (int it = 0; it < ntiles; ++it) {
+    const unsigned long long c0 = stamp_now();
     f32x4 dcur[TT];
 #pragma unroll
     for (int j = 0; j < T; ++j) dcur[j] = dnext[j];
@@ -572,9 +601,14 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     const float at = *reinterpret_cast<const float*>(buf + G::OS + c * 4);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(at), w_a,
                                           (live && slice0 && w == G::NC - 1 && g == 0) ? ib * sa : kOutside, 0, 0);
+    const unsigned long long c1 = stamp_now();
     lds_barrier();  // it + 1
+    c_busy += c1 - c0;
+    c_barrier += stamp_now() - c1;
   }
   GDN_STAMP(6);
+  GDN_STAMP_AT(10, 0, c_busy);
+  GDN_STAMP_AT(14, 0, c_barrier);
 }
 
 template <int DK, int DV, int T>
@@ -665,10 +699,12 @@ int launch_beam_fused(const gdn_shape& sh, const gdn_store& st, int t, int Wt, c
 }  // namespace gdn
 
 #ifdef GDN_STAMPS
-// Measurement builds only: copy the first n_wg rows of clock stamps (8 per
-// workgroup: entry, barriers Q, P, S, A, 0, after the last tile, and
-// (XCD << 32 | hardware id)) to host memory, and report the real-time
-// clock's rate.
+// Measurement builds only: copy the first n_wg rows of clock stamps (16 per
+// workgroup: entry, barriers Q, P, S, A, 0, after the last tile, (XCD << 32 |
+// hardware id), then clock ticks: the dot wave's work over the loop and on
+// tile 0, consumer wave 0's work over the loop, the two DMA waves' waits,
+// the dot wave's and consumer wave 0's time at the loop's barriers, and one
+// spare) to host memory, and report the real-time clock's rate.
 extern "C" int gdn_stamps_read(unsigned long long* host, int n_wg) {
   if (host == nullptr || n_wg < 0 || n_wg > gdn::kStampWgs) return GDN_EINVAL;
   return hipMemcpyFromSymbol(host, HIP_SYMBOL(gdn::g_stamps), (size_t)n_wg * gdn::kStamps * 8, 0,

@@ -1,7 +1,7 @@
 """Where a headline decode launch spends its time: per-workgroup clock stamps.
 
-Runs the large-beam workload (8 requests x 512 beams, H = 32, d_k = d_v =
-128, four decode steps) on libgdnbeam_stamps.so, the library built with the
+Runs a beam workload (by default the large-beam one: 8 requests x 512 beams,
+H = 32, d_k = d_v = 128, four decode steps) on libgdnbeam_stamps.so, the library built with the
 fused kernel's clock stamps compiled in (lane 0 of one consumer wave per
 workgroup reads the 100 MHz real-time clock at entry, after each prologue
 barrier and after its last tile).  Each launch runs after a 1 GiB read-only
@@ -11,7 +11,7 @@ each phase boundary after the first workgroup's entry, the tile loop's
 length, the spread of the exits, and the time between the HIP events that no
 workgroup covers.
 
-    python -m linear_attention_beam_gdn_amd.measure.stamps [--reps N] [--out FILE]
+    python -m linear_attention_beam_gdn_amd.measure.stamps [--reps N] [--out FILE] [--workload NAME]
 """
 
 from __future__ import annotations
@@ -36,6 +36,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--out", default="")
+    ap.add_argument("--workload", default="gdn_large_beam",
+                    help="a scalar-decay beam workload whose chunks hold all its beams (one chunk per slice)")
     args = ap.parse_args()
 
     import torch
@@ -52,13 +54,14 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    w = configs.LARGE
+    w = configs.BY_NAME[args.workload]
+    nvs = w.dv // 128 if w.dv > 128 else 1  # value slices per (request, head)
     inp = w.inputs()
     steps = [B.upload(st, dev) for st in inp["steps"]]
-    store = B.Store(w.R, w.W, w.H, w.dk, w.dv, w.L, S=torch.from_numpy(inp["S0"]).to(dev))
+    store = B.Store(w.R, w.W, w.H, w.dk, w.dv, w.L, S=torch.from_numpy(inp["S0"]).to(dev), Hk=w.Hk)
     outs = [torch.empty(w.R, w.W, w.H, w.dv, dtype=torch.float32, device=dev) for _ in range(w.L)]
     stream = torch.cuda.current_stream()
-    n_wg = w.R * w.H  # one workgroup per (request, head) at this shape
+    n_wg = w.R * w.H * nvs  # one workgroup per (request, head, value slice) with every beam in one chunk
 
     def launch(t):
         d = steps[t]
@@ -74,7 +77,7 @@ def main():
     from linear_attention_beam_gdn_amd.measure import stream as S
 
     flush = S.ReadFlush(torch)
-    buf = np.zeros((n_wg, 8), np.uint64)
+    buf = np.zeros((n_wg, 16), np.uint64)
     rows = {t: [] for t in range(w.L)}
     for _ in range(args.reps):
         for t in range(w.L):
@@ -89,7 +92,8 @@ def main():
                 raise RuntimeError(f"gdn_stamps_read returned {rc}")
             rows[t].append((a.elapsed_time(b) * 1e3, buf.copy()))
 
-    lines = [f"Clock stamps of `k_beam_fused<128,128,t>` at `{w.name}` (8 x 512 beams, H = 32, d = 128), "
+    lines = [f"Clock stamps of `k_beam_fused<{w.dk},{w.dv},t>` at `{w.name}` ({w.R} x {w.W} beams, H = {w.H}, "
+             f"d_k = {w.dk}, d_v = {w.dv}; {n_wg} workgroups), "
              f"{args.reps} launches per step, each after a 1 GiB read-only cache-flushing sweep; real-time clock "
              f"{khz / 1e3:.0f} MHz; times in us after the first workgroup's entry, medians over "
              f"workgroups and launches.", ""]
@@ -115,6 +119,19 @@ def main():
         xcd = (st[:, :, 7] >> 32) & 0xF
         per = {int(x): float(np.median(rel[:, :, 6][xcd == x])) for x in np.unique(xcd)}
         xcd_rows.append((t, per))
+    lines += ["", "Work and waits inside the tile loop, us per tile (medians over workgroups and launches; "
+              f"{w.W // 16} tiles of 16 beams per workgroup): the dot wave forms tile i + 1's dot products and decay weights "
+              "while the consumers take tile i, and both then meet at a barrier; a DMA wave waits until the tile the "
+              "dot wave takes next has landed.", "",
+              "| step | dot wave: tile 0 (prologue) | dot wave: work per tile | dot wave: at barrier | "
+              "consumer wave 0: work per tile | consumer wave 0: at barrier | DMA wave 0: waiting | "
+              "DMA wave 1: waiting |", "|---|---|---|---|---|---|---|---|"]
+    for t in range(w.L):
+        st = np.stack([r[1] for r in rows[t]]).astype(np.int64)
+        nt = w.W // 16
+        f = lambda i, n: float(np.median(st[:, :, i])) * tick_us / n
+        lines.append(f"| {t} | {f(9, 1):.2f} | {f(8, nt - 1):.2f} | {f(13, nt):.2f} | {f(10, nt):.2f} | "
+                     f"{f(14, nt):.2f} | {f(11, nt):.2f} | {f(12, nt):.2f} |")
     lines += ["", "Median exit (last tile done) per XCD, us after the first entry:", "",
               "| step | " + " | ".join(f"XCD {x}" for x in sorted(xcd_rows[0][1])) + " |",
               "|---|" + "---|" * len(xcd_rows[0][1])]
