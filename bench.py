@@ -566,6 +566,25 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
 
+    # The same passes captured in a HIP graph and replayed (context: on this
+    # stack a replayed pass has so far been slower than the launches above).
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t, d in enumerate(steps):
+            B.decode_step(store, t, w.W, d.get("parent"), d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                          o=outs[t])
+    for _ in range(args.warmup):
+        graph.replay()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1)
+    del graph
+
     # What this GPU streams: the hand-written reference kernel at read:write
     # mixes from writes only to reads only (fully coalesced 16-byte accesses
     # over 2 GiB, best of several launch shapes and store kinds); the 1:1 mix
@@ -674,6 +693,7 @@ def main():
             "mfma_tflops": mfma_flops / mean_launch_s / 1e12,
             "mfma_frac_of_bf16_peak": mfma_flops / mean_launch_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         },
+        "value_graph_replay": beam_steps / (graph_ms * 1e-3),
         "cpu_baseline": cpu,
     }
     if not args.no_rows:

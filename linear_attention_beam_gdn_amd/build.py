@@ -3,7 +3,9 @@
 Every kernel source is compiled to an object in ``_build/`` (in parallel),
 then linked into ``linear_attention_beam_gdn_amd/libgdnbeam.so``.  Two
 measurement libraries are built beside it: ``libgdnbeam_stamps.so``, the same
-library with the headline kernel's clock stamps compiled in (GDN_STAMPS), and
+library with the headline kernel's clock stamps compiled in (GDN_STAMPS),
+``libgdnbeam_check.so``, the library with device-side parent-pointer checks
+(GDN_CHECK_PARENTS, include/gdn_beam_check.h), and
 ``measure/libgdnmeasure.so``, the streaming-rate reference kernels.  All HIP
 code is built with packed-FP32 instructions disabled.
 """
@@ -27,6 +29,9 @@ STAMPS_LIB = os.path.join(PKG, "libgdnbeam_stamps.so")
 MEASURE_SRC = os.path.join(PKG, "measure", "k_stream.hip")
 MEASURE_LIB = os.path.join(PKG, "measure", "libgdnmeasure.so")
 STAMPED = "k_beam_fused.hip"  # the source built a second time with GDN_STAMPS
+CHECK_LIB = os.path.join(PKG, "libgdnbeam_check.so")
+# the sources that read parent pointers (or own the counter), built again with GDN_CHECK_PARENTS
+CHECKED = ("abi.hip", "k_beam_decode.hip", "k_beam_fused.hip", "k_beam_fused_kda.hip")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -68,15 +73,20 @@ def build(verbose: bool = False, extra=()) -> str:
     stamped = os.path.join(CSRC, STAMPED)
     jobs = [(s, tuple(extra), "") for s in srcs]
     jobs.append((stamped, tuple(extra) + ("-DGDN_STAMPS",), "_stamps"))
+    checked = [os.path.join(CSRC, f) for f in CHECKED]
+    jobs += [(c, tuple(extra) + ("-DGDN_CHECK_PARENTS",), "_check") for c in checked]
     jobs.append((MEASURE_SRC, tuple(extra), ""))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         objs = list(ex.map(lambda j: _compile(*j), jobs))
-    prod = objs[:len(srcs)]
+    n = len(srcs)
+    prod = objs[:n]
     _link(prod, LIB)
-    _link([o for o, s in zip(prod, srcs) if s != stamped] + [objs[len(srcs)]], STAMPS_LIB)
+    _link([o for o, s in zip(prod, srcs) if s != stamped] + [objs[n]], STAMPS_LIB)
+    _link([o for o, s in zip(prod, srcs) if s not in checked] + objs[n + 1:n + 1 + len(checked)], CHECK_LIB)
     _link([objs[-1]], MEASURE_LIB)
     if verbose:
-        print(f"built {LIB} (and {os.path.basename(STAMPS_LIB)}, measure/{os.path.basename(MEASURE_LIB)})")
+        print(f"built {LIB} (and {os.path.basename(STAMPS_LIB)}, {os.path.basename(CHECK_LIB)}, "
+              f"measure/{os.path.basename(MEASURE_LIB)})")
     return LIB
 
 

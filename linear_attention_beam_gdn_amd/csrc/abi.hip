@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gdn_beam.h"
 #include "gdn_launch.h"
 
@@ -27,6 +29,29 @@ bool dims_supported(int dk, int dv, int decay_kind) {
 }  // namespace gdn
 
 namespace {
+
+#ifdef GDN_CHECK_PARENTS
+// Parent-check builds only: one device counter of parent pointers found
+// outside [0, W_max) by the beam decode kernels, per GPU; its address is
+// looked up once per device.
+__device__ int g_bad_parents;
+constexpr int kMaxDevices = 64;
+std::once_flag g_bad_once[kMaxDevices];
+int* g_bad_ptr[kMaxDevices];
+int* bad_parents_on(hipStream_t stream) {
+  hipDevice_t dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_bad_once[dev], [dev] {
+    int cur = -1;
+    const bool sw = hipGetDevice(&cur) == hipSuccess && cur != dev;
+    if (sw && hipSetDevice(dev) != hipSuccess) return;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_bad_parents)) == hipSuccess) g_bad_ptr[dev] = static_cast<int*>(p);
+    if (sw) (void)hipSetDevice(cur);
+  });
+  return g_bad_ptr[dev];
+}
+#endif
 
 bool aligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -85,8 +110,11 @@ int gdn_beam_decode_step(const gdn_shape* shape, const gdn_store* store, int32_t
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 16) ||
       !aligned(beta, 16) || !aligned(o, 16))
     return GDN_EINVAL;
-  const gdn::StepIO io{parent, q, k, v, alpha, beta, o};
+  gdn::StepIO io{parent, q, k, v, alpha, beta, o};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+#ifdef GDN_CHECK_PARENTS
+  io.bad_parents = bad_parents_on(s);
+#endif
   // one beam per request takes the sequence kernel where it is built; the
   // wider geometries run it through the beam kernel (the same step at W = 1)
   if (shape->W_max == 1 && gdn::seq_dims_supported(shape->dk, shape->dv))
@@ -159,3 +187,22 @@ int gdn_log_merge(const gdn_shape* shape, const gdn_store* store, int32_t n_rec,
 }
 
 }  // extern "C"
+
+#ifdef GDN_CHECK_PARENTS
+// Parent-check builds only (libgdnbeam_check.so): the number of parent
+// pointers outside [0, W_max) that beam decode steps on this stream's GPU
+// have met since the last call, which resets it.  Synchronises the stream.
+// Returns a negative status if the counter cannot be read.
+extern "C" int gdn_debug_bad_parents(void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int* p = bad_parents_on(s);
+  if (p == nullptr) return GDN_EHIP;
+  int n = 0;
+  if (hipMemcpyAsync(&n, p, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess) return GDN_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return GDN_EHIP;
+  const int zero = 0;
+  if (hipMemcpyAsync(p, &zero, sizeof(int), hipMemcpyHostToDevice, s) != hipSuccess) return GDN_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return GDN_EHIP;
+  return n;
+}
+#endif

@@ -15,6 +15,7 @@ struct BeamArgs {
   float* rec_alpha;
   int32_t* anc;
   const int32_t* parent;
+  int* bad_parents;  // parent-check builds: count of parents outside [0, W_max)
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
@@ -40,6 +41,19 @@ template <int DK>
 __device__ __forceinline__ bool klive(int g) {
   if constexpr (DK == 16) return g < 2;  // lane groups 2, 3 feed zero padding
   else return true;
+}
+
+// Parent-check builds (GDN_CHECK_PARENTS): count a parent pointer outside
+// [0, W_max) (the kernels clamp it into that range, so no access leaves the
+// store; the result for that beam is then meaningless).  One caller per
+// (request, beam) counts, so the total is the number of bad pointers.
+__device__ __forceinline__ void check_parent(const BeamArgs& a, int parent) {
+#ifdef GDN_CHECK_PARENTS
+  if ((parent < 0 || parent >= a.Wm) && a.bad_parents != nullptr) atomicAdd(a.bad_parents, 1);
+#else
+  (void)a;
+  (void)parent;
+#endif
 }
 
 __device__ __forceinline__ void load_f32x8(const float* p, float* x) {

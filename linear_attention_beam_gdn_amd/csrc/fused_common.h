@@ -123,7 +123,10 @@ __device__ __forceinline__ void build_schedule(const BeamArgs& a, int r, bool an
   wait_vm<0>();
   mid();
 #pragma unroll
-  for (int qi = 0; qi < QMAX; ++qi) slot[qi][TT - 1] = clampi(slot[qi][TT - 1], 0, a.Wm - 1);
+  for (int qi = 0; qi < QMAX; ++qi) {
+    if (anc_writer && lane + 64 * qi < nb) check_parent(a, slot[qi][TT - 1]);
+    slot[qi][TT - 1] = clampi(slot[qi][TT - 1], 0, a.Wm - 1);
+  }
   // Ancestry (§3.3): h_t(b, T-1) = parent, h_t(b, j) = h_{T-1}(parent, j);
   // the parent's position in the previous step's order is the sort key (its
   // own slot when the previous step is the first).

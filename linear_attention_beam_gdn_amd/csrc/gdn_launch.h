@@ -17,6 +17,9 @@ struct StepIO {
   const float* alpha;
   const float* beta;
   float* o;
+  // parent-check builds (GDN_CHECK_PARENTS) only: device counter of parent
+  // pointers found outside [0, W_max); null otherwise
+  int* bad_parents = nullptr;
 };
 
 // (d_k, d_v) pairs built for a decay kind, and those of the sequence kernel

@@ -108,7 +108,11 @@ __global__ __launch_bounds__((BeamGeom<DK, DV, CH>::NW * 64)) void k_beam_decode
 
     // ---- ancestry (§3.3): parent slot and the parent's own ancestry row
     int par = 0;
-    if (t > 0 && valid) par = clampi(a.parent[(size_t)r * a.Wt + b], 0, a.Wm - 1);
+    if (t > 0 && valid) {
+      const int raw = a.parent[(size_t)r * a.Wt + b];
+      if (anc_writer) check_parent(a, raw);
+      par = clampi(raw, 0, a.Wm - 1);
+    }
     const int32_t* prow = a.anc + (((size_t)(t > 0 ? t - 1 : 0) * a.R + r) * a.Wm + par) * a.L;
     auto slot_at = [&](int j) -> int {
       if (!valid) return 0;
@@ -352,6 +356,7 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO
   a.rec_alpha = st.rec_alpha;
   a.anc = st.anc;
   a.parent = io.parent;
+  a.bad_parents = io.bad_parents;
   a.q = io.q;
   a.k = io.k;
   a.v = io.v;

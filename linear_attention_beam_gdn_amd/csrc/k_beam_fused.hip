@@ -621,6 +621,7 @@ int launch(const gdn_shape& sh, const gdn_store& st, int Wt, const StepIO& io, h
   a.rec_alpha = st.rec_alpha;
   a.anc = st.anc;
   a.parent = io.parent;
+  a.bad_parents = io.bad_parents;
   a.q = io.q;
   a.k = io.k;
   a.v = io.v;

@@ -186,3 +186,25 @@ def test_noalloc_split_rejects_before_touching_the_gpu(L):
     assert call(shape(R=0, W_max=1)) == B.GDN_EINVAL
     assert call(shape(W_max=1), shared=0, st=store(S=FAKE + 8)) == B.GDN_EINVAL
 
+
+
+def test_parent_check_library_exports():
+    """libgdnbeam_check.so exports everything gdn_beam.h declares plus the
+    counter reader gdn_beam_check.h declares."""
+    import os
+    import re
+
+    from linear_attention_beam_gdn_amd import build
+
+    out = subprocess.run(["nm", "-D", "--defined-only", build.CHECK_LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    hdr = open(os.path.join(os.path.dirname(B.HEADER), "gdn_beam_check.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    extra = re.findall(r"^\s*\w+\s+(gdn_\w+)\s*\(", hdr, flags=re.M)
+    assert extra == ["gdn_debug_bad_parents"]
+    for n in B.header_functions() + extra:
+        assert n in exported, n
+    prod = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True,
+                          check=True).stdout
+    assert "gdn_debug_bad_parents" not in prod  # the product build has no counter
