@@ -504,6 +504,8 @@ def main():
                     help="skip the other path rows (channel decay, bounded log, materialise)")
     ap.add_argument("--rows", default="",
                     help="comma-separated subset of the rows to run (default: all of them)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the streaming-rate reference kernels (for profiler runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the warm-up, run a plain device copy of this many MiB three times "
                          "(a known-size reference for HBM byte counters)")
@@ -591,8 +593,8 @@ def main():
     # is the device copy.  torch's own copy kernel is timed beside it.
     from linear_attention_beam_gdn_amd.measure import stream as S
 
-    stream_rates = S.all_rates(torch, stream)
-    copy_gbps = stream_rates["r1w1"]["GBps"]
+    stream_rates = {} if args.no_ceilings else S.all_rates(torch, stream)
+    copy_gbps = stream_rates["r1w1"]["GBps"] if stream_rates else float("nan")
     src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -643,7 +645,7 @@ def main():
                    for t in range(w.L)]
     read_frac = [1.0 - wb / sb for wb, sb in zip(write_bytes, step_bytes)]
     _STREAM_RATES.update(stream_rates)
-    mix_rates = [mix_rate(f) for f in read_frac]
+    mix_rates = [mix_rate(f) for f in read_frac] if stream_rates else [float("nan")] * len(read_frac)
     mix_s = sum(b_ / (r * 1e9) for b_, r in zip(step_bytes, mix_rates))
     mfma_flops = 3 * 2 * 2 * w.dk * w.dv * w.R * w.W * w.H
     mean_launch_s = float(launch_ms.mean()) * 1e-3
