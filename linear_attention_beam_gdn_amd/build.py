@@ -3,7 +3,7 @@
 Every kernel source is compiled to an object in ``_build/`` (in parallel),
 then linked into ``linear_attention_beam_gdn_amd/libgdnbeam.so``.  Two
 measurement libraries are built beside it: ``libgdnbeam_stamps.so``, the same
-library with the headline kernel's clock stamps compiled in (GDN_STAMPS),
+library with the fused kernels' clock stamps compiled in (GDN_STAMPS),
 ``libgdnbeam_check.so``, the library with device-side parent-pointer checks
 (GDN_CHECK_PARENTS, include/gdn_beam_check.h), and
 ``measure/libgdnmeasure.so``, the streaming-rate reference kernels.  All HIP
@@ -28,7 +28,7 @@ LIB = os.path.join(PKG, "libgdnbeam.so")
 STAMPS_LIB = os.path.join(PKG, "libgdnbeam_stamps.so")
 MEASURE_SRC = os.path.join(PKG, "measure", "k_stream.hip")
 MEASURE_LIB = os.path.join(PKG, "measure", "libgdnmeasure.so")
-STAMPED = "k_beam_fused.hip"  # the source built a second time with GDN_STAMPS
+STAMPED = ("k_beam_fused.hip", "k_beam_fused_kda.hip")  # the sources built a second time with GDN_STAMPS
 CHECK_LIB = os.path.join(PKG, "libgdnbeam_check.so")
 # the sources that read parent pointers (or own the counter), built again with GDN_CHECK_PARENTS
 CHECKED = ("abi.hip", "k_beam_decode.hip", "k_beam_fused.hip", "k_beam_fused_kda.hip")
@@ -70,19 +70,19 @@ def _link(objs, out: str) -> None:
 def build(verbose: bool = False, extra=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    stamped = os.path.join(CSRC, STAMPED)
-    jobs = [(s, tuple(extra), "") for s in srcs]
-    jobs.append((stamped, tuple(extra) + ("-DGDN_STAMPS",), "_stamps"))
+    stamped = [os.path.join(CSRC, f) for f in STAMPED]
     checked = [os.path.join(CSRC, f) for f in CHECKED]
+    jobs = [(s, tuple(extra), "") for s in srcs]
+    jobs += [(st, tuple(extra) + ("-DGDN_STAMPS",), "_stamps") for st in stamped]
     jobs += [(c, tuple(extra) + ("-DGDN_CHECK_PARENTS",), "_check") for c in checked]
     jobs.append((MEASURE_SRC, tuple(extra), ""))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         objs = list(ex.map(lambda j: _compile(*j), jobs))
-    n = len(srcs)
+    n, ns, nc = len(srcs), len(stamped), len(checked)
     prod = objs[:n]
     _link(prod, LIB)
-    _link([o for o, s in zip(prod, srcs) if s != stamped] + [objs[n]], STAMPS_LIB)
-    _link([o for o, s in zip(prod, srcs) if s not in checked] + objs[n + 1:n + 1 + len(checked)], CHECK_LIB)
+    _link([o for o, s in zip(prod, srcs) if s not in stamped] + objs[n:n + ns], STAMPS_LIB)
+    _link([o for o, s in zip(prod, srcs) if s not in checked] + objs[n + ns:n + ns + nc], CHECK_LIB)
     _link([objs[-1]], MEASURE_LIB)
     if verbose:
         print(f"built {LIB} (and {os.path.basename(STAMPS_LIB)}, {os.path.basename(CHECK_LIB)}, "

@@ -62,52 +62,12 @@
 // 1 KiB access, free of bank conflicts.
 #include "fused_common.h"
 
-// Clock stamps (measurement builds only, compiled with GDN_STAMPS): lane 0 of
-// consumer wave 0 of every workgroup records the real-time clock at kernel
-// entry, after each prologue barrier and after its last tile, and the XCD
-// and compute unit it ran on; the dot wave, consumer wave 0 and the DMA
-// waves add up the time they spend working and waiting in the tile loop.
-// All go into a per-workgroup row of a device array that gdn_stamps_read
-// copies out.  The product build records nothing.
-#ifdef GDN_STAMPS
-namespace gdn {
-namespace {
-constexpr int kStampWgs = 4096, kStamps = 16;
-__device__ unsigned long long g_stamps[kStampWgs * kStamps];
-__device__ __forceinline__ unsigned long long stamp_now() { return __builtin_amdgcn_s_memrealtime(); }
-}  // namespace
-}  // namespace gdn
-// lane 0 of wave `wave` writes `val` into slot i of its workgroup's row
-#define GDN_STAMP_AT(i, wave, val)                                                    \
-  do {                                                                                \
-    if (w == (wave) && lane == 0 && blockIdx.x < kStampWgs)                           \
-      g_stamps[blockIdx.x * kStamps + (i)] = (val);                                   \
-  } while (0)
-#define GDN_STAMP(i) GDN_STAMP_AT(i, 0, stamp_now())
-#define GDN_STAMP_WHERE()                                                             \
-  do {                                                                                \
-    if (w == 0 && lane == 0 && blockIdx.x < kStampWgs) {                              \
-      const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xF;           \
-      const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);                  \
-      g_stamps[blockIdx.x * kStamps + 7] = ((unsigned long long)xcc << 32) | hw;      \
-    }                                                                                 \
-  } while (0)
-#else
-namespace gdn {
-namespace {
-__device__ __forceinline__ unsigned long long stamp_now() { return 0; }
-}  // namespace
-}  // namespace gdn
-#define GDN_STAMP_AT(i, wave, val) \
-  do {                             \
-  } while (0)
-#define GDN_STAMP(i) \
-  do {               \
-  } while (0)
-#define GDN_STAMP_WHERE() \
-  do {                    \
-  } while (0)
-#endif
+#include "stamps.h"
+
+// Clock stamps (GDN_STAMPS builds): consumer wave 0 stamps kernel entry,
+// each prologue barrier and its last tile, and where it ran; the dot wave,
+// consumer wave 0 and the DMA waves add up the time they spend working and
+// waiting in the tile loop.
 
 namespace gdn {
 namespace {
@@ -700,19 +660,13 @@ int launch_beam_fused(const gdn_shape& sh, const gdn_store& st, int t, int Wt, c
 }  // namespace gdn
 
 #ifdef GDN_STAMPS
-// Measurement builds only: copy the first n_wg rows of clock stamps (16 per
-// workgroup: entry, barriers Q, P, S, A, 0, after the last tile, (XCD << 32 |
-// hardware id), then clock ticks: the dot wave's work over the loop and on
-// tile 0, consumer wave 0's work over the loop, the two DMA waves' waits,
-// the dot wave's and consumer wave 0's time at the loop's barriers, and one
-// spare) to host memory, and report the real-time clock's rate.
-extern "C" int gdn_stamps_read(unsigned long long* host, int n_wg) {
-  if (host == nullptr || n_wg < 0 || n_wg > gdn::kStampWgs) return GDN_EINVAL;
-  return hipMemcpyFromSymbol(host, HIP_SYMBOL(gdn::g_stamps), (size_t)n_wg * gdn::kStamps * 8, 0,
-                             hipMemcpyDeviceToHost) == hipSuccess
-             ? GDN_OK
-             : GDN_EHIP;
-}
+// Measurement builds only: rows of 16 stamps per workgroup (entry, barriers
+// Q, P, S, A, 0, after the last tile, (XCD << 32 | hardware id), then clock
+// ticks: the dot wave's work over the loop and on tile 0, consumer wave 0's
+// work over the loop, the two DMA waves' waits, the dot wave's and consumer
+// wave 0's time at the loop's barriers, and one spare), and the real-time
+// clock's rate.
+GDN_STAMPS_READER(gdn_stamps_read)
 extern "C" int gdn_stamps_clock_khz(void) {
   int dev = 0, khz = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;

@@ -47,6 +47,13 @@
 // q|k rows and decay vector.
 #include "fused_common.h"
 
+#include "stamps.h"
+
+// Clock stamps (GDN_STAMPS builds): consumer wave 0 stamps kernel entry,
+// each prologue barrier and its last tile, and where it ran; consumer waves
+// 0 and NC - 1 add up their preparation, their finishing work and their
+// waits at the loop's barriers, the DMA waves their waits for tiles.
+
 namespace gdn {
 namespace {
 
@@ -283,17 +290,23 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     for (int p = 2 + dw; p < npro; p += 2) dma_tile(p);
     if (dw == 1) wait_tiles<G::OPT, 2>(later(1, npro - 1));  // tile 1 resident
     lds_barrier();                                          // 0
+    unsigned long long waited = 0;
     for (int i = 0; i < ntiles; ++i) {
       const int p = i + G::NBUF - 1;  // into the buffer released at the last barrier
       if (p < ntiles && (p & 1) == dw) dma_tile(p);
       const int last = min(p, ntiles - 1);
+      const unsigned long long w0 = stamp_now();
       if (i + 2 < ntiles && ((i + 2) & 1) == dw) wait_tiles<G::OPT, 2>(later(i + 2, last));  // tile i + 2 resident
+      waited += stamp_now() - w0;
       lds_barrier();                                                                     // i + 1
     }
+    GDN_STAMP_AT(11 + dw, G::WDMA + dw, waited);
     return;
   }
 
   // ============================================================ consumers
+  GDN_STAMP(0);
+  GDN_STAMP_WHERE();
   // record-store windows over the chunk's beams (appends at step T)
   const size_t rec0 = (((size_t)T * a.R + r) * a.Wm + b_begin) * a.H + h;
   const int sk = a.Hk * DK * 2, sa = a.H * DK * 4;  // bytes between beams
@@ -416,6 +429,7 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     }
   }
   if (T > 0) lds_barrier();  // Q
+  GDN_STAMP(1);
   // this lane's first value row in row block rb: row0 + 16 rb
   const int row0 = vs0 + w * NRB * 16 + 4 * g;
   const int so = a.H * DV * 4;
@@ -444,9 +458,11 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   };
 
   lds_barrier();  // P
+  GDN_STAMP(2);
   f32x4 dnext[TT][NRB];
   load_deltas(0, dnext);
   lds_barrier();  // S: S0 staged
+  GDN_STAMP(3);
   u32x4 As[NRB][KS][2];
   if constexpr (G::S0_LDS) {
     const float* S = reinterpret_cast<const float*>(smem + G::OS0);
@@ -466,10 +482,14 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       for (int s = 0; s < KS; ++s) split_planes<2>(s0x[rb][s], As[rb][s]);
   }
   lds_barrier();  // A: tile 0 resident
+  GDN_STAMP(4);
   prep(0);
   lds_barrier();  // 0
+  GDN_STAMP(5);
 
+  unsigned long long c_prep = 0, c_fin = 0, c_bar = 0;
   for (int it = 0; it < ntiles; ++it) {
+    const unsigned long long c0 = stamp_now();
     // Double-buffered: this tile's update vectors move to dcur and the next
     // tile's are loaded at once.  Otherwise each row block's next update
     // vectors are loaded into dnext right after the block has used them
@@ -488,6 +508,7 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     // this launch targets it any more), writes only there, and its appends
     // fall outside the store windows.
     prep(it + 1);
+    const unsigned long long c1 = stamp_now();
 
     const uint8_t* buf = smem + (it % G::NBUF) * G::BUF;
     u32x4 bh[KS], bl[KS];
@@ -550,8 +571,18 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, side ? off : kOutside, 0, 0);
       if constexpr (!DBUF) load_deltas(it + 1, dnext, rb, rb + 1);
     }
+    const unsigned long long c2 = stamp_now();
     lds_barrier();  // it + 1
+    c_prep += c1 - c0;
+    c_fin += c2 - c1;
+    c_bar += stamp_now() - c2;
   }
+  GDN_STAMP(6);
+  GDN_STAMP_AT(8, 0, c_prep);
+  GDN_STAMP_AT(9, 0, c_fin);
+  GDN_STAMP_AT(10, 0, c_bar);
+  GDN_STAMP_AT(13, G::NC - 1, c_prep + c_fin);
+  GDN_STAMP_AT(14, G::NC - 1, c_bar);
 }
 
 template <int DK, int DV, int T>
@@ -620,3 +651,12 @@ int launch_beam_fused_kda(const gdn_shape& sh, const gdn_store& st, int t, int W
 }
 
 }  // namespace gdn
+
+#ifdef GDN_STAMPS
+// Measurement builds only: rows of 16 stamps per workgroup (entry, barriers
+// Q, P, S, A, 0, after the last tile, (XCD << 32 | hardware id), then clock
+// ticks over the tile loop: consumer wave 0's preparation, finishing work and
+// time at the barriers, the two DMA waves' waits, consumer wave NC - 1's work
+// and time at the barriers, and one spare).
+GDN_STAMPS_READER(gdn_kda_stamps_read)
+#endif

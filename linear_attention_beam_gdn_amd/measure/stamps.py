@@ -1,10 +1,11 @@
 """Where a headline decode launch spends its time: per-workgroup clock stamps.
 
 Runs a beam workload (by default the large-beam one: 8 requests x 512 beams,
-H = 32, d_k = d_v = 128, four decode steps) on libgdnbeam_stamps.so, the library built with the
-fused kernel's clock stamps compiled in (lane 0 of one consumer wave per
-workgroup reads the 100 MHz real-time clock at entry, after each prologue
-barrier and after its last tile).  Each launch runs after a 1 GiB read-only
+H = 32, d_k = d_v = 128, four decode steps; or any scalar- or channel-decay
+beam workload whose chunks hold all its beams) on libgdnbeam_stamps.so, the
+library built with the fused kernels' clock stamps compiled in (lane 0 of one
+consumer wave per workgroup reads the 100 MHz real-time clock at entry, after
+each prologue barrier and after its last tile).  Each launch runs after a 1 GiB read-only
 sweep that evicts the Infinity Cache, between HIP events on the launch
 stream, as the benchmark times it.  Prints a markdown summary: per step, the median time of
 each phase boundary after the first workgroup's entry, the tile loop's
@@ -29,7 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 NAMES = ["entry", "Q (schedule inputs in)", "P (schedule built)", "S (S0 staged)", "A (tile 0 in)",
-         "loop start (dots of tile 0)", "last tile done"]
+         "loop start (tile 0 prepared)", "last tile done"]
 
 
 def main():
@@ -37,7 +38,7 @@ def main():
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--out", default="")
     ap.add_argument("--workload", default="gdn_large_beam",
-                    help="a scalar-decay beam workload whose chunks hold all its beams (one chunk per slice)")
+                    help="a beam workload whose chunks hold all its beams (one chunk per slice)")
     args = ap.parse_args()
 
     import torch
@@ -47,18 +48,28 @@ def main():
 
     B.LIB_PATH = build.STAMPS_LIB
     L = B.lib()
-    L.gdn_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_int]
-    L.gdn_stamps_read.restype = ctypes.c_int
+    w = configs.BY_NAME[args.workload]
+    kda = w.channel_decay
+    read = L.gdn_kda_stamps_read if kda else L.gdn_stamps_read
+    read.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    read.restype = ctypes.c_int
     L.gdn_stamps_clock_khz.argtypes = []
     L.gdn_stamps_clock_khz.restype = ctypes.c_int
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    w = configs.BY_NAME[args.workload]
-    nvs = w.dv // 128 if w.dv > 128 else 1  # value slices per (request, head)
+    # value slices per (request, head): 128 value rows each, or 256 for
+    # channel decay with d_v >= 256 and chains of at most three records
+    nvs = w.dv // 128 if w.dv > 128 else 1
+    if kda and w.dv >= 256:
+        if w.L > 4:
+            raise SystemExit("channel decay at d_v >= 256: the slice width changes past t = 3; use L <= 4")
+        nvs = w.dv // 256
+    tb = 8 if kda else 16  # beams per tile
     inp = w.inputs()
     steps = [B.upload(st, dev) for st in inp["steps"]]
-    store = B.Store(w.R, w.W, w.H, w.dk, w.dv, w.L, S=torch.from_numpy(inp["S0"]).to(dev), Hk=w.Hk)
+    store = B.Store(w.R, w.W, w.H, w.dk, w.dv, w.L, S=torch.from_numpy(inp["S0"]).to(dev), Hk=w.Hk,
+                    channel_decay=kda)
     outs = [torch.empty(w.R, w.W, w.H, w.dv, dtype=torch.float32, device=dev) for _ in range(w.L)]
     stream = torch.cuda.current_stream()
     n_wg = w.R * w.H * nvs  # one workgroup per (request, head, value slice) with every beam in one chunk
@@ -87,12 +98,13 @@ def main():
             launch(t)
             b.record(stream)
             torch.cuda.synchronize()
-            rc = L.gdn_stamps_read(buf.ctypes.data, n_wg)
+            rc = read(buf.ctypes.data, n_wg)
             if rc != 0:
                 raise RuntimeError(f"gdn_stamps_read returned {rc}")
             rows[t].append((a.elapsed_time(b) * 1e3, buf.copy()))
 
-    lines = [f"Clock stamps of `k_beam_fused<{w.dk},{w.dv},t>` at `{w.name}` ({w.R} x {w.W} beams, H = {w.H}, "
+    kname = "k_beam_fused_kda" if kda else "k_beam_fused"
+    lines = [f"Clock stamps of `{kname}<{w.dk},{w.dv},t>` at `{w.name}` ({w.R} x {w.W} beams, H = {w.H}, "
              f"d_k = {w.dk}, d_v = {w.dv}; {n_wg} workgroups), "
              f"{args.reps} launches per step, each after a 1 GiB read-only cache-flushing sweep; real-time clock "
              f"{khz / 1e3:.0f} MHz; times in us after the first workgroup's entry, medians over "
@@ -119,19 +131,33 @@ def main():
         xcd = (st[:, :, 7] >> 32) & 0xF
         per = {int(x): float(np.median(rel[:, :, 6][xcd == x])) for x in np.unique(xcd)}
         xcd_rows.append((t, per))
-    lines += ["", "Work and waits inside the tile loop, us per tile (medians over workgroups and launches; "
-              f"{w.W // 16} tiles of 16 beams per workgroup): the dot wave forms tile i + 1's dot products and decay weights "
-              "while the consumers take tile i, and both then meet at a barrier; a DMA wave waits until the tile the "
-              "dot wave takes next has landed.", "",
-              "| step | dot wave: tile 0 (prologue) | dot wave: work per tile | dot wave: at barrier | "
-              "consumer wave 0: work per tile | consumer wave 0: at barrier | DMA wave 0: waiting | "
-              "DMA wave 1: waiting |", "|---|---|---|---|---|---|---|---|"]
-    for t in range(w.L):
-        st = np.stack([r[1] for r in rows[t]]).astype(np.int64)
-        nt = w.W // 16
-        f = lambda i, n: float(np.median(st[:, :, i])) * tick_us / n
-        lines.append(f"| {t} | {f(9, 1):.2f} | {f(8, nt - 1):.2f} | {f(13, nt):.2f} | {f(10, nt):.2f} | "
-                     f"{f(14, nt):.2f} | {f(11, nt):.2f} | {f(12, nt):.2f} |")
+    nt = w.W // tb
+    if kda:
+        lines += ["", "Work and waits inside the tile loop, us per tile (medians over workgroups and launches; "
+                  f"{nt} tiles of {tb} beams per workgroup): each consumer wave prepares its share of tile i + 1 (probes, "
+                  "record weights, appends), then finishes tile i (matrix-core products, replay, stores), and all meet "
+                  "at a barrier; a DMA wave waits until the tile prepared next has landed.", "",
+                  "| step | consumer wave 0: preparation | consumer wave 0: finishing | consumer wave 0: at barrier | "
+                  "last consumer wave: work | last consumer wave: at barrier | DMA wave 0: waiting | "
+                  "DMA wave 1: waiting |", "|---|---|---|---|---|---|---|---|"]
+        for t in range(w.L):
+            st = np.stack([r[1] for r in rows[t]]).astype(np.int64)
+            f = lambda i: float(np.median(st[:, :, i])) * tick_us / nt
+            lines.append(f"| {t} | {f(8):.2f} | {f(9):.2f} | {f(10):.2f} | {f(13):.2f} | {f(14):.2f} | "
+                         f"{f(11):.2f} | {f(12):.2f} |")
+    else:
+        lines += ["", "Work and waits inside the tile loop, us per tile (medians over workgroups and launches; "
+                  f"{nt} tiles of {tb} beams per workgroup): the dot wave forms tile i + 1's dot products and decay "
+                  "weights while the consumers take tile i, and both then meet at a barrier; a DMA wave waits until "
+                  "the tile the dot wave takes next has landed.", "",
+                  "| step | dot wave: tile 0 (prologue) | dot wave: work per tile | dot wave: at barrier | "
+                  "consumer wave 0: work per tile | consumer wave 0: at barrier | DMA wave 0: waiting | "
+                  "DMA wave 1: waiting |", "|---|---|---|---|---|---|---|---|"]
+        for t in range(w.L):
+            st = np.stack([r[1] for r in rows[t]]).astype(np.int64)
+            f = lambda i, n: float(np.median(st[:, :, i])) * tick_us / n
+            lines.append(f"| {t} | {f(9, 1):.2f} | {f(8, nt - 1):.2f} | {f(13, nt):.2f} | {f(10, nt):.2f} | "
+                         f"{f(14, nt):.2f} | {f(11, nt):.2f} | {f(12, nt):.2f} |")
     lines += ["", "Median exit (last tile done) per XCD, us after the first entry:", "",
               "| step | " + " | ".join(f"XCD {x}" for x in sorted(xcd_rows[0][1])) + " |",
               "|---|" + "---|" * len(xcd_rows[0][1])]

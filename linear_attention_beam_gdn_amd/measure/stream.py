@@ -109,3 +109,48 @@ class ReadFlush:
         if rc != 0:
             raise RuntimeError(f"gdn_stream_run(1, 0) returned {rc}")
 
+
+
+def empty_launch_us(torch, stream, reps=20, workgroups=256):
+    """Median time between HIP events around a launch that does almost
+    nothing (256 workgroups reading 16 KiB), each after the read-only sweep:
+    the floor that an event-timed launch of any kernel pays."""
+    flush = ReadFlush(torch)
+    src = torch.zeros(4 * UNIT // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty(1024, dtype=torch.float32, device="cuda")
+    h = ctypes.c_void_p(stream.cuda_stream)
+    times = []
+    for _ in range(reps):
+        flush(stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        rc = lib().gdn_stream_run(1, 0, src.data_ptr(), dst.data_ptr(), 4, workgroups, 0, h)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise RuntimeError(f"gdn_stream_run(1, 0) returned {rc}")
+        times.append(a.elapsed_time(b) * 1e3)
+    del flush
+    return sorted(times)[len(times) // 2]
+
+
+def main():
+    """Prints the best rate of every mix as a markdown table, and the
+    event-timed floor of a launch."""
+    import torch
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    rates = all_rates(torch, stream)
+    print("| mix (read:write) | read fraction | best GB/s | of 8 TB/s | workgroups | non-temporal stores |")
+    print("|---|---|---|---|---|---|")
+    for key, v in rates.items():
+        rd, wr = key[1:].split("w")
+        print(f"| {rd}:{wr} | {v['read_fraction']:.3f} | {v['GBps']:.0f} | {v['GBps'] / 8000:.3f} | "
+              f"{v['workgroups']} | {'yes' if v['nontemporal_stores'] else 'no'} |", flush=True)
+    print(f"\nA launch of 256 workgroups reading 16 KiB, between HIP events after the read-only sweep: "
+          f"{empty_launch_us(torch, stream):.1f} us (median of 20).", flush=True)
+
+
+if __name__ == "__main__":
+    main()

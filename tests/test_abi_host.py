@@ -208,3 +208,22 @@ def test_parent_check_library_exports():
     prod = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True,
                           check=True).stdout
     assert "gdn_debug_bad_parents" not in prod  # the product build has no counter
+
+
+def test_stamps_library_exports():
+    """libgdnbeam_stamps.so exports everything gdn_beam.h declares plus the
+    clock-stamp readers of the two fused kernels; the product library has
+    none of them."""
+    from linear_attention_beam_gdn_amd import build
+
+    def exported(path):
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+        return {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+
+    st = exported(build.STAMPS_LIB)
+    readers = ["gdn_stamps_read", "gdn_kda_stamps_read", "gdn_stamps_clock_khz"]
+    for n in B.header_functions() + readers:
+        assert n in st, n
+    prod = exported(B.LIB_PATH)
+    for n in readers:
+        assert n not in prod, n
