@@ -254,6 +254,19 @@ def beam_row(B, torch, dev, stream, wl, reps):
            "launch_us": us, **{k: v for k, v in _bw(tot_b / wl.L, tot_us / wl.L).items() if k != "us"},
            "back_to_back": {"launch_us": us_b2b, "beam_steps_per_s": wl.R * wl.W * wl.L / (tot_us_b2b * 1e-6),
                             **{k: v for k, v in _bw(tot_b / wl.L, tot_us_b2b / wl.L).items() if k != "us"}}}
+    # the L launches captured in a HIP graph, replayed back to back (what a
+    # caller that replays whole decode passes sees; launch-bound shapes gain)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(wl.L):
+            d = steps[t]
+            B.decode_step(store, t, wl.W, d.get("parent"), d["q"], d["k"], d["v"], d["alpha"], d["beta"], o=outs[t])
+    graph.replay()
+    torch.cuda.synchronize()
+    g_us = float(np.mean(_queued(torch, stream, [graph.replay] * reps)))
+    del graph
+    out["graph_replay"] = {"us_per_pass": g_us, "beam_steps_per_s": wl.R * wl.W * wl.L / (g_us * 1e-6),
+                           **{k: v for k, v in _bw(tot_b / wl.L, g_us / wl.L).items() if k != "us"}}
     if _STREAM_RATES:
         out["read_fraction"] = [p["read_fraction"] for p in per]
         out["frac_of_mix_matched"] = (sum(p["bytes"] / (mix_rate(p["read_fraction"]) * 1e9) for p in per)
