@@ -101,11 +101,12 @@ def merge_bytes(*, R, H, dk, dv, n_rec, channel_decay=False, plain=False):
 
 def decode_merge_bytes(*, R, H, dk, dv, log_len, channel_decay=False, plain=False):
     """The decode that fills the log with the merge in the same pass: the
-    token's bytes (base read once), the base written back, and the log's
-    log_len + 1 records read by the fold."""
-    rec = record_bytes(dk, dv, channel_decay, plain)
+    token's bytes (base read once, the log's log_len records read once, the
+    new record appended) and the base written back.  The fold takes the same
+    log_len records the replay reads, plus the record the step appends, so
+    it moves no record a second time."""
     return (sequence_token_bytes(R=R, H=H, dk=dk, dv=dv, log_len=log_len, channel_decay=channel_decay, plain=plain)
-            + R * H * (4 * dk * dv + (log_len + 1) * rec))
+            + R * H * 4 * dk * dv)
 
 
 def onela_fig8b(*, R, W, H, K, V, O, record_bytes_per_head):

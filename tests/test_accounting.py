@@ -64,17 +64,18 @@ def test_unique_ancestors():
 def test_bounded_log_run_bytes():
     # 128 sequences, H/d_k/d_v = 32/128/128, log capacity M = 8 (DeltaLog
     # Table 3), 64 tokens: 8 full cycles of log lengths 0..7.  A merge cycle
-    # either merges separately (base read + written + 8 records) or folds the
-    # log in the decode that fills it (base written + 8 records, no second
-    # base read).
+    # either merges separately (base read + written + 8 records read again)
+    # or folds the log in the decode that fills it (base written; the fold
+    # takes the records that decode already reads and appends).
     kw = dict(R=128, H=32, dk=128, dv=128)
     tokens = 8 * sum(A.sequence_token_bytes(log_len=j, **kw) for j in range(8))
     separate = tokens + 8 * A.merge_bytes(n_rec=8, **kw)
     fused = 8 * (sum(A.sequence_token_bytes(log_len=j, **kw) for j in range(7))
                  + A.decode_merge_bytes(log_len=7, **kw))
     assert separate == 22_925_541_376
-    assert fused == 20_778_057_728
-    assert separate - fused == 8 * 128 * 32 * 4 * 128 * 128  # one base read per cycle
+    assert fused == 20_575_682_560
+    # per cycle: one base read and the merge's second read of the 8 records
+    assert separate - fused == 8 * 128 * 32 * (4 * 128 * 128 + 8 * A.record_bytes(128, 128, False, False))
 
 
 def test_step_write_bytes_are_the_written_part():
