@@ -38,10 +38,12 @@
  *     independent.  Calls that write the same store must be stream-ordered.
  *     The one exception is gdn_decode_step_split_noalloc, whose built-in
  *     scratch buffer (one per GPU) all its calls on that GPU share.
- *   - Two environment variables, read at every beam-decode call, exist for
+ *   - Three environment variables, read at every beam-decode call, exist for
  *     tests and comparisons only: GDN_BEAM_CHUNK=n (a multiple of 16, at
  *     least 16) fixes the number of beams per workgroup, which only changes
- *     which lanes compute a beam, never a result; GDN_BEAM_GENERIC=1 makes
+ *     which lanes compute a beam, never a result; GDN_BEAM_PAIR=0 keeps the
+ *     channel-decay kernel at one head per workgroup where it would take two
+ *     (the same bits either way); GDN_BEAM_GENERIC=1 makes
  *     gdn_beam_decode_step use its general kernel for every shape, whose
  *     results differ from the fused kernels' by FP32 rounding only.
  */

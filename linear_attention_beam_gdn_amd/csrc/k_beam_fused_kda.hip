@@ -29,14 +29,29 @@
 //     wave takes the q or the k row of a beam, walks the chain from the
 //     current step down (y = a_t * x; weight_j = k_j . y; y = a_j * y), and
 //     writes the probe Q_0 * x as hi and lo bf16 planes over the raw row, the
-//     record weights and k_t . q_t (chains of up to six records); in the
-//     first value slice it also appends
-//     the beam's key row and decay vector to the record store;
+//     record weights and k_t . q_t (chains of up to six records; the T + 1
+//     sums of a half wave reduced together, halving the set at each lane
+//     exchange); in the first value slice it also appends the beam's key row
+//     and decay vector to the record store;
 //   - then finishes the current tile: hi*hi + hi*lo + lo*hi plane products
-//     on the matrix cores, the q- and k-halves of the result exchanged with
-//     a DPP row rotation, the replay with the ancestral update vectors
-//     (loaded into registers one tile ahead), and the stores of o_t (q-half
-//     lanes) and delta_t (k-half lanes).
+//     on the matrix cores; each lane replays its own column's projection
+//     (u_q in the q columns, u_k in the k columns) with its side's record
+//     weights and the ancestral update vectors (loaded into registers one
+//     tile ahead, addressed by 32-bit offsets from per-depth bases);
+//     delta_t is formed in the k columns and handed to the q columns of the
+//     same beam by a DPP row rotation, which form o_t; the q columns store
+//     o_t and the k columns delta_t.
+//
+// Two heads per workgroup (NI = 2).  When the grid would hold two rounds of
+// workgroups or more, a workgroup takes two heads h, h + 1 of one request in
+// turn instead (one value slice, one chunk): their beams and parents are the
+// same, so they share one schedule, and one tile loop runs over both heads'
+// tiles, the DMA waves streaming the second head's first tiles while the
+// consumers finish the first's.  The consumers load the second head's part of
+// S0 from memory and form its planes when they reach its first tile.  This
+// spares the second head the prologue a second round of workgroups would pay
+// (the schedule's loads and sort, S0 and the first tiles in flight); every
+// beam's arithmetic is unchanged.
 //
 // LDS layouts: the 16-row q|k arrays use the beam-fastest layout of the
 // scalar kernel (chunk ch of row b at slot (ch/4)*64 + (ch%4)*16 + b); the
@@ -91,7 +106,11 @@ struct KdaGeom {
   static constexpr int VB = TB * VS * 2;
   static constexpr int AB = TB * DK * 4;
   static constexpr int SMB = 256;          // beta_t
-  static constexpr int NWT = (2 + 2 * T + 3) / 4 * 4;  // beta, k.q, T q-weights, T k-weights
+  // weights per beam: beta_t and k_t . q_t in the first 16 bytes, then the T
+  // q-side and the T k-side record weights, each side padded to 16 bytes, so
+  // that a lane reads its own side's weights in whole 16-byte words
+  static constexpr int P4 = (T + 3) / 4 * 4;
+  static constexpr int NWT = 4 + 2 * P4;
   static constexpr int WTB = TB * NWT * 4;
   static constexpr int RKB = TB * DK * 2;  // keys of one record depth
   static_assert(AB == QKB, "the lo plane of a tile takes the place of its decay vectors");
@@ -126,7 +145,7 @@ __device__ __forceinline__ int slot8(int b, int ch) { return (ch >> 3) * 64 + (c
 
 // value of lane l^8 within each 16-lane row (DPP row_ror:8)
 __device__ __forceinline__ float swap8(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, true));
 }
 
 // Sum over each 32-lane half of a wave64: quad swaps and row rotations by
@@ -134,7 +153,7 @@ __device__ __forceinline__ float swap8(float x) {
 // gfx950 row-swap instruction.  Lane 0 of a half always forms the same sum.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float sum_half(float x) {
   x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
@@ -144,6 +163,52 @@ __device__ __forceinline__ float sum_half(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+// NV sums (NV = 1, 2, 4 or 8) over each 32-lane half at once.  Exchanges
+// that halve the set come first: a lane keeps half of its values and adds
+// its partner's copy of them, sending the other half, which its partner
+// keeps (partners l and 7 - l choosing on bit 2, then l ^ 1 on bit 0, then
+// l ^ 2 on bit 1); plain sums over the remaining lane bits follow.  Lane l
+// ends with the sum of value 4 b2 + 2 b0 + b1 (NV = 8), 2 b0 + b1 (NV = 4),
+// b0 (NV = 2) or 0 (NV = 1), b_i being bit i of l.  v is overwritten.
+template <int NV>
+__device__ __forceinline__ float sum_half_many(float* v, int lane) {
+  static_assert(NV == 1 || NV == 2 || NV == 4 || NV == 8, "NV must be 1, 2, 4 or 8");
+  const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
+  if constexpr (NV == 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float keep = b2 ? v[4 + i] : v[i], send = b2 ? v[i] : v[4 + i];
+      v[i] = keep + dpp<0x141>(send);  // row_half_mirror: l <-> 7 - l
+    }
+  }
+  if constexpr (NV >= 2) {
+    constexpr int HV = NV >= 4 ? 2 : 1;
+#pragma unroll
+    for (int i = 0; i < HV; ++i) {
+      const float keep = b0 ? v[HV + i] : v[i], send = b0 ? v[i] : v[HV + i];
+      v[i] = keep + dpp<0xB1>(send);  // l ^ 1
+    }
+  }
+  if constexpr (NV >= 4) {
+    const float keep = b1 ? v[1] : v[0], send = b1 ? v[0] : v[1];
+    v[0] = keep + dpp<0x4E>(send);  // l ^ 2
+  }
+  float x = v[0];
+  if constexpr (NV < 2) x += dpp<0xB1>(x);
+  if constexpr (NV < 4) x += dpp<0x4E>(x);
+  if constexpr (NV < 8) x += dpp<0x124>(x);  // row_ror:4
+  x += dpp<0x128>(x);                        // row_ror:8
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+// the value whose sum lane l (bits 0 .. 4 of its index) holds after sum_half_many<NV>
+template <int NV>
+__device__ __forceinline__ int sum_half_many_index(int l) {
+  const int b0 = l & 1, b1 = (l >> 1) & 1, b2 = (l >> 2) & 1;
+  return NV == 8 ? 4 * b2 + 2 * b0 + b1 : NV == 4 ? 2 * b0 + b1 : NV == 2 ? b0 : 0;
 }
 
 // EPL consecutive bf16 (EPL = 2 or 4) as packed words, and EPL floats
@@ -177,7 +242,7 @@ __device__ __forceinline__ void lds_put(uint8_t* p, const uint32_t* w) {
     *reinterpret_cast<uint32_t*>(p) = w[0];
 }
 
-template <int DK, int DV, int T>
+template <int DK, int DV, int T, int NI>
 __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(BeamArgs a) {
   using G = KdaGeom<DK, DV, T>;
   constexpr int KS = G::KS;
@@ -189,24 +254,33 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
+  static_assert(NI == 1 || (NI == 2 && G::NVS == 1), "two heads per workgroup take one value slice each");
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  // (with NI = 2 the launch has one chunk and one value slice, and bid runs
+  // over (request, head pair))
   const int chunk_id = bid % a.nchunk;
   const int vsl = (bid / a.nchunk) % G::NVS;  // value slice
   const int rh = bid / (a.nchunk * G::NVS);
-  const int h = rh % a.H;
-  const int r = rh / a.H;
+  const int hpr = a.H / NI;                    // head groups per request
+  const int h = (rh % hpr) * NI;               // first head of the workgroup
+  const int r = rh / hpr;
   const int vs0 = vsl * G::VS;  // first value row of the slice
   const bool slice0 = vsl == 0;  // writes ancestry, record keys and decays
   const int b_begin = chunk_id * a.chunk;
   const int b_end = min(b_begin + a.chunk, a.Wt);
   const int nb = b_end - b_begin;
-  const int ntiles = (nb + G::TB - 1) / G::TB;
+  const int ntiles = (nb + G::TB - 1) / G::TB;  // per head
+  const int ntot = NI * ntiles;                 // tiles of the loop over the heads
+  // head item (0 or 1) of loop tile p, and p's tile within that head (tiles
+  // past the end count as the last head's)
+  auto item_of = [&](int p) { return NI > 1 && p >= ntiles ? 1 : 0; };
+  auto local = [&](int p) { return NI > 1 && p >= ntiles ? p - ntiles : p; };
 
   // Barriers: Q (t > 0: the schedule's loads have arrived), P (schedule
   // table written), S (S0 staged in LDS), A (tile 0 resident), then
-  // 0 .. ntiles.  Between barrier i and i + 1 the consumers finish tile i and
+  // 0 .. ntot.  Between barrier i and i + 1 the consumers finish tile i and
   // prepare tile i + 1, and a DMA wave refills the buffer of tile i - 1.
 
   if (w >= G::WDMA) {
@@ -238,7 +312,8 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
 
     auto dma_tile = [&](int p) {
       uint8_t* buf = smem + (p % G::NBUF) * G::BUF;
-      const int posi = min(p * G::TB + (lane & 7), nb - 1);  // positions past the chunk repeat its last
+      const int hp = h + item_of(p);
+      const int posi = min(local(p) * G::TB + (lane & 7), nb - 1);  // positions past the chunk repeat its last
       int ib = posi, sl[TT > 3 ? TT : 3] = {};
       if constexpr (T > 0) {
         const u32x4 e = lds_read128_opaque(&s_tab[posi]);
@@ -249,9 +324,9 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
 #pragma unroll
         for (int j = 3; j < T; ++j) sl[j] = lds_read_opaque(&s_slot_hi[(j - 3) * kMaxChunkF + posi]);
       }
-      const size_t tok = ((size_t)r * a.Wt + b_begin + ib) * a.H + h;
+      const size_t tok = ((size_t)r * a.Wt + b_begin + ib) * a.H + hp;
       // q|k: rows 0-7 the q rows, rows 8-15 the k rows of the tile's beams
-      const size_t tok_k = ((size_t)r * a.Wt + b_begin + ib) * a.Hk + h / a.gq;  // its key head
+      const size_t tok_k = ((size_t)r * a.Wt + b_begin + ib) * a.Hk + hp / a.gq;  // its key head
       const uint16_t* qkrow = ((lane & 8) ? a.k : a.q) + tok_k * DK;
 #pragma unroll
       for (int m = 0; m < G::QKB / 1024; ++m) dma16(qkrow + (m * 4 + (lane >> 4)) * 8, buf + G::OQK + m * 1024);
@@ -263,8 +338,8 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       dma4(a.beta + tok, buf + G::OS);
 #pragma unroll
       for (int j = 0; j < T; ++j) {
-        const size_t rj = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + h;
-        const size_t rjk = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.Hk + h / a.gq;
+        const size_t rj = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + hp;
+        const size_t rjk = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.Hk + hp / a.gq;
 #pragma unroll
         for (int m = 0; m < G::RKB / 1024; ++m)
           dma16(a.rec_k + rjk * DK + (m * 8 + (lane >> 3)) * 8, buf + G::ORK + j * G::RKB + m * 1024);
@@ -278,7 +353,7 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     lds_barrier();  // P
     // tiles 0 and 1 first, on their own; the other prologue tiles follow A,
     // once S0 has left LDS
-    const int npro = min(G::NBUF - 1, ntiles);
+    const int npro = min(G::NBUF - 1, ntot);
     if (dw < npro) dma_tile(dw);
     if (dw == 1) {
       if (npro > 1) wait_vm<G::OPT>();  // S0 staged; tile 1 may still be in flight
@@ -291,12 +366,12 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     if (dw == 1) wait_tiles<G::OPT, 2>(later(1, npro - 1));  // tile 1 resident
     lds_barrier();                                          // 0
     unsigned long long waited = 0;
-    for (int i = 0; i < ntiles; ++i) {
+    for (int i = 0; i < ntot; ++i) {
       const int p = i + G::NBUF - 1;  // into the buffer released at the last barrier
-      if (p < ntiles && (p & 1) == dw) dma_tile(p);
-      const int last = min(p, ntiles - 1);
+      if (p < ntot && (p & 1) == dw) dma_tile(p);
+      const int last = min(p, ntot - 1);
       const unsigned long long w0 = stamp_now();
-      if (i + 2 < ntiles && ((i + 2) & 1) == dw) wait_tiles<G::OPT, 2>(later(i + 2, last));  // tile i + 2 resident
+      if (i + 2 < ntot && ((i + 2) & 1) == dw) wait_tiles<G::OPT, 2>(later(i + 2, last));  // tile i + 2 resident
       waited += stamp_now() - w0;
       lds_barrier();                                                                     // i + 1
     }
@@ -307,14 +382,21 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   // ============================================================ consumers
   GDN_STAMP(0);
   GDN_STAMP_WHERE();
-  // record-store windows over the chunk's beams (appends at step T)
-  const size_t rec0 = (((size_t)T * a.R + r) * a.Wm + b_begin) * a.H + h;
+  // record-store windows over the chunk's beams (appends at step T) of the
+  // head prep() works on (with NI = 2 they move to the second head before
+  // its first tile is prepared)
   const int sk = a.Hk * DK * 2, sa = a.H * DK * 4;  // bytes between beams
-  // the record key lives per key head: one of its value heads writes it
-  const size_t rec0k = (((size_t)T * a.R + r) * a.Wm + b_begin) * a.Hk + h / a.gq;
-  const bool key_writer = h % a.gq == 0 && slice0;
-  const __amdgpu_buffer_rsrc_t w_k = store_window(a.rec_k + rec0k * DK, (nb - 1) * sk + DK * 2);
-  const __amdgpu_buffer_rsrc_t w_a = store_window(a.rec_alpha + rec0 * DK, (nb - 1) * sa + DK * 4);
+  __amdgpu_buffer_rsrc_t w_k, w_a;
+  bool key_writer;
+  auto prep_head = [&](int hh) {
+    const size_t rec0 = (((size_t)T * a.R + r) * a.Wm + b_begin) * a.H + hh;
+    // the record key lives per key head: one of its value heads writes it
+    const size_t rec0k = (((size_t)T * a.R + r) * a.Wm + b_begin) * a.Hk + hh / a.gq;
+    key_writer = hh % a.gq == 0 && slice0;
+    w_k = store_window(a.rec_k + rec0k * DK, (nb - 1) * sk + DK * 2);
+    w_a = store_window(a.rec_alpha + rec0 * DK, (nb - 1) * sa + DK * 4);
+  };
+  prep_head(h);
 
   // Preparation of beams w * BPW .. w * BPW + BPW - 1 of tile p.  Lane
   // (side, el): channels EPL * el .. EPL * el + EPL - 1 of the q row
@@ -361,20 +443,22 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
         wj[j] = pj;
       }
       // appends of step T: the key row (side 1) and the decay vector (side 0)
-      const int posi = p * G::TB + pb;
+      const int posi = local(p) * G::TB + pb;
       const bool live = posi < nb;
       const int ib = T > 0 ? (int)s_tab[min(posi, nb - 1)][0] : posi;  // read unconditionally: no branch
+      // byte offsets of the beam's appends (24-bit products: beams and strides
+      // are far below 2^24)
+      const int ib_k = (int)__umul24((uint32_t)ib, (uint32_t)sk), ib_a = (int)__umul24((uint32_t)ib, (uint32_t)sa);
       if constexpr (EPL == 4) {
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{kw[0], kw[1]}, w_k,
-                                              live && ps && key_writer ? ib * sk + e0 * 2 : kOutside,
-                                              0, 0);
+                                              live && ps && key_writer ? ib_k + e0 * 2 : kOutside, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{at[0], at[1], at[2], at[3]}), w_a,
-                                               live && !ps && slice0 ? ib * sa + e0 * 4 : kOutside, 0, 0);
+                                               live && !ps && slice0 ? ib_a + e0 * 4 : kOutside, 0, 0);
       } else {
-        __builtin_amdgcn_raw_buffer_store_b32(kw[0], w_k, live && ps && key_writer ? ib * sk + e0 * 2 : kOutside,
+        __builtin_amdgcn_raw_buffer_store_b32(kw[0], w_k, live && ps && key_writer ? ib_k + e0 * 2 : kOutside,
                                               0, 0);
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(at[0]), __float_as_uint(at[1])}, w_a,
-                                              live && !ps && slice0 ? ib * sa + e0 * 4 : kOutside, 0, 0);
+                                              live && !ps && slice0 ? ib_a + e0 * 4 : kOutside, 0, 0);
       }
       // probe Q_0 x as hi + lo bf16 planes, over the raw row and this beam's alpha_t
       uint32_t hw[EPL / 2], lw[EPL / 2];
@@ -385,24 +469,22 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       }
       lds_put<EPL>(buf + G::OQK + oqk + (pb + 8 * ps) * 16, hw);
       lds_put<EPL>(buf + G::OLO + oqk + (pb + 8 * ps) * 16, lw);
-      // weights: beta, k.q, q-weights (side 0 sums), k-weights (side 1 sums)
-      sqq = sum_half(sqq);
+      // weights: k.q (side 0), the q-weights (side 0 sums) and the
+      // k-weights (side 1 sums), all summed over the half-waves at once
+      constexpr int NV = T == 0 ? 1 : T == 1 ? 2 : T <= 3 ? 4 : 8;
+      float sv[NV];
+      sv[0] = sqq;
 #pragma unroll
-      for (int j = 0; j < T; ++j) wj[j] = sum_half(wj[j]);
-      // one store for the wave, no branch: lane 0 beta, lane 1 k.q, lanes
-      // 2 + j and 32 + j the q- and k-weights of record j; every other lane
-      // writes beta again to entry 0
-      int wi = 0;
-      float wv = beta;
-      if (lane == 1) wv = sqq;
-#pragma unroll
-      for (int j = 0; j < T; ++j) {
-        if (lane == 2 + j) wv = wj[j];
-        if (lane == 32 + j) wv = wj[j];
-      }
-      if (lane >= 1 && lane < 2 + T) wi = lane;
-      if (lane >= 32 && lane < 32 + T) wi = lane - 30 + T;
-      reinterpret_cast<float*>(buf + G::OW)[pb * G::NWT + wi] = wv;
+      for (int i = 1; i < NV; ++i) sv[i] = i <= T ? wj[i <= T ? i - 1 : 0] : 0.f;
+      const float red = sum_half_many<NV>(sv, lane);
+      // one store for the wave, no branch: the lanes holding value i of
+      // their side write it (side 0: k.q to entry 1, q-weight j to 4 + j;
+      // side 1: k-weight j to 4 + P4 + j); every other lane writes beta to
+      // entry 0
+      const int l5 = lane & 31, qi = sum_half_many_index<NV>(l5);
+      const bool has = l5 < NV && qi <= T && (qi > 0 || ps == 0);
+      const int wi = !has ? 0 : qi == 0 ? 1 : 3 + qi + ps * G::P4;
+      reinterpret_cast<float*>(buf + G::OW)[pb * G::NWT + wi] = has ? red : beta;
     }
   };
 
@@ -433,26 +515,42 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   // this lane's first value row in row block rb: row0 + 16 rb
   const int row0 = vs0 + w * NRB * 16 + 4 * g;
   const int so = a.H * DV * 4;
-  const size_t tok0 = ((size_t)r * a.Wt + b_begin) * a.H + h;
-  const __amdgpu_buffer_rsrc_t w_o = store_window(a.o + tok0 * DV, (nb - 1) * so + DV * 4);
-  const __amdgpu_buffer_rsrc_t w_d = store_window(a.rec_delta + rec0 * DV, (nb - 1) * so + DV * 4);
+  // windows of o and the appended update vectors of the head being finished
+  __amdgpu_buffer_rsrc_t w_o, w_d;
+  auto out_head = [&](int hh) {
+    const size_t tok0 = ((size_t)r * a.Wt + b_begin) * a.H + hh;
+    const size_t rec0 = (((size_t)T * a.R + r) * a.Wm + b_begin) * a.H + hh;
+    w_o = store_window(a.o + tok0 * DV, (nb - 1) * so + DV * 4);
+    w_d = store_window(a.rec_delta + rec0 * DV, (nb - 1) * so + DV * 4);
+  };
+  out_head(h);
 
   // ancestral update vectors of tile p, this lane's 4 rows of beam bb in row
-  // blocks rb0 .. rb1 - 1
+  // blocks rb0 .. rb1 - 1: slot s of depth j sits s * so bytes past the
+  // depth's first slot of the head (a 32-bit offset: the store holds less
+  // than 2 GiB of update vectors per depth and request).  The depths' bases
+  // move to the second head (NI = 2) before its first tile's vectors load.
+  const uint8_t* dbase[TT];
+  auto delta_head = [&](int hh) {
+#pragma unroll
+    for (int j = 0; j < T; ++j)
+      dbase[j] = reinterpret_cast<const uint8_t*>(a.rec_delta + ((((size_t)j * a.R + r) * a.Wm) * a.H + hh) * DV);
+  };
+  delta_head(h);
   auto load_deltas = [&](int p, f32x4 (*d)[NRB], int rb0 = 0, int rb1 = G::NRB) {
     if constexpr (T > 0) {
-      const int posi = min(p * G::TB + bb, nb - 1);
+      const int posi = min(local(p) * G::TB + bb, nb - 1);
       const u32x4 e = s_tab[posi];
       int sl[TT > 3 ? TT : 3] = {(int)e[1], (int)e[2], (int)e[3]};
 #pragma unroll
       for (int j = 3; j < T; ++j) sl[j] = s_slot_hi[(j - 3) * kMaxChunkF + posi];
 #pragma unroll
       for (int j = 0; j < T; ++j) {
-        const size_t rj = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + h;
+        const uint32_t off = __umul24((uint32_t)sl[j], (uint32_t)so) + (uint32_t)row0 * 4;
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
           if (rb >= rb0 && rb < rb1)
-            d[j][rb] = *reinterpret_cast<const f32x4*>(a.rec_delta + rj * DV + row0 + 16 * rb);
+            d[j][rb] = *reinterpret_cast<const f32x4*>(dbase[j] + off + 64 * rb);
       }
     }
   };
@@ -488,8 +586,13 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   GDN_STAMP(5);
 
   unsigned long long c_prep = 0, c_fin = 0, c_bar = 0;
-  for (int it = 0; it < ntiles; ++it) {
+  // one tile of the loop (the loop runs once per head, so that the planes of
+  // S0 stay fixed inside it)
+  auto step = [&](int it) {
     const unsigned long long c0 = stamp_now();
+    if constexpr (NI > 1) {
+      if (it + 1 == ntiles) delta_head(h + 1);  // the next tile's update vectors are the second head's
+    }
     // Double-buffered: this tile's update vectors move to dcur and the next
     // tile's are loaded at once.  Otherwise each row block's next update
     // vectors are loaded into dnext right after the block has used them
@@ -507,6 +610,9 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     // tile's work.  Past the last tile it reads a free buffer (no load of
     // this launch targets it any more), writes only there, and its appends
     // fall outside the store windows.
+    if constexpr (NI > 1) {
+      if (it + 1 == ntiles) prep_head(h + 1);
+    }
     prep(it + 1);
     const unsigned long long c1 = stamp_now();
 
@@ -517,14 +623,16 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       bh[s] = *reinterpret_cast<const u32x4*>(buf + G::OQK + slot16(c, s * 4 + g) * 16);
       bl[s] = *reinterpret_cast<const u32x4*>(buf + G::OLO + slot16(c, s * 4 + g) * 16);
     }
-    float wt[G::NWT];
+    // beta_t and k_t . q_t, then this lane's side's record weights
+    const f32x4 w01 = *reinterpret_cast<const f32x4*>(buf + G::OW + bb * G::NWT * 4);
+    float ws[G::P4 > 0 ? G::P4 : 1];
 #pragma unroll
-    for (int v = 0; v < G::NWT; v += 4) {
-      const f32x4 q4 = *reinterpret_cast<const f32x4*>(buf + G::OW + (bb * G::NWT + v) * 4);
+    for (int v = 0; v < G::P4; v += 4) {
+      const f32x4 q4 = *reinterpret_cast<const f32x4*>(buf + G::OW + (bb * G::NWT + 4 + side * G::P4 + v) * 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) wt[v + e] = q4[e];
+      for (int e = 0; e < 4; ++e) ws[v + e] = q4[e];
     }
-    const int posi = it * G::TB + bb;
+    const int posi = local(it) * G::TB + bb;
     const bool live = posi < nb;
     const int ib = T > 0 ? (int)s_tab[min(posi, nb - 1)][0] : posi;
 
@@ -542,31 +650,26 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
         u = mfma16x16x32(As[rb][s][0], bl[s], u);
         u = mfma16x16x32(As[rb][s][0], bh[s], u);
       }
-      f32x4 uq, uk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float other = swap8(u[i]);
-        uq[i] = side ? other : u[i];
-        uk[i] = side ? u[i] : other;
-      }
-      f32x4 xq = uq, xk = uk;
+      // Replay of this lane's own projection (u_q in the q columns, u_k in
+      // the k columns), delta_t formed in the k columns and handed to the q
+      // columns of the same beam (lane c ^ 8), o_t formed there.
+      f32x4 x = u;
 #pragma unroll
       for (int j = 0; j < T; ++j) {
         const f32x4 dj = DBUF ? dcur[DBUF ? j : 0][DBUF ? rb : 0] : dnext[j][rb];
-        xq += wt[2 + j] * dj;
-        xk += wt[2 + T + j] * dj;
+        x += ws[j] * dj;
       }
       f32x4 dt, ot;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t word = vw[i >> 1];
         const float vv = (i & 1) ? bf16_hi(word) : bf16_lo(word);
-        dt[i] = wt[0] * (vv - xk[i]);
-        ot[i] = xq[i] + dt[i] * wt[1];
+        dt[i] = w01[0] * (vv - x[i]);
+        ot[i] = x[i] + swap8(dt[i]) * w01[1];
       }
 
       // output (q-column lanes) and the appended update vector (k-column lanes)
-      const int off = live ? ib * so + (row0 + 16 * rb) * 4 : kOutside;
+      const int off = live ? (int)__umul24((uint32_t)ib, (uint32_t)so) + (row0 + 16 * rb) * 4 : kOutside;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, side ? kOutside : off, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, side ? off : kOutside, 0, 0);
       if constexpr (!DBUF) load_deltas(it + 1, dnext, rb, rb + 1);
@@ -576,6 +679,21 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     c_prep += c1 - c0;
     c_fin += c2 - c1;
     c_bar += stamp_now() - c2;
+  };
+  for (int it = 0; it < ntiles; ++it) step(it);
+  if constexpr (NI > 1) {
+    // the second head: its part of S0 from memory into the planes, its
+    // output windows, then its tiles
+    out_head(h + 1);
+    const float* Sg = a.S + ((size_t)r * a.H + h + 1) * DK * DV + vs0 + w * 16 + c;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = Sg[(size_t)(s * 32 + g * 8 + e) * DV];
+      split_planes<2>(x, As[0][s]);
+    }
+    for (int it = ntiles; it < ntot; ++it) step(it);
   }
   GDN_STAMP(6);
   GDN_STAMP_AT(8, 0, c_prep);
@@ -611,11 +729,24 @@ int launch(const gdn_shape& sh, const gdn_store& st, int Wt, const StepIO& io, h
   a.Hk = key_heads(sh);
   a.gq = sh.H / a.Hk;
   // one workgroup per compute unit: the tile ring takes most of its LDS
-  a.chunk = pick_chunk(sh.R * sh.H * G::NVS, Wt, kMaxChunkF, cu_count(stream));
+  const int cus = cu_count(stream);
+  a.chunk = pick_chunk(sh.R * sh.H * G::NVS, Wt, kMaxChunkF, cus);
   a.nchunk = (Wt + a.chunk - 1) / a.chunk;
   const long grid = (long)sh.R * sh.H * G::NVS * a.nchunk;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
-  hipLaunchKernelGGL((k_beam_fused_kda<DK, DV, T>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
+  // Two heads per workgroup where a grid of one per head would run two
+  // rounds or more (one chunk, one value slice, chains of up to three records,
+  // whose registers leave room for the second head's S0).  GDN_BEAM_PAIR=0
+  // turns it off, for comparisons.
+  if constexpr (G::NVS == 1 && T <= 3) {
+    const char* pair = getenv("GDN_BEAM_PAIR");
+    const bool off = pair != nullptr && pair[0] == '0';
+    if (!off && a.nchunk == 1 && sh.H % 2 == 0 && grid >= 2L * cus) {
+      hipLaunchKernelGGL((k_beam_fused_kda<DK, DV, T, 2>), dim3((unsigned)(grid / 2)), dim3(G::NT), 0, stream, a);
+      return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
+    }
+  }
+  hipLaunchKernelGGL((k_beam_fused_kda<DK, DV, T, 1>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
@@ -636,9 +767,11 @@ int launch_dims(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const S
 }  // namespace
 
 bool beam_fused_kda_supported(const gdn_shape& sh, int t) {
+  // the consumers address a depth's update vectors with 32-bit offsets
+  const bool offsets_fit = (long long)sh.W_max * sh.H * sh.dv * 4 < (1LL << 31);
   return sh.decay_kind == GDN_DECAY_CHANNEL && t >= 0 && t <= 6 &&
          ((sh.dk == 64 && sh.dv == 64) || (sh.dk == 128 && (sh.dv == 128 || sh.dv == 256 || sh.dv == 512))) &&
-         windows_fit(sh);
+         windows_fit(sh) && offsets_fit;
 }
 
 int launch_beam_fused_kda(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO& io,

@@ -35,14 +35,18 @@ __device__ __forceinline__ unsigned long long stamp_now() { return __builtin_amd
     }                                                                                 \
   } while (0)
 // Copies the first n_wg rows (16 stamps each) of this source's array to host
-// memory; GDN_EINVAL for a null pointer or n_wg outside [0, 4096].
-#define GDN_STAMPS_READER(name)                                                                    \
-  extern "C" int name(unsigned long long* host, int n_wg) {                                        \
-    if (host == nullptr || n_wg < 0 || n_wg > gdn::kStampWgs) return GDN_EINVAL;                   \
-    return hipMemcpyFromSymbol(host, HIP_SYMBOL(gdn::g_stamps), (size_t)n_wg * gdn::kStamps * 8, 0, \
-                               hipMemcpyDeviceToHost) == hipSuccess                                \
-               ? GDN_OK                                                                            \
-               : GDN_EHIP;                                                                         \
+// memory and clears the whole array (so that rows of workgroups a launch did
+// not have read zero); GDN_EINVAL for a null pointer or n_wg outside
+// [0, 4096].
+#define GDN_STAMPS_READER(name)                                                                          \
+  extern "C" int name(unsigned long long* host, int n_wg) {                                              \
+    if (host == nullptr || n_wg < 0 || n_wg > gdn::kStampWgs) return GDN_EINVAL;                         \
+    if (hipMemcpyFromSymbol(host, HIP_SYMBOL(gdn::g_stamps), (size_t)n_wg * gdn::kStamps * 8, 0,         \
+                            hipMemcpyDeviceToHost) != hipSuccess)                                        \
+      return GDN_EHIP;                                                                                   \
+    void* dev = nullptr;                                                                                 \
+    if (hipGetSymbolAddress(&dev, HIP_SYMBOL(gdn::g_stamps)) != hipSuccess) return GDN_EHIP;             \
+    return hipMemset(dev, 0, sizeof(gdn::g_stamps)) == hipSuccess ? GDN_OK : GDN_EHIP;                   \
   }
 #else
 namespace gdn {

@@ -72,7 +72,10 @@ def main():
                     channel_decay=kda)
     outs = [torch.empty(w.R, w.W, w.H, w.dv, dtype=torch.float32, device=dev) for _ in range(w.L)]
     stream = torch.cuda.current_stream()
-    n_wg = w.R * w.H * nvs  # one workgroup per (request, head, value slice) with every beam in one chunk
+    # at most one workgroup per (request, head, value slice) with every beam in
+    # one chunk (fewer where a workgroup takes two heads); the reader clears
+    # the stamps, so rows of workgroups a launch did not have read zero
+    n_wg = w.R * w.H * nvs
 
     def launch(t):
         d = steps[t]
@@ -89,6 +92,8 @@ def main():
 
     flush = S.ReadFlush(torch)
     buf = np.zeros((n_wg, 16), np.uint64)
+    if read(buf.ctypes.data, n_wg) != 0:  # clears what the warm-up launches wrote
+        raise RuntimeError("gdn_stamps_read failed")
     rows = {t: [] for t in range(w.L)}
     for _ in range(args.reps):
         for t in range(w.L):
@@ -103,6 +108,10 @@ def main():
                 raise RuntimeError(f"gdn_stamps_read returned {rc}")
             rows[t].append((a.elapsed_time(b) * 1e3, buf.copy()))
 
+    live = np.stack([r[1] for r in rows[0]])[0, :, 0] != 0  # workgroups the launches had
+    for t in range(w.L):
+        rows[t] = [(ev, st[live]) for ev, st in rows[t]]
+    n_wg = int(live.sum())
     kname = "k_beam_fused_kda" if kda else "k_beam_fused"
     lines = [f"Clock stamps of `{kname}<{w.dk},{w.dv},t>` at `{w.name}` ({w.R} x {w.W} beams, H = {w.H}, "
              f"d_k = {w.dk}, d_v = {w.dv}; {n_wg} workgroups), "
@@ -131,7 +140,7 @@ def main():
         xcd = (st[:, :, 7] >> 32) & 0xF
         per = {int(x): float(np.median(rel[:, :, 6][xcd == x])) for x in np.unique(xcd)}
         xcd_rows.append((t, per))
-    nt = w.W // tb
+    nt = w.W // tb * (w.R * w.H * nvs // n_wg)  # tiles per workgroup (two heads' worth where paired)
     if kda:
         lines += ["", "Work and waits inside the tile loop, us per tile (medians over workgroups and launches; "
                   f"{nt} tiles of {tb} beams per workgroup): each consumer wave prepares its share of tile i + 1 (probes, "

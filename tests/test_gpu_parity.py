@@ -86,6 +86,22 @@ def test_full_size_workload_every_pair(wname, channel, tmp_path):
     _full_beam(getattr(configs, wname), channel, tmp_path)
 
 
+def test_kda_two_heads_per_workgroup_same_bits(monkeypatch):
+    """The channel-decay workload at full size (16 x 256 beams, H = 32: two
+    rounds of workgroups, so the launch takes two heads per workgroup) gives
+    the same bits as one head per workgroup (GDN_BEAM_PAIR=0): outputs,
+    update vectors, keys, decays and ancestry of every step."""
+    inp = configs.KDA.inputs()
+    log("[parity] kda_channel_decay_beam: two heads per workgroup against one, every step")
+    store2, outs2 = run_beam(inp, True)
+    monkeypatch.setenv("GDN_BEAM_PAIR", "0")
+    store1, outs1 = run_beam(inp, True)
+    for t in range(len(outs1)):
+        assert np.array_equal(outs1[t], outs2[t]), t
+    for name in ("rec_delta", "rec_k", "rec_alpha", "anc"):
+        assert torch.equal(getattr(store1, name), getattr(store2, name)), name
+
+
 def test_large_beam_workload_sampled():
     # full size, eager oracle on a sample (kept beside the full comparison)
     check_beam(configs.LARGE.inputs(), False, requests=[0, 5], heads=[0, 13, 31],
