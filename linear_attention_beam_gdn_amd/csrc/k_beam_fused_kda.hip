@@ -91,6 +91,12 @@ struct KdaGeom {
   static constexpr int VS = DV < 128 ? DV : 128 * NRB;  // value rows per workgroup
   static_assert(DV % VS == 0, "d_v must split evenly over value slices");
   static constexpr int NVS = DV / VS;      // value slices
+  // 32-bit offsets from per-depth bases (24-bit products) for the update
+  // vectors, the outputs and the appends: faster with one row block per
+  // consumer wave (seven steps at 16 x 256 beams: 10 % faster), slower with
+  // two (the 256-row slices: 18 % slower at t = 1), which keep 64-bit
+  // addresses and plain products
+  static constexpr bool LEAN = NRB == 1;
   static constexpr int NC = VS / (16 * NRB);  // consumer waves, 16 NRB value rows each
   static_assert(TB % NC == 0, "each consumer wave prepares whole beams");
   static constexpr int BPW = TB / NC;      // beams a consumer wave prepares per tile
@@ -446,9 +452,11 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       const int posi = local(p) * G::TB + pb;
       const bool live = posi < nb;
       const int ib = T > 0 ? (int)s_tab[min(posi, nb - 1)][0] : posi;  // read unconditionally: no branch
-      // byte offsets of the beam's appends (24-bit products: beams and strides
-      // are far below 2^24)
-      const int ib_k = (int)__umul24((uint32_t)ib, (uint32_t)sk), ib_a = (int)__umul24((uint32_t)ib, (uint32_t)sa);
+      // byte offsets of the beam's appends (24-bit products where a consumer
+      // wave holds one row block: beams and strides are far below 2^24; the
+      // 256-row slices measured faster with plain products)
+      const int ib_k = G::LEAN ? (int)__umul24((uint32_t)ib, (uint32_t)sk) : ib * sk;
+      const int ib_a = G::LEAN ? (int)__umul24((uint32_t)ib, (uint32_t)sa) : ib * sa;
       if constexpr (EPL == 4) {
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{kw[0], kw[1]}, w_k,
                                               live && ps && key_writer ? ib_k + e0 * 2 : kOutside, 0, 0);
@@ -526,10 +534,11 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   out_head(h);
 
   // ancestral update vectors of tile p, this lane's 4 rows of beam bb in row
-  // blocks rb0 .. rb1 - 1: slot s of depth j sits s * so bytes past the
-  // depth's first slot of the head (a 32-bit offset: the store holds less
-  // than 2 GiB of update vectors per depth and request).  The depths' bases
-  // move to the second head (NI = 2) before its first tile's vectors load.
+  // blocks rb0 .. rb1 - 1.  LEAN: slot s of depth j sits s * so bytes past
+  // the depth's first slot of the head (a 32-bit offset: the store holds
+  // less than 2 GiB of update vectors per depth and request); the depths'
+  // bases move to the second head (NI = 2) before its first tile's vectors
+  // load.
   const uint8_t* dbase[TT];
   auto delta_head = [&](int hh) {
 #pragma unroll
@@ -546,11 +555,18 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       for (int j = 3; j < T; ++j) sl[j] = s_slot_hi[(j - 3) * kMaxChunkF + posi];
 #pragma unroll
       for (int j = 0; j < T; ++j) {
-        const uint32_t off = __umul24((uint32_t)sl[j], (uint32_t)so) + (uint32_t)row0 * 4;
+        if constexpr (G::LEAN) {
+          const uint32_t off = __umul24((uint32_t)sl[j], (uint32_t)so) + (uint32_t)row0 * 4;
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          if (rb >= rb0 && rb < rb1)
-            d[j][rb] = *reinterpret_cast<const f32x4*>(dbase[j] + off + 64 * rb);
+          for (int rb = 0; rb < NRB; ++rb)
+            if (rb >= rb0 && rb < rb1) d[j][rb] = *reinterpret_cast<const f32x4*>(dbase[j] + off + 64 * rb);
+        } else {
+          const size_t rj = (((size_t)j * a.R + r) * a.Wm + sl[j]) * a.H + h + item_of(p);
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+            if (rb >= rb0 && rb < rb1)
+              d[j][rb] = *reinterpret_cast<const f32x4*>(a.rec_delta + rj * DV + row0 + 16 * rb);
+        }
       }
     }
   };
@@ -669,7 +685,8 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       }
 
       // output (q-column lanes) and the appended update vector (k-column lanes)
-      const int off = live ? (int)__umul24((uint32_t)ib, (uint32_t)so) + (row0 + 16 * rb) * 4 : kOutside;
+      const int off = live ? (G::LEAN ? (int)__umul24((uint32_t)ib, (uint32_t)so) : ib * so) + (row0 + 16 * rb) * 4
+                           : kOutside;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, side ? kOutside : off, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, side ? off : kOutside, 0, 0);
       if constexpr (!DBUF) load_deltas(it + 1, dnext, rb, rb + 1);
