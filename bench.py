@@ -6,9 +6,9 @@ transition, output and append) of 8 requests x 512 beams, H = 32 heads,
 d_k = d_v = 128, on seeded synthetic inputs already resident in HBM.
 
 Prints one JSON line: beam-steps/s, the roofline of the decode kernel
-(algorithmic bytes per launch over its HIP-event-timed mean duration, against
-8 TB/s), and the FP64 CPU oracle timed on a bounded sample of the same
-workload on the host cores.
+(algorithmic bytes per launch over its mean kernel time, taken by HIP events
+that the runtime records around each launch, against 8 TB/s), and the FP64
+CPU oracle timed on a bounded sample of the same workload on the host cores.
 """
 
 from __future__ import annotations
@@ -149,6 +149,29 @@ def _queued(torch, stream, calls, flush=False):
     return [a.elapsed_time(b) * 1e3 for a, b in ev]
 
 
+def _queued_kernel(torch, stream, calls, flush=False):
+    """As _queued, for calls that take a pair of timing events and hand it to
+    their kernel launch (gdn_beam_decode_step_timed): the runtime records the
+    pair as the kernel starts and completes, so each duration is the kernel's
+    execution alone, without event commands of its own in the stream or a
+    system-scope fence (KernelEvents)."""
+    from linear_attention_beam_gdn_amd.measure import stream as S
+
+    ev = S.KernelEvents(len(calls))
+    try:
+        _pad(torch, stream)
+        for pair, fn in zip(ev.pairs, calls):
+            if flush == "copy":
+                _copy_flush(torch)
+            elif flush:
+                _flush(torch)
+            fn(pair)
+        torch.cuda.synchronize()
+        return ev.elapsed_us()
+    finally:
+        ev.close()
+
+
 _FLUSH_BUF = []
 _COPY_BUF = []
 
@@ -219,10 +242,10 @@ def beam_row(B, torch, dev, stream, wl, reps):
                     S=torch.from_numpy(inp["S0"]).to(dev), Hk=wl.Hk)
     outs = [torch.empty(wl.R, wl.W, wl.H, wl.dv, dtype=torch.float32, device=dev) for _ in range(wl.L)]
 
-    def launch(t):
+    def launch(t, ev=None):
         d = steps[t]
         B.decode_step(store, t, wl.W, d.get("parent"), d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                      o=outs[t], stream=stream)
+                      o=outs[t], stream=stream, events=ev)
 
     for _ in range(2):
         for t in range(wl.L):
@@ -230,14 +253,20 @@ def beam_row(B, torch, dev, stream, wl, reps):
     torch.cuda.synchronize()
     # keep the step order: step t reads step t-1's records.  As for the
     # headline's roofline launches, a 1 GiB read-only sweep runs (untimed)
-    # before every launch; the same launches back to back, where each one
-    # also drains the previous one's dirty lines from the Infinity Cache,
-    # are reported beside.
-    calls = [(lambda t=t: launch(t)) for _ in range(reps) for t in range(wl.L)]
-    d = _queued(torch, stream, calls, flush=True)
-    d_b2b = _queued(torch, stream, calls)
+    # before every launch, and the runtime brackets each kernel with timing
+    # events; the same launches back to back, where each one also drains the
+    # previous one's dirty lines from the Infinity Cache, and the flushed
+    # launches timed between event commands of their own, are reported beside.
+    calls = [(lambda ev, t=t: launch(t, ev)) for _ in range(reps) for t in range(wl.L)]
+    # one round untimed first: the first round of swept launches after a
+    # workload's buffers are new runs 1-3 % slower than every later one
+    _queued_kernel(torch, stream, calls, flush=True)
+    d = _queued_kernel(torch, stream, calls, flush=True)
+    d_b2b = _queued_kernel(torch, stream, calls)
+    d_pair = _queued(torch, stream, [(lambda t=t: launch(t)) for _ in range(reps) for t in range(wl.L)], flush=True)
     us = [float(np.mean(d[t::wl.L])) for t in range(wl.L)]
     us_b2b = [float(np.mean(d_b2b[t::wl.L])) for t in range(wl.L)]
+    us_pair = [float(np.mean(d_pair[t::wl.L])) for t in range(wl.L)]
     anc = store.anc.cpu().numpy()
     per = []
     for t in range(wl.L):
@@ -250,9 +279,11 @@ def beam_row(B, torch, dev, stream, wl, reps):
         per[-1]["read_fraction"] = 1.0 - wb / nbytes
     tot_b, tot_us, tot_us_b2b = sum(p["bytes"] for p in per), sum(us), sum(us_b2b)
     out = {"workload": wl.name, "precision": beam_precision(wl), "decode_steps": wl.L,
-           "cache": "Infinity Cache flushed (1 GiB read-only sweep) before every event-timed launch",
+           "cache": "Infinity Cache flushed (1 GiB read-only sweep) before every timed launch",
+           "timing": "kernel time as the runtime brackets the launch (gdn_beam_decode_step_timed)",
            "beam_steps_per_s": wl.R * wl.W * wl.L / (tot_us * 1e-6),
            "launch_us": us, **{k: v for k, v in _bw(tot_b / wl.L, tot_us / wl.L).items() if k != "us"},
+           "launch_us_event_pair": us_pair,
            "back_to_back": {"launch_us": us_b2b, "beam_steps_per_s": wl.R * wl.W * wl.L / (tot_us_b2b * 1e-6),
                             **{k: v for k, v in _bw(tot_b / wl.L, tot_us_b2b / wl.L).items() if k != "us"}}}
     # the L launches captured in a HIP graph, replayed back to back (what a
@@ -534,7 +565,7 @@ def main():
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the streaming-rate reference kernels (for profiler runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="before the warm-up, run a plain device copy of this many MiB three times "
+                    help="before the rows and the warm-up, run a plain device copy of this many MiB three times "
                          "(a known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -561,16 +592,23 @@ def main():
     outs = [torch.empty(w.R, w.W, w.H, w.dv, dtype=torch.float32, device=dev) for _ in range(w.L)]
     stream = torch.cuda.current_stream()
 
-    def one_pass(ev=None, flush=None):
-        for t, d in enumerate(steps):
-            if flush is not None:
-                flush()
-            if ev is not None:
-                ev[t][0].record(stream)
-            B.decode_step(store, t, w.W, d.get("parent"), d["q"], d["k"], d["v"], d["alpha"],
-                          d["beta"], o=outs[t], stream=stream)
-            if ev is not None:
-                ev[t][1].record(stream)
+    def one_step(t, ev=None):
+        d = steps[t]
+        B.decode_step(store, t, w.W, d.get("parent"), d["q"], d["k"], d["v"], d["alpha"], d["beta"], o=outs[t],
+                      stream=stream, events=ev)
+
+    def one_pass():
+        for t in range(w.L):
+            one_step(t)
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 18  # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # The other rows run first.  This GPU raises its clocks over the first
     # tens of milliseconds of sustained work (measured: a cold device's first
@@ -621,15 +659,6 @@ def main():
                  + [r for r in pick if r in last])
         done = {name: rows[name]() for name in order}
         row_results = {name: done[name] for name in pick}
-
-    if args.copy_calibration > 0:
-        n = args.copy_calibration << 18  # float32 elements
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     for _ in range(args.warmup):
         one_pass()
@@ -685,28 +714,35 @@ def main():
     torch.cuda.synchronize()
     torch_copy_gbps = 2 * src.numel() * 4 / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
 
-    # Per-launch durations of the decode kernel, from HIP events recorded on
-    # the launch stream around every launch (a second live loop of K passes;
-    # the events themselves add a few microseconds between launches).  A
-    # 1 GiB read-only sweep runs, untimed, before every launch, so that each
-    # launch starts with the 256 MB Infinity Cache holding none of its data
-    # and no dirty line of other work.  A third loop flushes with a 1 GiB copy
-    # instead (whose dirty lines drain during the launch), for comparison.
-    def timed_passes(flush):
-        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(w.L)]
-               for _ in range(args.steps)]
-        _pad(torch, stream)
-        for k in range(args.steps):
-            one_pass(evs[k], flush=flush)
-        torch.cuda.synchronize()
-        return np.array([[e[0].elapsed_time(e[1]) for e in ev] for ev in evs])  # [K, L] ms
+    # Per-launch durations of the decode kernel (a second live loop of K
+    # passes): HIP events on the launch stream that the runtime records as
+    # each kernel starts and completes (gdn_beam_decode_step_timed), created
+    # without the system-scope fence a default event adds, so that they time
+    # the kernel as rocprofv3's kernel trace does.  A 1 GiB read-only sweep
+    # runs, untimed, before every launch, so that each launch starts with the
+    # 256 MB Infinity Cache holding none of its data and no dirty line of
+    # other work.  Beside: the same launches between default event commands
+    # recorded around each (which add their own cost to every launch), and
+    # after a 1 GiB copy instead of the sweep (whose dirty lines drain during
+    # the launch).
+    def timed_passes(flush, kernel=True):
+        if kernel:
+            calls = [(lambda ev, t=t: one_step(t, ev)) for _ in range(args.steps) for t in range(w.L)]
+            us = _queued_kernel(torch, stream, calls, flush=flush)
+        else:
+            calls = [(lambda t=t: one_step(t)) for _ in range(args.steps) for t in range(w.L)]
+            us = _queued(torch, stream, calls, flush=flush)
+        return np.array(us).reshape(args.steps, w.L) * 1e-3  # [K, L] ms
 
-    launch_ms = timed_passes(lambda: _flush(torch))
-    launch_ms_copy = timed_passes(lambda: dst.copy_(src))
+    timed_passes(True)  # untimed round (as in the rows)
+    launch_ms = timed_passes(True)
+    launch_ms_pair = timed_passes(True, kernel=False)
+    launch_ms_copy = timed_passes("copy")
     del src, dst
-    # the floor any event-timed launch pays: a near-empty launch after the
-    # same sweep
-    empty_us = S.empty_launch_us(torch, stream)
+    # what any launch timed the same way costs: a near-empty launch after the
+    # same sweep, bracketed by the runtime, and between event commands
+    empty_us = S.empty_kernel_us(torch, stream)
+    empty_pair_us = S.empty_launch_us(torch, stream)
 
     # algorithmic bytes per launch (unique-record model, from the lineage itself)
     anc = store.anc.cpu().numpy()
@@ -764,13 +800,19 @@ def main():
             "read_fraction": read_frac,
             "mix_matched_GBps": mix_rates,
             "frac_of_mix_matched": mix_s / (float(launch_ms.mean(0).sum()) * 1e-3),
-            "cache": "Infinity Cache flushed (1 GiB read-only sweep) before every event-timed launch",
+            "cache": "Infinity Cache flushed (1 GiB read-only sweep) before every timed launch",
+            "timing": ("kernel time as the runtime brackets each launch (gdn_beam_decode_step_timed: "
+                       "hipExtLaunchKernel events without a system-scope fence), as rocprofv3's kernel "
+                       "trace times it"),
+            "launch_us_event_pair": [float(x) * 1e3 for x in launch_ms_pair.mean(0)],
+            "frac_event_pair": mean_bytes / (float(launch_ms_pair.mean()) * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "launch_us_after_copy_flush": [float(x) * 1e3 for x in launch_ms_copy.mean(0)],
             "traffic": measured_traffic(),
             "bytes_per_launch": mean_bytes,
             "bytes_per_launch_per_beam_gather": float(np.mean(gather_bytes)),
             "launch_us": [float(x) * 1e3 for x in launch_ms.mean(0)],
             "empty_launch_us": empty_us,
+            "empty_launch_us_event_pair": empty_pair_us,
             # the S0^T [q | k] contraction on the matrix cores: three bf16 planes
             # x two probes x 2 d_k d_v FLOP per beam-head, over the same launches
             "mfma_tflops": mfma_flops / mean_launch_s / 1e12,

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GDN_BEAM_ABI_VERSION 5
+#define GDN_BEAM_ABI_VERSION 6
 
 /* status codes */
 #define GDN_OK 0
@@ -152,6 +152,24 @@ int gdn_beam_decode_step(const gdn_shape* shape, const gdn_store* store, int32_t
                          int32_t W_t, const int32_t* parent, const uint16_t* q,
                          const uint16_t* k, const uint16_t* v, const float* alpha,
                          const float* beta, float* o, void* stream);
+
+/*
+ * gdn_beam_decode_step with its kernel time taken by the runtime, for
+ * callers that measure the step (throughput against HBM bandwidth, profiles)
+ * without adding event commands of their own around it.  ev_start and
+ * ev_stop are HIP events (hipEvent_t) created by the caller on the stream's
+ * device, either of them NULL: the runtime records ev_start when the step's
+ * first kernel starts executing and ev_stop when its last kernel completes
+ * (hipExtLaunchKernel), so hipEventElapsedTime(ev_start, ev_stop) is the
+ * step's kernel time alone.  Everything else (arguments, results, errors)
+ * is exactly gdn_beam_decode_step's; with both events NULL the two calls are
+ * the same.
+ */
+int gdn_beam_decode_step_timed(const gdn_shape* shape, const gdn_store* store, int32_t t,
+                               int32_t W_t, const int32_t* parent, const uint16_t* q,
+                               const uint16_t* k, const uint16_t* v, const float* alpha,
+                               const float* beta, float* o, void* stream, void* ev_start,
+                               void* ev_stop);
 
 /*
  * Bounded-log decoding with the merge in the same pass (DeltaLog Figure 4: the

@@ -52,6 +52,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_beam_decode_step.argtypes = [ctypes.POINTER(GdnShape), ctypes.POINTER(GdnStore), I32, I32,
                                            P, P, P, P, P, P, P, P]
         L.gdn_beam_decode_step.restype = ctypes.c_int
+        L.gdn_beam_decode_step_timed.argtypes = [ctypes.POINTER(GdnShape), ctypes.POINTER(GdnStore), I32, I32,
+                                                 P, P, P, P, P, P, P, P, P, P]
+        L.gdn_beam_decode_step_timed.restype = ctypes.c_int
         L.gdn_materialize.argtypes = [ctypes.POINTER(GdnShape), ctypes.POINTER(GdnStore), I32, P, I32, P, P]
         L.gdn_materialize.restype = ctypes.c_int
         L.gdn_log_merge.argtypes = [ctypes.POINTER(GdnShape), ctypes.POINTER(GdnStore), I32, I32, P]
@@ -150,8 +153,10 @@ class Store:
                                _ptr(self.rec_alpha), _ptr(self.anc))
 
 
-def decode_step(store: Store, t, W_t, parent, q, k, v, alpha, beta, o=None, stream=None):
-    """One decode step (gdn_beam_decode_step); returns o [R,W_t,H,dv] FP32."""
+def decode_step(store: Store, t, W_t, parent, q, k, v, alpha, beta, o=None, stream=None, events=None):
+    """One decode step (gdn_beam_decode_step); returns o [R,W_t,H,dv] FP32.
+    ``events``: a pair of HIP event handles (ints) that the runtime records as
+    the step's kernel starts and completes (gdn_beam_decode_step_timed)."""
     R, H, dk, dv, dev = store.R, store.H, store.dk, store.dv, store.device
     _check(q, "q", _BF16, (R, W_t, store.Hk, dk), dev)
     _check(k, "k", _BF16, (R, W_t, store.Hk, dk), dev)
@@ -164,11 +169,14 @@ def decode_step(store: Store, t, W_t, parent, q, k, v, alpha, beta, o=None, stre
     if o is None:
         o = torch.empty(R, W_t, H, dv, dtype=torch.float32, device=dev)
     _check(o, "o", (torch.float32,), (R, W_t, H, dv), dev)
-    rc = lib().gdn_beam_decode_step(ctypes.byref(store.shape), ctypes.byref(store.cstore), t, W_t,
-                                    _ptr(parent) if t > 0 else None, _ptr(q), _ptr(k), _ptr(v),
-                                    _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream, store.device))
+    args = (ctypes.byref(store.shape), ctypes.byref(store.cstore), t, W_t, _ptr(parent) if t > 0 else None,
+            _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream, store.device))
+    if events is None:
+        rc = lib().gdn_beam_decode_step(*args)
+    else:
+        rc = lib().gdn_beam_decode_step_timed(*args, events[0], events[1])
     if rc != GDN_OK:
-        raise GdnError(rc, "gdn_beam_decode_step")
+        raise GdnError(rc, "gdn_beam_decode_step_timed" if events is not None else "gdn_beam_decode_step")
     return o
 
 

@@ -100,6 +100,14 @@ int gdn_beam_decode_step(const gdn_shape* shape, const gdn_store* store, int32_t
                          const int32_t* parent, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, const float* alpha, const float* beta, float* o,
                          void* stream) {
+  return gdn_beam_decode_step_timed(shape, store, t, W_t, parent, q, k, v, alpha, beta, o, stream, nullptr,
+                                    nullptr);
+}
+
+int gdn_beam_decode_step_timed(const gdn_shape* shape, const gdn_store* store, int32_t t, int32_t W_t,
+                               const int32_t* parent, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const float* alpha, const float* beta, float* o,
+                               void* stream, void* ev_start, void* ev_stop) {
   int rc = check_shape(shape);
   if (rc != GDN_OK) return rc;
   if ((rc = check_store(store)) != GDN_OK) return rc;
@@ -111,6 +119,8 @@ int gdn_beam_decode_step(const gdn_shape* shape, const gdn_store* store, int32_t
       !aligned(beta, 16) || !aligned(o, 16))
     return GDN_EINVAL;
   gdn::StepIO io{parent, q, k, v, alpha, beta, o};
+  io.ev_start = static_cast<hipEvent_t>(ev_start);
+  io.ev_stop = static_cast<hipEvent_t>(ev_stop);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 #ifdef GDN_CHECK_PARENTS
   io.bad_parents = bad_parents_on(s);

@@ -1,6 +1,7 @@
 // Internal launch interface between the C ABI (abi.hip) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,7 +21,22 @@ struct StepIO {
   // parent-check builds (GDN_CHECK_PARENTS) only: device counter of parent
   // pointers found outside [0, W_max); null otherwise
   int* bad_parents = nullptr;
+  // timed calls only: events the runtime records as the step's first kernel
+  // starts and as its last kernel completes; null otherwise
+  hipEvent_t ev_start = nullptr;
+  hipEvent_t ev_stop = nullptr;
 };
+
+// Launches a kernel as hipLaunchKernelGGL does; with either timing event
+// set, through hipExtLaunchKernel, which records ev0 as the dispatch starts
+// and ev1 as it completes (no event command of its own in the stream).
+#define GDN_DISPATCH(ev0, ev1, kernel, grid, block, lds, stream, ...)                     \
+  do {                                                                                   \
+    if ((ev0) != nullptr || (ev1) != nullptr)                                            \
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ev0, ev1, 0, __VA_ARGS__); \
+    else                                                                                 \
+      hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                 \
+  } while (0)
 
 // (d_k, d_v) pairs built for a decay kind, and those of the sequence kernel
 bool dims_supported(int dk, int dv, int decay_kind);

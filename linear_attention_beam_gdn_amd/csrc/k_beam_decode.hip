@@ -376,8 +376,8 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, int Wt, const StepIO
   a.nchunk = (Wt + a.chunk - 1) / a.chunk;
   const long grid = (long)sh.R * sh.H * NVS * a.nchunk;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
-  hipLaunchKernelGGL((k_beam_decode<DK, DV, CH, NPL>), dim3((unsigned)grid),
-                     dim3(BeamGeom<DK, DV, CH>::NW * 64), 0, stream, a);
+  GDN_DISPATCH(io.ev_start, io.ev_stop, (k_beam_decode<DK, DV, CH, NPL>), dim3((unsigned)grid),
+               dim3(BeamGeom<DK, DV, CH>::NW * 64), 0, stream, a);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 

@@ -601,7 +601,7 @@ int launch(const gdn_shape& sh, const gdn_store& st, int Wt, const StepIO& io, h
   a.nchunk = (Wt + a.chunk - 1) / a.chunk;
   const long grid = (long)sh.R * sh.H * G::NVS * a.nchunk;
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
-  hipLaunchKernelGGL((k_beam_fused<DK, DV, T>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
+  GDN_DISPATCH(io.ev_start, io.ev_stop, (k_beam_fused<DK, DV, T>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 

@@ -759,11 +759,13 @@ int launch(const gdn_shape& sh, const gdn_store& st, int Wt, const StepIO& io, h
     const char* pair = getenv("GDN_BEAM_PAIR");
     const bool off = pair != nullptr && pair[0] == '0';
     if (!off && a.nchunk == 1 && sh.H % 2 == 0 && grid >= 2L * cus) {
-      hipLaunchKernelGGL((k_beam_fused_kda<DK, DV, T, 2>), dim3((unsigned)(grid / 2)), dim3(G::NT), 0, stream, a);
+      GDN_DISPATCH(io.ev_start, io.ev_stop, (k_beam_fused_kda<DK, DV, T, 2>), dim3((unsigned)(grid / 2)), dim3(G::NT),
+                   0, stream, a);
       return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
     }
   }
-  hipLaunchKernelGGL((k_beam_fused_kda<DK, DV, T, 1>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
+  GDN_DISPATCH(io.ev_start, io.ev_stop, (k_beam_fused_kda<DK, DV, T, 1>), dim3((unsigned)grid), dim3(G::NT), 0, stream,
+               a);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 

@@ -457,12 +457,13 @@ int launch(const gdn_shape& sh, const gdn_store& st, int t, const StepIO& io, fl
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
   if constexpr (PREP == 1) {
     const size_t lds = (size_t)((t + 2) * DK + (((t + 1) * (CH ? DK : 1) + 3) & ~3)) * sizeof(float);
-    hipLaunchKernelGGL((k_seq_prep<DK, CH, PLAIN>), dim3((unsigned)(sh.R * sh.H)), dim3(256), lds, stream, a);
+    GDN_DISPATCH(io.ev_start, (hipEvent_t) nullptr, (k_seq_prep<DK, CH, PLAIN>), dim3((unsigned)(sh.R * sh.H)),
+                 dim3(256), lds, stream, a);
     if (hipGetLastError() != hipSuccess) return GDN_EHIP;
   }
   const size_t lds = (size_t)seq_lds_floats(DK, DV / NS, CH ? DK : 1, t) * sizeof(float);
-  hipLaunchKernelGGL((k_seq_decode<DK, DV, NS, CH, MRG, PLAIN, PREP>), dim3((unsigned)grid),
-                     dim3(SeqGeom<DK, DV / NS>::NT), lds, stream, a);
+  GDN_DISPATCH(PREP == 1 ? (hipEvent_t) nullptr : io.ev_start, io.ev_stop, (k_seq_decode<DK, DV, NS, CH, MRG, PLAIN, PREP>),
+               dim3((unsigned)grid), dim3(SeqGeom<DK, DV / NS>::NT), lds, stream, a);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 

@@ -11,6 +11,7 @@
 // (units is a multiple of UNR, so no access is conditional).
 // Stored values are the xor of the unit's loaded words (a constant pattern
 // when RD = 0), so no load can be dropped.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,12 +55,25 @@ __global__ __launch_bounds__(NT) void k_stream(const u32x4* __restrict__ src, u3
   }
 }
 
-template <int RD, int WR>
-int run(const void* src, void* dst, long long units, int n_wg, bool nts, hipStream_t s) {
-  if (nts)
-    hipLaunchKernelGGL((k_stream<RD, WR, true>), dim3(n_wg), dim3(NT), 0, s, (const u32x4*)src, (u32x4*)dst, units);
+// one launch; with either event set, the runtime records ev0 as the kernel
+// starts and ev1 as it completes (hipExtLaunchKernel)
+template <bool NTS, int RD, int WR>
+void dispatch(const void* src, void* dst, long long units, int n_wg, hipStream_t s, hipEvent_t ev0,
+              hipEvent_t ev1) {
+  if (ev0 != nullptr || ev1 != nullptr)
+    hipExtLaunchKernelGGL((k_stream<RD, WR, NTS>), dim3(n_wg), dim3(NT), 0, s, ev0, ev1, 0, (const u32x4*)src,
+                          (u32x4*)dst, units);
   else
-    hipLaunchKernelGGL((k_stream<RD, WR, false>), dim3(n_wg), dim3(NT), 0, s, (const u32x4*)src, (u32x4*)dst, units);
+    hipLaunchKernelGGL((k_stream<RD, WR, NTS>), dim3(n_wg), dim3(NT), 0, s, (const u32x4*)src, (u32x4*)dst, units);
+}
+
+template <int RD, int WR>
+int run(const void* src, void* dst, long long units, int n_wg, bool nts, hipStream_t s, hipEvent_t ev0,
+        hipEvent_t ev1) {
+  if (nts)
+    dispatch<true, RD, WR>(src, dst, units, n_wg, s, ev0, ev1);
+  else
+    dispatch<false, RD, WR>(src, dst, units, n_wg, s, ev0, ev1);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
@@ -71,16 +85,19 @@ extern "C" {
 // WR 4-KiB writes to `dst` (so src holds units*rd*4096 bytes and dst
 // units*wr*4096 bytes, both 16-byte aligned device memory owned by the
 // caller; with wr = 0, dst must still hold 4096 bytes; units a multiple of 4), on n_wg workgroups; nontemporal != 0 marks the stores
-// non-temporal.  Returns 0, -1 for a mix that is not built or a bad size, -3
-// if the launch failed.
-int gdn_stream_run(int rd, int wr, const void* src, void* dst, long long units, int n_wg, int nontemporal,
-                   void* stream) {
+// non-temporal.  ev_start and ev_stop (HIP events, either may be null) are
+// recorded by the runtime as the kernel starts and completes; gdn_stream_run
+// is the same launch without them.  Returns 0, -1 for a mix that is not
+// built or a bad size, -3 if the launch failed.
+int gdn_stream_run_timed(int rd, int wr, const void* src, void* dst, long long units, int n_wg,
+                         int nontemporal, void* stream, void* ev_start, void* ev_stop) {
   if (units < 0 || units % UNR != 0 || n_wg < 1 || (rd > 0 && src == nullptr) || dst == nullptr) return -1;
   if (units == 0) return 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool nts = nontemporal != 0;
+  hipEvent_t ev0 = static_cast<hipEvent_t>(ev_start), ev1 = static_cast<hipEvent_t>(ev_stop);
 #define GDN_MIX(R_, W_) \
-  if (rd == R_ && wr == W_) return run<R_, W_>(src, dst, units, n_wg, nts, s);
+  if (rd == R_ && wr == W_) return run<R_, W_>(src, dst, units, n_wg, nts, s, ev0, ev1);
   GDN_MIX(1, 0)
   GDN_MIX(0, 1)
   GDN_MIX(1, 2)
@@ -92,6 +109,37 @@ int gdn_stream_run(int rd, int wr, const void* src, void* dst, long long units, 
   GDN_MIX(2, 1)
 #undef GDN_MIX
   return -1;
+}
+
+int gdn_stream_run(int rd, int wr, const void* src, void* dst, long long units, int n_wg, int nontemporal,
+                   void* stream) {
+  return gdn_stream_run_timed(rd, wr, src, dst, units, n_wg, nontemporal, stream, nullptr, nullptr);
+}
+
+// Timing events for kernel-bracketing measurements (the decode library's
+// gdn_beam_decode_step_timed and gdn_stream_run_timed): created without the
+// system-scope fence a default event performs when it is recorded, which
+// would write back and invalidate caches inside the measured interval.
+// Nothing synchronises with them but hipEventSynchronize.  Null on failure.
+void* gdn_timing_event_create(void) {
+  hipEvent_t e = nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
+  return e;
+}
+
+void gdn_timing_event_destroy(void* ev) {
+  if (ev != nullptr) (void)hipEventDestroy(static_cast<hipEvent_t>(ev));
+}
+
+// Microseconds from `start` to `stop` once `stop` has been recorded (waits
+// for it); negative if either event has not been recorded or on error.
+double gdn_timing_elapsed_us(void* start, void* stop) {
+  if (start == nullptr || stop == nullptr) return -1.0;
+  if (hipEventSynchronize(static_cast<hipEvent_t>(stop)) != hipSuccess) return -1.0;
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)) != hipSuccess)
+    return -1.0;
+  return 1e3 * (double)ms;
 }
 
 }  // extern "C"

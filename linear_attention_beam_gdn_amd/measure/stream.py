@@ -33,6 +33,16 @@ def lib():
         L.gdn_stream_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         L.gdn_stream_run.restype = ctypes.c_int
+        L.gdn_stream_run_timed.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+        L.gdn_stream_run_timed.restype = ctypes.c_int
+        L.gdn_timing_event_create.argtypes = []
+        L.gdn_timing_event_create.restype = ctypes.c_void_p
+        L.gdn_timing_event_destroy.argtypes = [ctypes.c_void_p]
+        L.gdn_timing_event_destroy.restype = None
+        L.gdn_timing_elapsed_us.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.gdn_timing_elapsed_us.restype = ctypes.c_double
         _lib = L
     return _lib
 
@@ -111,10 +121,65 @@ class ReadFlush:
 
 
 
+class KernelEvents:
+    """HIP event pairs for kernel-bracketing timing: handed to a launch
+    (gdn_beam_decode_step_timed, gdn_stream_run_timed), the runtime records
+    the first as the kernel starts and the second as it completes, so their
+    difference is the kernel's execution alone, with no event command in the
+    stream and no system-scope fence (see gdn_timing_event_create)."""
+
+    def __init__(self, n):
+        self.pairs = []
+        for _ in range(n):
+            a, b = lib().gdn_timing_event_create(), lib().gdn_timing_event_create()
+            if not a or not b:
+                self.close()
+                raise RuntimeError("gdn_timing_event_create failed")
+            self.pairs.append((a, b))
+
+    def elapsed_us(self):
+        """Microseconds of every pair, in order (waits for each)."""
+        out = []
+        for a, b in self.pairs:
+            us = lib().gdn_timing_elapsed_us(a, b)
+            if us < 0:
+                raise RuntimeError("gdn_timing_elapsed_us failed (an event pair was not recorded)")
+            out.append(us)
+        return out
+
+    def close(self):
+        for a, b in self.pairs:
+            lib().gdn_timing_event_destroy(a)
+            lib().gdn_timing_event_destroy(b)
+        self.pairs = []
+
+
+def empty_kernel_us(torch, stream, reps=20, workgroups=256):
+    """Median kernel time, as the runtime brackets it (KernelEvents), of a
+    launch that does almost nothing (256 workgroups reading 16 KiB), each
+    after the read-only sweep: what any kernel launched this way costs."""
+    flush = ReadFlush(torch)
+    src = torch.zeros(4 * UNIT // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty(1024, dtype=torch.float32, device="cuda")
+    h = ctypes.c_void_p(stream.cuda_stream)
+    ev = KernelEvents(reps)
+    try:
+        for a, b in ev.pairs:
+            flush(stream)
+            rc = lib().gdn_stream_run_timed(1, 0, src.data_ptr(), dst.data_ptr(), 4, workgroups, 0, h, a, b)
+            if rc != 0:
+                raise RuntimeError(f"gdn_stream_run_timed(1, 0) returned {rc}")
+        times = ev.elapsed_us()
+    finally:
+        ev.close()
+    del flush
+    return sorted(times)[len(times) // 2]
+
+
 def empty_launch_us(torch, stream, reps=20, workgroups=256):
-    """Median time between HIP events around a launch that does almost
-    nothing (256 workgroups reading 16 KiB), each after the read-only sweep:
-    the floor that an event-timed launch of any kernel pays."""
+    """Median time between HIP events recorded around a launch that does
+    almost nothing (256 workgroups reading 16 KiB), each after the read-only
+    sweep: the floor that a launch timed with its own event pair pays."""
     flush = ReadFlush(torch)
     src = torch.zeros(4 * UNIT // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty(1024, dtype=torch.float32, device="cuda")
@@ -135,8 +200,8 @@ def empty_launch_us(torch, stream, reps=20, workgroups=256):
 
 
 def main():
-    """Prints the best rate of every mix as a markdown table, and the
-    event-timed floor of a launch."""
+    """Prints the best rate of every mix as a markdown table, and what a
+    near-empty launch costs, timed both ways."""
     import torch
 
     torch.cuda.set_device(0)
@@ -148,8 +213,9 @@ def main():
         rd, wr = key[1:].split("w")
         print(f"| {rd}:{wr} | {v['read_fraction']:.3f} | {v['GBps']:.0f} | {v['GBps'] / 8000:.3f} | "
               f"{v['workgroups']} | {'yes' if v['nontemporal_stores'] else 'no'} |", flush=True)
-    print(f"\nA launch of 256 workgroups reading 16 KiB, between HIP events after the read-only sweep: "
-          f"{empty_launch_us(torch, stream):.1f} us (median of 20).", flush=True)
+    print(f"\nA launch of 256 workgroups reading 16 KiB, after the read-only sweep: {empty_kernel_us(torch, stream):.1f} us "
+          f"as the runtime brackets the kernel, {empty_launch_us(torch, stream):.1f} us between HIP events recorded "
+          f"around it (medians of 20).", flush=True)
 
 
 if __name__ == "__main__":

@@ -29,11 +29,13 @@ def store(**kw):
 
 
 def decode(L, sh=None, st=None, t=1, W_t=4, parent=FAKE, q=FAKE, k=FAKE, v=FAKE, alpha=FAKE,
-           beta=FAKE, o=FAKE):
+           beta=FAKE, o=FAKE, timed=False):
     sh = shape() if sh is None else sh
     st = store() if st is None else st
-    return L.gdn_beam_decode_step(ctypes.byref(sh), ctypes.byref(st), t, W_t, parent, q, k, v,
-                                  alpha, beta, o, None)
+    args = (ctypes.byref(sh), ctypes.byref(st), t, W_t, parent, q, k, v, alpha, beta, o, None)
+    if timed:  # event handles that are never used: validation fails first
+        return L.gdn_beam_decode_step_timed(*args, FAKE, FAKE)
+    return L.gdn_beam_decode_step(*args)
 
 
 def test_exports_every_header_function(L):
@@ -41,7 +43,7 @@ def test_exports_every_header_function(L):
     assert set(names) == {"gdn_beam_decode_step", "gdn_decode_merge_step", "gdn_materialize",
                           "gdn_log_merge", "gdn_status_string", "gdn_abi_version",
                           "gdn_split_workspace_bytes", "gdn_decode_step_split",
-                          "gdn_decode_step_split_noalloc"}
+                          "gdn_decode_step_split_noalloc", "gdn_beam_decode_step_timed"}
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
@@ -51,44 +53,51 @@ def test_exports_every_header_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gdn_abi_version() == 5
+    assert L.gdn_abi_version() == 6
     for s in (B.GDN_OK, B.GDN_EINVAL, B.GDN_EUNSUPPORTED, B.GDN_EHIP, B.GDN_ESCRATCH, 12345):
         assert isinstance(B.status_string(s), str) and B.status_string(s)
 
 
-def test_decode_validation(L):
+@pytest.mark.parametrize("timed", [False, True], ids=["untimed", "timed"])
+def test_decode_validation(L, timed):
+    """gdn_beam_decode_step and gdn_beam_decode_step_timed reject the same
+    arguments with the same codes."""
     E, U = B.GDN_EINVAL, B.GDN_EUNSUPPORTED
     P = ctypes.POINTER
-    assert L.gdn_beam_decode_step(P(B.GdnShape)(), ctypes.byref(store()), 0, 1, FAKE, FAKE, FAKE,
-                                  FAKE, FAKE, FAKE, FAKE, None) == E
-    assert L.gdn_beam_decode_step(ctypes.byref(shape()), P(B.GdnStore)(), 0, 1, FAKE, FAKE, FAKE,
-                                  FAKE, FAKE, FAKE, FAKE, None) == E
-    assert decode(L, sh=shape(R=0)) == E
-    assert decode(L, sh=shape(H=0)) == E
-    assert decode(L, sh=shape(L_max=0)) == E
-    assert decode(L, sh=shape(L_max=B.GDN_MAX_STEPS + 1)) == E
-    assert decode(L, sh=shape(dk=96, dv=96)) == U
-    assert decode(L, sh=shape(dk=128, dv=64)) == U
-    assert decode(L, sh=shape(dk=256, dv=64)) == U
-    assert decode(L, sh=shape(dk=512, dv=512)) == U
-    assert decode(L, sh=shape(dk=256, dv=128, decay_kind=1)) == U  # channel decay: d_k = 128 only
-    assert decode(L, sh=shape(dk=128, dv=256, decay_kind=2, W_max=1)) == U  # plain: square only
-    assert decode(L, sh=shape(decay_kind=2)) == U  # the plain (RWKV6) rule: sequences only
-    assert decode(L, sh=shape(decay_kind=3)) == U
-    assert decode(L, sh=shape(H=4, H_k=3)) == E  # key heads must divide the value heads
-    assert decode(L, sh=shape(H_k=-1)) == E
-    assert decode(L, t=-1) == E
-    assert decode(L, t=4) == E
-    assert decode(L, W_t=0) == E
-    assert decode(L, W_t=9) == E
-    assert decode(L, t=1, parent=None) == E
-    assert decode(L, t=1, parent=FAKE + 2) == E
+    fn = L.gdn_beam_decode_step_timed if timed else L.gdn_beam_decode_step
+    ev = (FAKE, FAKE) if timed else ()
+    assert fn(P(B.GdnShape)(), ctypes.byref(store()), 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, *ev) == E
+    assert fn(ctypes.byref(shape()), P(B.GdnStore)(), 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, *ev) == E
+
+    def dec(L, **kw):
+        return decode(L, timed=timed, **kw)
+
+    assert dec(L, sh=shape(R=0)) == E
+    assert dec(L, sh=shape(H=0)) == E
+    assert dec(L, sh=shape(L_max=0)) == E
+    assert dec(L, sh=shape(L_max=B.GDN_MAX_STEPS + 1)) == E
+    assert dec(L, sh=shape(dk=96, dv=96)) == U
+    assert dec(L, sh=shape(dk=128, dv=64)) == U
+    assert dec(L, sh=shape(dk=256, dv=64)) == U
+    assert dec(L, sh=shape(dk=512, dv=512)) == U
+    assert dec(L, sh=shape(dk=256, dv=128, decay_kind=1)) == U  # channel decay: d_k = 128 only
+    assert dec(L, sh=shape(dk=128, dv=256, decay_kind=2, W_max=1)) == U  # plain: square only
+    assert dec(L, sh=shape(decay_kind=2)) == U  # the plain (RWKV6) rule: sequences only
+    assert dec(L, sh=shape(decay_kind=3)) == U
+    assert dec(L, sh=shape(H=4, H_k=3)) == E  # key heads must divide the value heads
+    assert dec(L, sh=shape(H_k=-1)) == E
+    assert dec(L, t=-1) == E
+    assert dec(L, t=4) == E
+    assert dec(L, W_t=0) == E
+    assert dec(L, W_t=9) == E
+    assert dec(L, t=1, parent=None) == E
+    assert dec(L, t=1, parent=FAKE + 2) == E
     for name in ("q", "k", "v", "alpha", "beta", "o"):
-        assert decode(L, **{name: None}) == E, name
-        assert decode(L, **{name: FAKE + 8}) == E, name
+        assert dec(L, **{name: None}) == E, name
+        assert dec(L, **{name: FAKE + 8}) == E, name
     for name in ("S", "rec_delta", "rec_k", "rec_alpha", "anc"):
-        assert decode(L, st=store(**{name: None})) == E, name
-        assert decode(L, st=store(**{name: FAKE + 4})) == E, name
+        assert dec(L, st=store(**{name: None})) == E, name
+        assert dec(L, st=store(**{name: FAKE + 4})) == E, name
 
 
 def test_materialize_and_merge_validation(L):
