@@ -664,9 +664,13 @@ def main():
         one_pass()
     torch.cuda.synchronize()
 
-    # Timed region: K passes back to back, bracketed by synchronisation.
+    # Timed region: K passes back to back, bracketed by synchronisation.  The
+    # untimed pad ahead of the start event lets the host queue the first
+    # launches before the GPU reaches them, so the host's latency in issuing
+    # the first launch is not inside the region.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    _pad(torch, stream)
     start.record(stream)
     for _ in range(args.steps):
         one_pass()
@@ -685,6 +689,7 @@ def main():
         graph.replay()
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    _pad(torch, stream)
     g0.record(stream)
     for _ in range(args.steps):
         graph.replay()
