@@ -114,26 +114,39 @@ typedef struct gdn_store {
   uint16_t* rec_k;   /* [L_max][R][W_max][H_k][dk]  bf16 keys (bit copies)   */
   float* rec_alpha;  /* [L_max][R][W_max][H][A]   FP32 decays                */
   int32_t* anc;      /* [L_max][R][W_max][L_max]  ancestry: anc[t][r][b][j] =
-                        h_t(b, j), j < t.  The decode step may keep in the
-                        last entry, anc[t][r][b][L_max-1], the beam's
-                        position in the depth-first order of the beam tree
-                        (read by step t+1 to schedule beams that share
-                        ancestors together; any value there only affects
-                        speed, never results).  Other entries j >= t are
-                        unused.                                               */
+                        h_t(b, j), j < t: the record slot, at step j, of
+                        beam b's ancestor there.  The last entry,
+                        anc[t][r][b][L_max-1] (t >= 1), is the beam's order
+                        key at step t: its position in the depth-first order
+                        of the beam tree (when a request's beams are
+                        decoded by one workgroup) or its index.  Other
+                        entries j >= t are unused.                            */
 } gdn_store;
+
+/*
+ * Record slots.  Step t stores the record of beam b of request r at slot
+ * (t, r, s): with scalar decay and W_max > 1, s is the beam's order key
+ * anc[t][r][b][L_max-1] for t >= 1 (a permutation of 0 .. W_t-1 over the
+ * step's beams, so that later steps, which take beams in that order, gather
+ * each step's records in increasing slot order) and b at t == 0; with
+ * channel decay, and with W_max == 1, s = b.  The ancestry rows hold slots;
+ * an ancestor's beam index at step j is the beam whose order key there is
+ * that slot.
+ */
 
 /*
  * One decode step t for all R requests, W_t beams and H heads (OneLA §3.3,
  * §3.4; replay equations of §3.2).  In one kernel:
- *   1. ancestry: h_t(b, t-1) = parent[r][b], h_t(b, j) = h_{t-1}(parent, j)
- *      for j < t-1, written to anc[t][r][b][0..t-1] (skipped at t == 0);
+ *   1. ancestry: h_t(b, t-1) = the record slot of parent[r][b] at step t-1,
+ *      h_t(b, j) = h_{t-1}(parent, j) for j < t-1, written to
+ *      anc[t][r][b][0..t-1] with the beam's order key (skipped at t == 0);
  *   2. u_q = S[r]^T q and u_k = S[r]^T k for every beam (for channel decay
  *      the probes are (prod_{i<=t} a_i) * q and * k over the beam's chain);
  *   3. replay of the records at (j, h_t(b, j)), j < t, on u_q and u_k;
  *   4. delta_t = beta_t (v_t - alpha_t u_k), o_t = alpha_t u_q +
  *      delta_t (k_t . q_t) (channel decay: alpha_t sits in the probes);
- *   5. writes o and appends (alpha_t, delta_t, k_t) at slot (t, r, b).
+ *   5. writes o (at the beam's index) and appends (alpha_t, delta_t, k_t)
+ *      at the beam's record slot (see "Record slots").
  * Records of steps j < t are only read.
  *
  *   t       step index, 0 <= t < L_max; the chain of step t has t records

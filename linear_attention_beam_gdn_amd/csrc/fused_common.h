@@ -89,13 +89,21 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 //   next step.
 // The order only decides which lanes compute a beam, never its result.
 //
+// Record slots.  With KEY_SLOTS (the scalar-decay kernel) a step stores each
+// beam's record at the beam's order key (its position in the step's order,
+// the last entry of its ancestry row) rather than at its index, so the slots
+// an ancestry row holds are keys: a parent's slot is the key read from its
+// row.  The tiles of a step follow its order, so they gather every depth's
+// records in increasing slot order.  At step 0 (no order) a beam's key is
+// its index.  Without KEY_SLOTS records stay at the beam's index.
+//
 // Memory: the parent pointers and, for T >= 2, the whole previous-step
 // ancestry block of the request (W_max x L_max entries, staged into LDS by
 // LDS DMA when it fits in `scratch`) are fetched in one batch; `mid()` runs
 // once they have arrived (the caller's workgroup barrier), and the sort
 // follows.  `scratch` (scratch_bytes, 16-byte aligned) holds the bucket
 // counts and the staged block and is free for other use afterwards.
-template <int T, class Mid>
+template <int T, bool KEY_SLOTS, class Mid>
 __device__ __forceinline__ void build_schedule(const BeamArgs& a, int r, bool anc_writer, int b_begin, int nb, int lane,
                                                int scratch_bytes, uint8_t* scratch, u32x4* s_tab, int* s_slot_hi,
                                                Mid mid) {
@@ -140,6 +148,7 @@ __device__ __forceinline__ void build_schedule(const BeamArgs& a, int r, bool an
 #pragma unroll
         for (int j = 0; j < T - 1; ++j) slot[qi][j] = clampi(prow[j], 0, a.Wm - 1);
         key[qi] = clampi(prow[a.L - 1], 0, a.Wm - 1);
+        if constexpr (KEY_SLOTS) slot[qi][TT - 1] = key[qi];
       }
     } else {
 #pragma unroll
@@ -148,6 +157,7 @@ __device__ __forceinline__ void build_schedule(const BeamArgs& a, int r, bool an
 #pragma unroll
         for (int j = 0; j < T - 1; ++j) slot[qi][j] = clampi(prow[j], 0, a.Wm - 1);
         key[qi] = clampi(prow[a.L - 1], 0, a.Wm - 1);
+        if constexpr (KEY_SLOTS) slot[qi][TT - 1] = key[qi];
       }
     }
   } else {

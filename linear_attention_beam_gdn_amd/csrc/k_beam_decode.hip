@@ -114,10 +114,17 @@ __global__ __launch_bounds__((BeamGeom<DK, DV, CH>::NW * 64)) void k_beam_decode
       par = clampi(raw, 0, a.Wm - 1);
     }
     const int32_t* prow = a.anc + (((size_t)(t > 0 ? t - 1 : 0) * a.R + r) * a.Wm + par) * a.L;
+    // Record slots: with scalar decay a step's records sit at the beams'
+    // order keys (the last entry of their ancestry rows: this kernel takes
+    // beams in index order, so its key is the index; the fused kernel's is
+    // the beam's depth-first position), so the parent's slot is the key in
+    // its row; at step 0 and with channel decay a slot is the beam index.
     auto slot_at = [&](int j) -> int {
       if (!valid) return 0;
-      return j == t - 1 ? par : clampi(prow[j], 0, a.Wm - 1);
+      if (j == t - 1) return (!CH && t >= 2) ? clampi(prow[a.L - 1], 0, a.Wm - 1) : par;
+      return clampi(prow[j], 0, a.Wm - 1);
     };
+    if (anc_writer && valid) a.anc[(((size_t)t * a.R + r) * a.Wm + b) * a.L + a.L - 1] = b;  // this step's key
     auto rec_at = [&](int j, int slot) -> size_t {
       return (((size_t)j * a.R + r) * a.Wm + slot) * a.H + h;
     };

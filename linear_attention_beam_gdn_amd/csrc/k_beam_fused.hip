@@ -41,8 +41,9 @@
 //   product is exact; FP32 accumulation), the replay on its value rows with
 //   the ancestral update vectors delta_j (loaded into registers one tile
 //   ahead, each wave its own rows), then delta_t and o_t, stored with 64-byte
-//   contiguous writes per beam, plus the appended record (by the first value
-//   slice).  Two waves per SIMD hide each other's latencies.
+//   contiguous writes per beam (o at the beam's index, delta_t at its slot),
+//   plus the appended record (by the first value slice).  Two waves per SIMD
+//   hide each other's latencies.
 //
 // Schedule.  With one chunk per (r, h), the beams are taken in the depth-
 // first order of the beam tree (lexicographic in their ancestry rows), so that
@@ -52,7 +53,9 @@
 // the otherwise unused last entry of its ancestry rows; one wave sorts with a
 // counting sort in LDS.  The order only decides which tile and lane computes
 // a beam: every beam's arithmetic, and so its result, is the same in any
-// order.
+// order.  A step stores its records at the beams' positions in that order
+// (their keys), and the ancestry rows hold those slots, so the next steps'
+// tiles gather each depth's records in increasing slot order.
 //
 // LDS tile layout ("beam fastest"): a 16-row array with NCH 16-byte chunks
 // per row keeps chunk ch of row b at 16-byte slot (ch/4)*64 + (ch%4)*16 + b.
@@ -199,7 +202,7 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     };
     if (T > 0) {
       if (dw == 0) {
-        build_schedule<T>(a, r, h == 0 && slice0, b_begin, nb, lane, G::OS0, smem, s_tab, s_slot_hi,
+        build_schedule<T, true>(a, r, h == 0 && slice0, b_begin, nb, lane, G::OS0, smem, s_tab, s_slot_hi,
                           [] { lds_barrier(); });  // Q inside, once its loads have arrived
       } else {
         lds_barrier();  // Q
@@ -537,13 +540,17 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     }
 
     // output and append (§3.4): every wave issues the same four stores; a
-    // position past the chunk stores outside the windows
+    // position past the chunk stores outside the windows.  o goes to the
+    // beam's index, the record to its position in the step's order (its
+    // key: record slots follow the order, so the next steps gather them in
+    // increasing slot order)
     const int posi = it * 16 + c;
     const bool live = posi < nb;
     const int ib = live ? (T > 0 ? (int)s_tab[posi][0] : posi) : 0;
     const int off_o = live ? ib * so + row0 * 4 : kOutside;
+    const int off_r = live ? posi * so + row0 * 4 : kOutside;
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, off_o, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, off_o, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, off_r, 0, 0);
     u32x4 kk;
     if constexpr (kBInLoop) {
       kk = *reinterpret_cast<const u32x4*>(buf + G::OKK + (ks * 64 + lane) * 16);
@@ -553,14 +560,14 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
       for (int s = 1; s < KS; ++s)
         if (ks == s) kk = kf[s];
     }
-    const int off_k = live && key_writer && slice0 ? ib * sk + (ks * 32 + g * 8 + kh * 4) * 2 : kOutside;
+    const int off_k = live && key_writer && slice0 ? posi * sk + (ks * 32 + g * 8 + kh * 4) * 2 : kOutside;
     if constexpr (G::NC == 2 * KS)
       __builtin_amdgcn_raw_buffer_store_b64(kh ? u32x2{kk[2], kk[3]} : u32x2{kk[0], kk[1]}, w_k, off_k, 0, 0);
     else
       __builtin_amdgcn_raw_buffer_store_b128(kk, w_k, off_k, 0, 0);
     const float at = *reinterpret_cast<const float*>(buf + G::OS + c * 4);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(at), w_a,
-                                          (live && slice0 && w == G::NC - 1 && g == 0) ? ib * sa : kOutside, 0, 0);
+                                          (live && slice0 && w == G::NC - 1 && g == 0) ? posi * sa : kOutside, 0, 0);
     const unsigned long long c1 = stamp_now();
     lds_barrier();  // it + 1
     c_busy += c1 - c0;

@@ -101,12 +101,15 @@ void k_fold(FoldArgs a) {
   float* ld = lk + n * DK;      // [n][DV] update vectors
   float* la = ld + n * DV;      // [n][A] decays
   const int32_t* arow = a.anc + (((size_t)t * a.R + r) * a.Wm + b) * a.L;
+  // the beam's own record: at its order key (the last entry of its ancestry
+  // row) for scalar decay with beams after step 0, else at its index
+  const int own = (!CH && a.Wm > 1 && t > 0) ? clampi(arow[a.L - 1], 0, a.Wm - 1) : b;
   auto rec_at = [&](int j) -> size_t {
-    const int slot = j < t ? clampi(arow[j], 0, a.Wm - 1) : b;
+    const int slot = j < t ? clampi(arow[j], 0, a.Wm - 1) : own;
     return (((size_t)j * a.R + r) * a.Wm + slot) * a.H + h;
   };
   auto rec_at_k = [&](int j) -> size_t {
-    const int slot = j < t ? clampi(arow[j], 0, a.Wm - 1) : b;
+    const int slot = j < t ? clampi(arow[j], 0, a.Wm - 1) : own;
     return (((size_t)j * a.R + r) * a.Wm + slot) * a.Hk + h / a.gq;
   };
   const int nk = n * G::KCH, nd = UB16 ? n * G::VCH : n * G::DCH;

@@ -62,10 +62,34 @@ def run_beam(inp, channel=False, L_max=None, W_max=None, S=None):
     return store, [o.cpu().numpy() for o in outs]
 
 
-def step_records(store, t, W_t):
-    """(delta [R,W_t,H,dv], k bits [R,W_t,Hk,dk], alpha, anc [R,W_t,t]) at step t."""
-    d = store.rec_delta[t, :, :W_t].cpu().numpy()
-    k = store.rec_k[t, :, :W_t].view(torch.int16).cpu().numpy().view(np.uint16)
-    a = store.rec_alpha[t, :, :W_t].cpu().numpy()
-    anc = store.anc[t, :, :W_t, :t].cpu().numpy()
-    return d, k, a, anc
+def record_slots(store, t, W_t):
+    """[R, W_t] record slot of each beam at step t: with scalar decay and
+    beams (W_max > 1) a step stores a beam's record at its order key, the
+    last entry of its ancestry row, from step 1 on; otherwise at its index."""
+    idx = np.tile(np.arange(W_t, dtype=np.int64), (store.R, 1))
+    if t == 0 or store.channel_decay or store.W_max == 1:
+        return idx
+    keys = store.anc[t, :, :W_t, store.L_max - 1].cpu().numpy().astype(np.int64)
+    for r in range(store.R):  # the keys of a step's beams are a permutation of its slots
+        assert np.array_equal(np.sort(keys[r]), np.arange(W_t)), f"step {t}: order keys are not a permutation"
+    return keys
+
+
+def step_records(store, t, W_t, widths=None):
+    """(delta [R,W_t,H,dv], k bits [R,W_t,Hk,dk], alpha, anc [R,W_t,t]) at
+    step t, per beam index: each beam's record read at its slot, and the
+    ancestry rows' slots mapped back to the ancestors' beam indices (the
+    pages' h_t).  ``widths``: W_j of every step j <= t (default W_t)."""
+    widths = [W_t] * (t + 1) if widths is None else list(widths)
+    sl = record_slots(store, t, W_t)
+    rows = np.arange(store.R)[:, None]
+    d = store.rec_delta[t].cpu().numpy()[rows, sl]
+    k = store.rec_k[t].view(torch.int16).cpu().numpy().view(np.uint16)[rows, sl]
+    a = store.rec_alpha[t].cpu().numpy()[rows, sl]
+    anc = store.anc[t, :, :W_t, :t].cpu().numpy().astype(np.int64)
+    for j in range(t):
+        slj = record_slots(store, j, widths[j])
+        inv = np.full((store.R, store.W_max), -1, np.int64)
+        inv[rows, slj] = np.arange(widths[j])[None, :]
+        anc[:, :, j] = inv[rows, anc[:, :, j]]
+    return d, k, a, anc.astype(np.int32)

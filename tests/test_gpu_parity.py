@@ -28,7 +28,7 @@ def check_beam(inp, channel, requests=None, heads=None, label="", **run_kw):
     worst = 0.0
     for t, st in enumerate(inp["steps"]):
         W_t = st["q"].shape[1]
-        d, kbits, a, anc = step_records(store, t, W_t)
+        d, kbits, a, anc = step_records(store, t, W_t, [s_["q"].shape[1] for s_ in inp["steps"][:t + 1]])
         assert np.array_equal(anc, ref["anc"][t]), f"{label}: ancestry differs at t={t}"
         assert np.array_equal(kbits, st["k"]), f"{label}: record keys differ at t={t}"
         assert np.array_equal(a.reshape(st["alpha"].shape), st["alpha"]), f"{label}: decays t={t}"
@@ -573,6 +573,42 @@ def test_materialize(channel):
         err = rel_states(S, ref)
         log(f"[parity] materialize t={t} ch={channel}: {err:.2e}")
         assert err <= TOL
+
+
+@pytest.mark.parametrize("dims", [(128, 128), (64, 64)])
+def test_kernels_mixed_on_one_store(dims, monkeypatch):
+    """Scalar-decay beam steps alternate between the fused kernel (records at
+    the beams' depth-first positions) and the general kernel (records at the
+    beams' indices) on one store, with a hot parent so that the order is far
+    from the index order: every step, the ancestry and the records still
+    match the oracle, and so do states materialised from the store."""
+    dk, dv = dims
+    inp = synth.make_inputs(R=2, H=3, dk=dk, dv=dv, W=96, L=6, s0_std=0.05, seed=31, parents="topk_hot")
+    S0 = inp["S0"]
+    store = B.Store(2, 96, 3, dk, dv, 6, S=torch.from_numpy(S0).cuda())
+    outs = []
+    for t, st in enumerate(inp["steps"]):
+        if t % 2:
+            monkeypatch.setenv("GDN_BEAM_GENERIC", "1")
+        else:
+            monkeypatch.delenv("GDN_BEAM_GENERIC", raising=False)
+        d = B.upload(st)
+        outs.append(B.decode_step(store, t, 96, d.get("parent"), d["q"], d["k"], d["v"], d["alpha"], d["beta"]))
+    monkeypatch.delenv("GDN_BEAM_GENERIC", raising=False)
+    torch.cuda.synchronize()
+    ref = O.beam_decode(S0, inp["steps"])
+    for t, st in enumerate(inp["steps"]):
+        d, kbits, a, anc = step_records(store, t, 96)
+        assert np.array_equal(anc, ref["anc"][t]), t
+        assert np.array_equal(kbits, st["k"]), t
+        eo, ed = rel_slices(outs[t].cpu().numpy(), ref["o"][t]), rel_slices(d, ref["delta"][t])
+        assert eo <= TOL and ed <= TOL, (t, eo, ed)
+    pairs = [(0, 0), (1, 95), (0, 41), (1, 7)]
+    rb = torch.tensor(pairs, dtype=torch.int32, device="cuda")
+    for t in range(6):
+        err = rel_states(B.materialize(store, t, rb).cpu().numpy(), O.beam_states(S0, inp["steps"], t, pairs))
+        assert err <= TOL, (t, err)
+    log(f"[parity] fused and general kernels on one store, d = {dk}: ok")
 
 
 def test_merge_of_beam_chain():

@@ -111,7 +111,7 @@ def _check_geometry(case):
     worst = 0.0
     for t, st in enumerate(inp["steps"]):
         W_t = st["q"].shape[1]
-        d, kbits, a, anc = step_records(store, t, W_t)
+        d, kbits, a, anc = step_records(store, t, W_t, [s_["q"].shape[1] for s_ in inp["steps"][:t + 1]])
         assert np.array_equal(anc, ref["anc"][t]), f"{label}: ancestry differs at t={t}"
         assert np.array_equal(kbits, st["k"]), f"{label}: record keys differ at t={t}"
         assert np.array_equal(a.reshape(st["alpha"].shape), st["alpha"]), f"{label}: decays differ at t={t}"
