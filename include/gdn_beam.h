@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GDN_BEAM_ABI_VERSION 6
+#define GDN_BEAM_ABI_VERSION 7
 
 /* status codes */
 #define GDN_OK 0

@@ -53,7 +53,7 @@ def test_exports_every_header_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gdn_abi_version() == 6
+    assert L.gdn_abi_version() == 7
     for s in (B.GDN_OK, B.GDN_EINVAL, B.GDN_EUNSUPPORTED, B.GDN_EHIP, B.GDN_ESCRATCH, 12345):
         assert isinstance(B.status_string(s), str) and B.status_string(s)
 
