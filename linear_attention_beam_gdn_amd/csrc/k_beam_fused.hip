@@ -40,10 +40,17 @@
 //   S0^T [q | k] on the matrix cores (q and k are bf16, so every plane
 //   product is exact; FP32 accumulation), the replay on its value rows with
 //   the ancestral update vectors delta_j (loaded into registers one tile
-//   ahead, each wave its own rows), then delta_t and o_t, stored with 64-byte
-//   contiguous writes per beam (o at the beam's index, delta_t at its slot),
-//   plus the appended record (by the first value slice).  Two waves per SIMD
-//   hide each other's latencies.
+//   ahead, each wave its own rows), then delta_t and o_t (o at the beam's
+//   index, delta_t at its slot), plus the appended record (by the first
+//   value slice).  A wave holds 64 bytes of each beam's o and delta_t rows,
+//   so where LDS allows, the tile's o and delta_t pass through an LDS staging
+//   buffer and go out one tile later as whole 128-byte lines (8 beams x 32
+//   value rows per store instruction); the key row goes out as 64 contiguous
+//   bytes per beam and wave.  Measured at 8 x 512 beams, H = 32, d = 128:
+//   writes of half lines, and of 8-byte key pieces, kept the second consumer
+//   wave on each SIMD blocked on store issue for half of every tile, and the
+//   four launches took 8 % longer.  Two waves per SIMD hide each other's
+//   latencies.
 //
 // Schedule.  With one chunk per (r, h), the beams are taken in the depth-
 // first order of the beam tree (lexicographic in their ancestry rows), so that
@@ -120,21 +127,36 @@ struct FusedGeom {
   }
   static constexpr int TL = staged_depths();
   static constexpr int BUF = ORK + TL * RKB;
-  static constexpr int NBUF0 = (kLdsBytes - SLOTB) / BUF;
+  // Output staging.  A consumer wave holds 16 value rows (64 bytes) of each
+  // beam's o and delta, so its own stores would write half lines; instead
+  // the consumers leave a tile's o and delta in LDS and, after the next
+  // barrier, each wave stores a block of 8 beams x 32 value rows of each
+  // (every store instruction writes whole 128-byte lines).  Two staging
+  // buffers (tiles alternate), beam rows padded by 16 bytes so that the
+  // consumers' writes are free of bank conflicts; used where the tile ring
+  // keeps four buffers beside it.
+  static constexpr int PITCH = VS * 4 + 16;
+  static constexpr int STGB = 2 * 2 * 16 * PITCH;  // [tile parity][o | delta][beam][value row]
+  static constexpr bool STAGE = (kLdsBytes - SLOTB - STGB) / BUF >= 4;
+  static constexpr int NBUF0 = (kLdsBytes - SLOTB - (STAGE ? STGB : 0)) / BUF;
   static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
   static_assert(NBUF >= 3, "tile buffers do not fit in LDS");
   // The slice of S0[r, h] is staged in LDS past the first two tile buffers
   // (which the prologue fills first) until the consumers have split it into
   // planes, when it fits (d_k <= 128); with d_k = 256 the consumers load it
   // from HBM themselves.  The schedule's scratch (bucket counts, staged
-  // ancestry rows) is the first two buffers.
+  // ancestry rows) is the first two buffers.  The output staging follows the
+  // ring (S0 may extend over it: S0 has left LDS before the first tile's
+  // outputs arrive), then the schedule table.
   static constexpr int S0B = DK * VS * 4, OS0 = 2 * BUF;
   static constexpr bool S0_LDS = OS0 + S0B + SLOTB <= kLdsBytes;
-  static constexpr int RINGB = (S0_LDS && OS0 + S0B > NBUF * BUF) ? OS0 + S0B : NBUF * BUF;
+  static constexpr int OSTG = NBUF * BUF;
+  static constexpr int RINGB = (S0_LDS && OS0 + S0B > OSTG + (STAGE ? STGB : 0)) ? OS0 + S0B
+                                                                                : OSTG + (STAGE ? STGB : 0);
   static constexpr int LDS = RINGB + SLOTB;
   static_assert(LDS <= kLdsBytes, "LDS layout does not fit");
   static_assert(!S0_LDS || S0B % 1024 == 0, "S0 is staged in whole DMA blocks");
-  static_assert(NC == 2 * KS || NC == KS, "the key row is appended by the consumer waves in halves or wholes");
+  static_assert(NC >= KS, "every 32-channel step of the appended key row needs a consumer wave");
   // LDS-DMA instructions the DMA wave issues per tile
   static constexpr int OPT = 2 * (QB / 1024) + VB / 1024 + NSM + TL * (RKB / 1024);
   static_assert(QB % 1024 == 0 && VB % 1024 == 0, "tile arrays must be whole DMA blocks");
@@ -428,9 +450,8 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   const bool key_writer = h % a.gq == 0;
   const __amdgpu_buffer_rsrc_t w_k = store_window(a.rec_k + rec0k * DK, (nb - 1) * sk + DK * 2);
   const __amdgpu_buffer_rsrc_t w_a = store_window(a.rec_alpha + rec0, (nb - 1) * sa + 4);
-  // this wave's share of the appended key row: 4 channels per lane (8 when
-  // there are as many consumer waves as 32-channel steps)
-  const int ks = G::NC == 2 * KS ? w >> 1 : w, kh = G::NC == 2 * KS ? w & 1 : 0;
+  // The appended key row: consumer wave w < KS stores channels 32w .. 32w + 31
+  // of every beam of a tile (64 contiguous bytes per beam, 16 per lane).
 
   // ancestral update vectors of one tile, this lane's 4 rows of beam c
   auto load_deltas = [&](int p, f32x4* d) {
@@ -473,6 +494,27 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   lds_barrier();  // 0
   GDN_STAMP(5);
 
+  // Staged outputs of tile p (written by every consumer wave before the
+  // barrier that ends tile p): this wave stores line block w of o and of
+  // delta, value rows 32m .. 32m + 31 of beams 8 half .. 8 half + 7, lane
+  // (beam 8 half + l / 8, rows 32m + 4 (l % 8) .. + 3).
+  constexpr int PF = G::PITCH / 4;  // floats per staged beam row
+  float* const stg = reinterpret_cast<float*>(smem + G::OSTG);
+  auto store_staged = [&](int p) {
+    constexpr int NM = G::VS / 32;
+    const float* sb = stg + (p & 1) * (2 * 16 * PF);
+    const int bl = (w / NM) * 8 + (lane >> 3);
+    const int rrow = (w % NM) * 32 + (lane & 7) * 4;
+    const u32x4 vo = *reinterpret_cast<const u32x4*>(sb + bl * PF + rrow);
+    const u32x4 vd = *reinterpret_cast<const u32x4*>(sb + (16 + bl) * PF + rrow);
+    const int pos = p * 16 + bl;
+    const bool lv = pos < nb;
+    const int ibb = lv ? (T > 0 ? (int)s_tab[pos][0] : pos) : 0;
+    const int rb = (vs0 + rrow) * 4;
+    __builtin_amdgcn_raw_buffer_store_b128(vo, w_o, lv ? ibb * so + rb : kOutside, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(vd, w_d, lv ? pos * so + rb : kOutside, 0, 0);
+  };
+
   unsigned long long c_busy = 0, c_barrier = 0;
   for (int it = 0; it < ntiles; ++it) {
     const unsigned long long c0 = stamp_now();
@@ -480,6 +522,10 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
 #pragma unroll
     for (int j = 0; j < T; ++j) dcur[j] = dnext[j];
     if (it + 1 < ntiles) load_deltas(it + 1, dnext);
+    // the previous tile's outputs, issued after the next tile's loads so
+    // that waiting for those loads does not wait for these stores
+    if constexpr (G::STAGE)
+      if (it > 0) store_staged(it - 1);
 
     const uint8_t* buf = smem + (it % G::NBUF) * G::BUF;
     // the tile's q and k fragments (B operands); with d_k = 256 each is read
@@ -546,25 +592,30 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     // increasing slot order)
     const int posi = it * 16 + c;
     const bool live = posi < nb;
-    const int ib = live ? (T > 0 ? (int)s_tab[posi][0] : posi) : 0;
-    const int off_o = live ? ib * so + row0 * 4 : kOutside;
-    const int off_r = live ? posi * so + row0 * 4 : kOutside;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, off_o, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, off_r, 0, 0);
-    u32x4 kk;
-    if constexpr (kBInLoop) {
-      kk = *reinterpret_cast<const u32x4*>(buf + G::OKK + (ks * 64 + lane) * 16);
+    if constexpr (G::STAGE) {
+      float* sb = stg + (it & 1) * (2 * 16 * PF);
+      *reinterpret_cast<f32x4*>(sb + c * PF + w * 16 + 4 * g) = ot;
+      *reinterpret_cast<f32x4*>(sb + (16 + c) * PF + w * 16 + 4 * g) = dt;
     } else {
-      kk = kf[0];
-#pragma unroll
-      for (int s = 1; s < KS; ++s)
-        if (ks == s) kk = kf[s];
+      const int ib = live ? (T > 0 ? (int)s_tab[posi][0] : posi) : 0;
+      const int off_o = live ? ib * so + row0 * 4 : kOutside;
+      const int off_r = live ? posi * so + row0 * 4 : kOutside;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, off_o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, off_r, 0, 0);
     }
-    const int off_k = live && key_writer && slice0 ? posi * sk + (ks * 32 + g * 8 + kh * 4) * 2 : kOutside;
-    if constexpr (G::NC == 2 * KS)
-      __builtin_amdgcn_raw_buffer_store_b64(kh ? u32x2{kk[2], kk[3]} : u32x2{kk[0], kk[1]}, w_k, off_k, 0, 0);
-    else
+    if (w < KS) {
+      u32x4 kk;
+      if constexpr (kBInLoop) {
+        kk = *reinterpret_cast<const u32x4*>(buf + G::OKK + (w * 64 + lane) * 16);
+      } else {
+        kk = kf[0];
+#pragma unroll
+        for (int s = 1; s < KS; ++s)
+          if (w == s) kk = kf[s];
+      }
+      const int off_k = live && key_writer && slice0 ? posi * sk + (w * 32 + g * 8) * 2 : kOutside;
       __builtin_amdgcn_raw_buffer_store_b128(kk, w_k, off_k, 0, 0);
+    }
     const float at = *reinterpret_cast<const float*>(buf + G::OS + c * 4);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(at), w_a,
                                           (live && slice0 && w == G::NC - 1 && g == 0) ? posi * sa : kOutside, 0, 0);
@@ -573,6 +624,8 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     c_busy += c1 - c0;
     c_barrier += stamp_now() - c1;
   }
+  if constexpr (G::STAGE)
+    if (ntiles > 0) store_staged(ntiles - 1);  // the last barrier ended its tile
   GDN_STAMP(6);
   GDN_STAMP_AT(10, 0, c_busy);
   GDN_STAMP_AT(14, 0, c_barrier);
