@@ -39,8 +39,10 @@
 //     weights and the ancestral update vectors (loaded into registers one
 //     tile ahead, addressed by 32-bit offsets from per-depth bases);
 //     delta_t is formed in the k columns and handed to the q columns of the
-//     same beam by a DPP row rotation, which form o_t; the q columns store
-//     o_t and the k columns delta_t.
+//     same beam by a DPP row rotation, which form o_t; the q columns give
+//     o_t and the k columns delta_t to an LDS staging buffer, from which the
+//     tile leaves after the next barrier as whole 128-byte lines (where LDS
+//     allows; else each lane stores its 16 bytes).
 //
 // Two heads per workgroup (NI = 2).  When the grid would hold two rounds of
 // workgroups or more, a workgroup takes two heads h, h + 1 of one request in
@@ -126,7 +128,16 @@ struct KdaGeom {
   static_assert(T <= 6, "the channel-decay kernel takes at most six record depths");
   // schedule table: per position {beam, slot_0, slot_1, slot_2}, plus slots 3 .. T-1
   static constexpr int SLOTB = T > 0 ? kMaxChunkF * 16 + (T > 3 ? (T - 3) * kMaxChunkF * 4 : 0) : 0;
-  static constexpr int NBUF0 = (kLdsBytes - SLOTB) / BUF;
+  // Output staging, as in the scalar-decay kernel: a consumer wave holds 16
+  // value rows (64 bytes) of each beam's o or delta, so the tile's o and
+  // delta wait in LDS and leave after the next barrier as whole 128-byte
+  // lines (8 beams x 32 value rows per store instruction).  Two buffers
+  // (tiles alternate), beam rows padded by 16 bytes; used where the ring
+  // keeps four buffers beside them.
+  static constexpr int PITCH = VS * 4 + 16;
+  static constexpr int STGB = 2 * 2 * TB * PITCH;  // [tile parity][o | delta][beam][value row]
+  static constexpr bool STAGE = (kLdsBytes - SLOTB - STGB) / BUF >= 4;
+  static constexpr int NBUF0 = (kLdsBytes - SLOTB - (STAGE ? STGB : 0)) / BUF;
   static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
   static_assert(NBUF >= 3, "tile buffers do not fit in LDS");
   // The slice of S0[r, h] ([d_k][VS]) is staged in LDS past the first two
@@ -135,7 +146,11 @@ struct KdaGeom {
   // themselves.  The schedule's scratch is the first two buffers.
   static constexpr int S0B = DK * VS * 4, OS0 = 2 * BUF;
   static constexpr bool S0_LDS = OS0 + S0B + SLOTB <= kLdsBytes;
-  static constexpr int RINGB = (S0_LDS && OS0 + S0B > NBUF * BUF) ? OS0 + S0B : NBUF * BUF;
+  // the output staging follows the ring (S0 may extend over it: S0 has left
+  // LDS before the first tile's outputs arrive), then the schedule table
+  static constexpr int OSTG = NBUF * BUF;
+  static constexpr int RINGB = (S0_LDS && OS0 + S0B > OSTG + (STAGE ? STGB : 0)) ? OS0 + S0B
+                                                                                : OSTG + (STAGE ? STGB : 0);
   static constexpr int LDS = RINGB + SLOTB;
   static_assert(LDS <= kLdsBytes, "LDS layout does not fit");
   static_assert(!S0_LDS || S0B % 1024 == 0, "S0 is staged in whole DMA blocks");
@@ -602,6 +617,29 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
   GDN_STAMP(5);
 
   unsigned long long c_prep = 0, c_fin = 0, c_bar = 0;
+  // Staged outputs of tile p (written by every consumer wave before the
+  // barrier that ends tile p, the head's windows still current): this wave
+  // stores line blocks NRB w .. NRB w + NRB - 1 of the tile's o (blocks
+  // 0 .. VS/32 - 1) and delta (the next VS/32), each value rows 32m .. 32m + 31
+  // of the 8 beams, lane (beam l / 8, rows 32m + 4 (l % 8) .. + 3).
+  constexpr int PF = G::PITCH / 4;  // floats per staged beam row
+  float* const stg = reinterpret_cast<float*>(smem + G::OSTG);
+  auto store_staged = [&](int p) {
+    constexpr int NM = G::VS / 32;
+    const int bl = lane >> 3;
+    const int pos = local(p) * G::TB + bl;
+    const bool lv = pos < nb;
+    const int ibb = lv ? (T > 0 ? (int)s_tab[pos][0] : pos) : 0;
+#pragma unroll
+    for (int k = 0; k < NRB; ++k) {
+      const int idx = w * NRB + k;
+      const int arr = idx / NM;  // 0: o, 1: delta
+      const int rrow = (idx % NM) * 32 + (lane & 7) * 4;
+      const u32x4 v =
+          *reinterpret_cast<const u32x4*>(stg + (p & 1) * (2 * G::TB * PF) + (arr * G::TB + bl) * PF + rrow);
+      __builtin_amdgcn_raw_buffer_store_b128(v, arr ? w_d : w_o, lv ? ibb * so + (vs0 + rrow) * 4 : kOutside, 0, 0);
+    }
+  };
   // one tile of the loop (the loop runs once per head, so that the planes of
   // S0 stay fixed inside it)
   auto step = [&](int it) {
@@ -622,6 +660,10 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
         for (int rb = 0; rb < NRB; ++rb) dcur[j][rb] = dnext[j][rb];
       load_deltas(it + 1, dnext);
     }
+    // the previous tile of this head's outputs (issued after the next tile's
+    // update vectors where those load in one batch)
+    if constexpr (G::STAGE)
+      if (local(it) > 0) store_staged(it - 1);
     // Next tile, unconditionally so that it shares a basic block with this
     // tile's work.  Past the last tile it reads a free buffer (no load of
     // this launch targets it any more), writes only there, and its appends
@@ -685,10 +727,15 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       }
 
       // output (q-column lanes) and the appended update vector (k-column lanes)
-      const int off = live ? (G::LEAN ? (int)__umul24((uint32_t)ib, (uint32_t)so) : ib * so) + (row0 + 16 * rb) * 4
-                           : kOutside;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, side ? kOutside : off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, side ? off : kOutside, 0, 0);
+      if constexpr (G::STAGE) {
+        *reinterpret_cast<f32x4*>(stg + (it & 1) * (2 * G::TB * PF) + (side * G::TB + bb) * PF +
+                                  (w * NRB + rb) * 16 + 4 * g) = side ? dt : ot;
+      } else {
+        const int off = live ? (G::LEAN ? (int)__umul24((uint32_t)ib, (uint32_t)so) : ib * so) + (row0 + 16 * rb) * 4
+                             : kOutside;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, side ? kOutside : off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, side ? off : kOutside, 0, 0);
+      }
       if constexpr (!DBUF) load_deltas(it + 1, dnext, rb, rb + 1);
     }
     const unsigned long long c2 = stamp_now();
@@ -698,6 +745,9 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     c_bar += stamp_now() - c2;
   };
   for (int it = 0; it < ntiles; ++it) step(it);
+  // the head's last tile (its barrier has passed) before the windows move on
+  if constexpr (G::STAGE)
+    if (ntiles > 0) store_staged(ntiles - 1);
   if constexpr (NI > 1) {
     // the second head: its part of S0 from memory into the planes, its
     // output windows, then its tiles
@@ -711,6 +761,8 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       split_planes<2>(x, As[0][s]);
     }
     for (int it = ntiles; it < ntot; ++it) step(it);
+    if constexpr (G::STAGE)
+      if (ntot > ntiles) store_staged(ntot - 1);
   }
   GDN_STAMP(6);
   GDN_STAMP_AT(8, 0, c_prep);
