@@ -45,8 +45,8 @@
 //   value slice).  A wave holds 64 bytes of each beam's o and delta_t rows,
 //   so where LDS allows, the tile's o and delta_t pass through an LDS staging
 //   buffer and go out one tile later as whole 128-byte lines (8 beams x 32
-//   value rows per store instruction); the key row goes out as 64 contiguous
-//   bytes per beam and wave.  Measured at 8 x 512 beams, H = 32, d = 128:
+//   value rows per store instruction); the key rows go out as whole lines
+//   too, read from the tile buffer.  Measured at 8 x 512 beams, H = 32, d = 128:
 //   writes of half lines, and of 8-byte key pieces, kept the second consumer
 //   wave on each SIMD blocked on store issue for half of every tile, and the
 //   four launches took 8 % longer.  Two waves per SIMD hide each other's
@@ -450,8 +450,9 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
   const bool key_writer = h % a.gq == 0;
   const __amdgpu_buffer_rsrc_t w_k = store_window(a.rec_k + rec0k * DK, (nb - 1) * sk + DK * 2);
   const __amdgpu_buffer_rsrc_t w_a = store_window(a.rec_alpha + rec0, (nb - 1) * sa + 4);
-  // The appended key row: consumer wave w < KS stores channels 32w .. 32w + 31
-  // of every beam of a tile (64 contiguous bytes per beam, 16 per lane).
+  // The appended key row: consumer waves w < KS store it, whole 128-byte
+  // lines of 8 beams each (d_k >= 64), else channels 32w .. 32w + 31 of every
+  // beam (16 bytes per lane).
 
   // ancestral update vectors of one tile, this lane's 4 rows of beam c
   auto load_deltas = [&](int p, f32x4* d) {
@@ -603,7 +604,20 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot), w_o, off_o, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dt), w_d, off_r, 0, 0);
     }
-    if (w < KS) {
+    if constexpr (DK >= 64) {
+      // whole 128-byte lines of the key rows, read from the tile buffer:
+      // wave w < KS takes line w % (DK / 64) of 8 beams, lane (beam l / 8,
+      // 16-byte chunk l % 8 of the line)
+      constexpr int LPR = DK / 64;
+      if (w < KS) {
+        const int bl = (w / LPR) * 8 + (lane >> 3);
+        const int ch = (w % LPR) * 8 + (lane & 7);
+        const u32x4 kk = *reinterpret_cast<const u32x4*>(buf + G::OKK + ((ch >> 2) * 64 + (ch & 3) * 16 + bl) * 16);
+        const int pk = it * 16 + bl;
+        __builtin_amdgcn_raw_buffer_store_b128(kk, w_k, pk < nb && key_writer && slice0 ? pk * sk + ch * 16 : kOutside,
+                                               0, 0);
+      }
+    } else if (w < KS) {
       u32x4 kk;
       if constexpr (kBInLoop) {
         kk = *reinterpret_cast<const u32x4*>(buf + G::OKK + (w * 64 + lane) * 16);
