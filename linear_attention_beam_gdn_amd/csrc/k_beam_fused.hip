@@ -512,8 +512,8 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
     const bool lv = pos < nb;
     const int ibb = lv ? (T > 0 ? (int)s_tab[pos][0] : pos) : 0;
     const int rb = (vs0 + rrow) * 4;
-    __builtin_amdgcn_raw_buffer_store_b128(vo, w_o, lv ? ibb * so + rb : kOutside, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(vd, w_d, lv ? pos * so + rb : kOutside, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(vo, w_o, lv ? ibb * so + rb : kOutside, 0, kStreamStore);
+    __builtin_amdgcn_raw_buffer_store_b128(vd, w_d, lv ? pos * so + rb : kOutside, 0, kStreamStore);
   };
 
   unsigned long long c_busy = 0, c_barrier = 0;

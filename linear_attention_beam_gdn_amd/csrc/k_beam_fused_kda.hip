@@ -637,7 +637,8 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       const int rrow = (idx % NM) * 32 + (lane & 7) * 4;
       const u32x4 v =
           *reinterpret_cast<const u32x4*>(stg + (p & 1) * (2 * G::TB * PF) + (arr * G::TB + bl) * PF + rrow);
-      __builtin_amdgcn_raw_buffer_store_b128(v, arr ? w_d : w_o, lv ? ibb * so + (vs0 + rrow) * 4 : kOutside, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v, arr ? w_d : w_o, lv ? ibb * so + (vs0 + rrow) * 4 : kOutside, 0,
+                                             kStreamStore);
     }
   };
   // one tile of the loop (the loop runs once per head, so that the planes of
