@@ -7,8 +7,10 @@ d_k = d_v = 128, on seeded synthetic inputs already resident in HBM.
 
 Prints one JSON line: beam-steps/s, the roofline of the decode kernel
 (algorithmic bytes per launch over its mean kernel time, taken by HIP events
-that the runtime records around each launch, against 8 TB/s), and the FP64
-CPU oracle timed on a bounded sample of the same workload on the host cores.
+that the runtime records around each launch after a cache-evicting read-only
+sweep, against 8 TB/s; beside it the same launches back to back with no sweep,
+and the timed loop's own rate, launch gaps included), and the FP64 CPU oracle
+timed on a bounded sample of the same workload on the host cores.
 """
 
 from __future__ import annotations
@@ -743,6 +745,9 @@ def main():
     launch_ms = timed_passes(True)
     launch_ms_pair = timed_passes(True, kernel=False)
     launch_ms_copy = timed_passes("copy")
+    # and back to back with no sweep (the steady state of the timed loop:
+    # each launch meets what the previous one left in the caches)
+    launch_ms_b2b = timed_passes(False)
     del src, dst
     # what any launch timed the same way costs: a near-empty launch after the
     # same sweep, bracketed by the runtime, and between event commands
@@ -812,6 +817,11 @@ def main():
             "launch_us_event_pair": [float(x) * 1e3 for x in launch_ms_pair.mean(0)],
             "frac_event_pair": mean_bytes / (float(launch_ms_pair.mean()) * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "launch_us_after_copy_flush": [float(x) * 1e3 for x in launch_ms_copy.mean(0)],
+            "launch_us_back_to_back": [float(x) * 1e3 for x in launch_ms_b2b.mean(0)],
+            "frac_back_to_back": mean_bytes / (float(launch_ms_b2b.mean()) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            # the timed loop's own rate: every launch's bytes over the wall
+            # clock of the back-to-back passes, the gaps between launches included
+            "frac_sustained": w.L * mean_bytes / (total_ms / args.steps * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "traffic": measured_traffic(),
             "bytes_per_launch": mean_bytes,
             "bytes_per_launch_per_beam_gather": float(np.mean(gather_bytes)),
