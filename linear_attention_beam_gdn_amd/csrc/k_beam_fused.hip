@@ -314,6 +314,11 @@ __global__ __launch_bounds__((FusedGeom<DK, DV, T>::NT)) void k_beam_fused(BeamA
 
   if (w == G::WDOT) {
     // ============================================================ dot wave
+    // With d_k = 256 the dot wave's work paces the tile loop from t = 2 on,
+    // and it shares its SIMD with two consumer waves: it issues first
+    // (measured at 8 x 512 beams, H = 16, d_v = 512: t = 3 4 % faster; at
+    // d_k = 128, where it does not pace the loop, no gain).
+    if constexpr (DK > 128) __builtin_amdgcn_s_setprio(3);
     // keys of record depth j of tile p's beams from the record store
     auto load_key = [&](int p, int j, u32x4* kj) {
       const int posi = min(p * 16 + c, nb - 1);
