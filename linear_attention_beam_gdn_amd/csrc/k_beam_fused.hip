@@ -45,12 +45,12 @@
 //   value slice).  A wave holds 64 bytes of each beam's o and delta_t rows,
 //   so where LDS allows, the tile's o and delta_t pass through an LDS staging
 //   buffer and go out one tile later as whole 128-byte lines (8 beams x 32
-//   value rows per store instruction); the key rows go out as whole lines
-//   too, read from the tile buffer.  Measured at 8 x 512 beams, H = 32, d = 128:
-//   writes of half lines, and of 8-byte key pieces, kept the second consumer
-//   wave on each SIMD blocked on store issue for half of every tile, and the
-//   four launches took 8 % longer.  Two waves per SIMD hide each other's
-//   latencies.
+//   value rows per store instruction, non-temporal); the key rows go out as
+//   whole lines too, read from the tile buffer.  Measured at 8 x 512 beams,
+//   H = 32, d = 128: writes of half lines, and of 8-byte key pieces, kept the
+//   second consumer wave on each SIMD blocked on store issue for half of
+//   every tile, and the four launches took 13 % longer.  Two waves per SIMD
+//   hide each other's latencies.
 //
 // Schedule.  With one chunk per (r, h), the beams are taken in the depth-
 // first order of the beam tree (lexicographic in their ancestry rows), so that
