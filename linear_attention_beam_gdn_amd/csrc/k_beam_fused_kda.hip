@@ -133,10 +133,13 @@ struct KdaGeom {
   // delta wait in LDS and leave after the next barrier as whole 128-byte
   // lines (8 beams x 32 value rows per store instruction).  Two buffers
   // (tiles alternate), beam rows padded by 16 bytes; used where the ring
-  // keeps four buffers beside them.
+  // keeps three buffers beside them (at d_v = 512, t = 3 the staging with
+  // three buffers measured 6 % faster than half-line stores with four, and
+  // chains of five to seven records 1-3 % faster; the scalar-decay kernel
+  // keeps four: with three its wide state ran t = 2 and 3 slower).
   static constexpr int PITCH = VS * 4 + 16;
   static constexpr int STGB = 2 * 2 * TB * PITCH;  // [tile parity][o | delta][beam][value row]
-  static constexpr bool STAGE = (kLdsBytes - SLOTB - STGB) / BUF >= 4;
+  static constexpr bool STAGE = (kLdsBytes - SLOTB - STGB) / BUF >= 3;
   static constexpr int NBUF0 = (kLdsBytes - SLOTB - (STAGE ? STGB : 0)) / BUF;
   static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
   static_assert(NBUF >= 3, "tile buffers do not fit in LDS");
