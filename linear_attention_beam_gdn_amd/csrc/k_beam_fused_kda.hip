@@ -46,11 +46,12 @@
 //
 // Two heads per workgroup (NI = 2).  When the grid would hold two rounds of
 // workgroups or more, a workgroup takes two heads h, h + 1 of one request in
-// turn instead (one value slice, one chunk): their beams and parents are the
-// same, so they share one schedule, and one tile loop runs over both heads'
-// tiles, the DMA waves streaming the second head's first tiles while the
-// consumers finish the first's.  The consumers load the second head's part of
-// S0 from memory and form its planes when they reach its first tile.  This
+// turn instead (one value slice of up to 128 rows, one chunk): their beams
+// and parents are the same, so they share one schedule, and one tile loop
+// runs over both heads' tiles, the DMA waves streaming the second head's
+// first tiles while the consumers finish the first's.  The consumers load the
+// second head's part of S0 from memory and form its planes when they reach
+// its first tile.  This
 // spares the second head the prologue a second round of workgroups would pay
 // (the schedule's loads and sort, S0 and the first tiles in flight); every
 // beam's arithmetic is unchanged.
@@ -756,13 +757,16 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     // the second head: its part of S0 from memory into the planes, its
     // output windows, then its tiles
     out_head(h + 1);
-    const float* Sg = a.S + ((size_t)r * a.H + h + 1) * DK * DV + vs0 + w * 16 + c;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      float x[8];
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float* Sg = a.S + ((size_t)r * a.H + h + 1) * DK * DV + vs0 + (w * NRB + rb) * 16 + c;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = Sg[(size_t)(s * 32 + g * 8 + e) * DV];
-      split_planes<2>(x, As[0][s]);
+      for (int s = 0; s < KS; ++s) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = Sg[(size_t)(s * 32 + g * 8 + e) * DV];
+        split_planes<2>(x, As[rb][s]);
+      }
     }
     for (int it = ntiles; it < ntot; ++it) step(it);
     if constexpr (G::STAGE)
@@ -809,9 +813,11 @@ int launch(const gdn_shape& sh, const gdn_store& st, int Wt, const StepIO& io, h
   if (grid > 0x7FFFFFFFL) return GDN_EINVAL;
   // Two heads per workgroup where a grid of one per head would run two
   // rounds or more (one chunk, one value slice, chains of up to three records,
-  // whose registers leave room for the second head's S0).  GDN_BEAM_PAIR=0
-  // turns it off, for comparisons.
-  if constexpr (G::NVS == 1 && T <= 3) {
+  // whose registers leave room for the second head's S0).  Not with two row
+  // blocks per consumer wave (d_v = 256 in one slice): there the pair spills
+  // registers and 16 x 32 heads of 256 beams ran no faster (four steps 746
+  // against 740 us).  GDN_BEAM_PAIR=0 turns it off, for comparisons.
+  if constexpr (G::NVS == 1 && G::NRB == 1 && T <= 3) {
     const char* pair = getenv("GDN_BEAM_PAIR");
     const bool off = pair != nullptr && pair[0] == '0';
     if (!off && a.nchunk == 1 && sh.H % 2 == 0 && grid >= 2L * cus) {

@@ -143,6 +143,18 @@ def test_many_value_heads_sampled(H, Hk, dv, R, W, channel):
     check_beam(inp, channel, requests=[R - 1], heads=heads, label=f"H = {H} on H_k = {Hk}, d_v = {dv}")
 
 
+@pytest.mark.parametrize("dk,dv,pair", [(64, 64, "1"), (128, 256, "1"), (128, 256, "0")])
+def test_channel_decay_two_rounds_of_heads(dk, dv, pair, monkeypatch):
+    # 16 x 32 (request, head) pairs in one value slice: a grid of two rounds,
+    # which the launch folds into two heads per workgroup at d_v = 64 (pair
+    # "1"); at d_v = 256 (two row blocks per consumer wave) it keeps one head
+    # per workgroup either way.  Both heads of a workgroup pair are checked.
+    monkeypatch.setenv("GDN_BEAM_PAIR", pair)
+    inp = synth.make_inputs(R=16, H=32, dk=dk, dv=dv, W=48, L=4, s0_std=0.05, seed=57, parents="topk",
+                            channel_decay=True)
+    check_beam(inp, True, requests=[0, 15], heads=[0, 1, 30, 31], label=f"channel decay {dk} x {dv}, pair={pair}")
+
+
 @pytest.mark.parametrize("wname,channel,requests,heads", [("LARGE", False, [6], [0, 29]),
                                                            ("WIDE", False, [2], [11]),
                                                            ("KDA", True, [9], [4])])
