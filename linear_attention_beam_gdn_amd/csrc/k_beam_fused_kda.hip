@@ -666,8 +666,13 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       load_deltas(it + 1, dnext);
     }
     // the previous tile of this head's outputs (issued after the next tile's
-    // update vectors where those load in one batch)
-    if constexpr (G::STAGE)
+    // update vectors where those load in one batch).  With three records and
+    // two row blocks per wave, the register-bound case, they leave after the
+    // next tile's preparation instead: two registers spilled instead of four,
+    // and t = 3 at d_v = 512 8 % faster (at t = 2, or with one row block, that
+    // placement was 2-4 % slower).
+    constexpr bool LATE_STORE = T == 3 && G::NRB == 2;
+    if constexpr (G::STAGE && !LATE_STORE)
       if (local(it) > 0) store_staged(it - 1);
     // Next tile, unconditionally so that it shares a basic block with this
     // tile's work.  Past the last tile it reads a free buffer (no load of
@@ -677,6 +682,8 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       if (it + 1 == ntiles) prep_head(h + 1);
     }
     prep(it + 1);
+    if constexpr (G::STAGE && LATE_STORE)
+      if (local(it) > 0) store_staged(it - 1);
     const unsigned long long c1 = stamp_now();
 
     const uint8_t* buf = smem + (it % G::NBUF) * G::BUF;
