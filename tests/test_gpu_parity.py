@@ -155,6 +155,18 @@ def test_channel_decay_two_rounds_of_heads(dk, dv, pair, monkeypatch):
     check_beam(inp, True, requests=[0, 15], heads=[0, 1, 30, 31], label=f"channel decay {dk} x {dv}, pair={pair}")
 
 
+@pytest.mark.parametrize("dk,dv,channel", [(128, 256, False), (256, 128, False), (256, 256, False),
+                                            (128, 512, True)])
+def test_grids_of_several_rounds(dk, dv, channel):
+    # 16 x 32 (request, head) pairs: every value slice of every head in a grid
+    # of two rounds or more on the 256 compute units (the XCD-grouped
+    # workgroup order, slices and store windows at that size); the first and
+    # last heads of the first and last requests are checked
+    inp = synth.make_inputs(R=16, H=32, dk=dk, dv=dv, W=40, L=4, s0_std=0.05, seed=59 + dk + dv, parents="topk",
+                            channel_decay=channel)
+    check_beam(inp, channel, requests=[0, 15], heads=[0, 1, 30, 31], label=f"{dk} x {dv}, 16 x 32 heads")
+
+
 @pytest.mark.parametrize("wname,channel,requests,heads", [("LARGE", False, [6], [0, 29]),
                                                            ("WIDE", False, [2], [11]),
                                                            ("KDA", True, [9], [4])])
