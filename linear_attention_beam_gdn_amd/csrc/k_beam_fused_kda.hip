@@ -670,9 +670,13 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
     // two row blocks per wave, the register-bound case, they leave after the
     // next tile's preparation instead: two registers spilled instead of four,
     // and t = 3 at d_v = 512 8 % faster (at t = 2, or with one row block, that
-    // placement was 2-4 % slower).
+    // placement was 2-4 % slower).  At one record with one 256-row slice
+    // (d_v = 256) they leave at the end of the tile: no register spilled
+    // instead of three, t = 1 at 16 x 256 beams 9 % faster (at d_v = 512 that
+    // placement was not faster).
     constexpr bool LATE_STORE = T == 3 && G::NRB == 2;
-    if constexpr (G::STAGE && !LATE_STORE)
+    constexpr bool END_STORE = T == 1 && G::NRB == 2 && G::NVS == 1;
+    if constexpr (G::STAGE && !LATE_STORE && !END_STORE)
       if (local(it) > 0) store_staged(it - 1);
     // Next tile, unconditionally so that it shares a basic block with this
     // tile's work.  Past the last tile it reads a free buffer (no load of
@@ -750,6 +754,8 @@ __global__ __launch_bounds__((KdaGeom<DK, DV, T>::NT)) void k_beam_fused_kda(Bea
       }
       if constexpr (!DBUF) load_deltas(it + 1, dnext, rb, rb + 1);
     }
+    if constexpr (G::STAGE && END_STORE)
+      if (local(it) > 0) store_staged(it - 1);
     const unsigned long long c2 = stamp_now();
     lds_barrier();  // it + 1
     c_prep += c1 - c0;
